@@ -1,0 +1,105 @@
+"""Device-buffer plumbing around the C ABI: torch allocates the compressed cache,
+the workspace and the outputs; every step of the codec runs in libqvg.so."""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+def config(d: int, n_centroids: int, n_stages: int, group_size: int, iters_cold: int,
+           iters_warm: int, seed: int, dtype: str) -> L.qvg_config:
+    dt = {"bf16": L.QVG_BF16, "f32": L.QVG_F32}[dtype]
+    return L.make_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dt)
+
+
+def _dtype_of(cfg: L.qvg_config) -> torch.dtype:
+    return torch.bfloat16 if cfg.dtype == L.QVG_BF16 else torch.float32
+
+
+class CompressedKV:
+    """The compressed cache of one tensor of one layer: codes, scales,
+    assignments and per-chunk centroids, plus the qvg_cache_view over them."""
+
+    def __init__(self, cfg: L.qvg_config, heads: int, cap_tokens: int, chunk_tokens: int, device):
+        self.cfg, self.heads, self.cap, self.chunk_tokens = cfg, heads, cap_tokens, chunk_tokens
+        nb = L.qvg_cache_view_bytes(cfg, heads, cap_tokens, chunk_tokens)
+        d, G, T, K = cfg.d, cfg.group_size, cfg.n_stages, cfg.n_centroids
+        self.n_chunks = -(-cap_tokens // chunk_tokens)
+        self.codes = torch.empty((heads, cap_tokens, d // 4), dtype=torch.uint8, device=device)
+        self.scales = torch.empty((heads, cap_tokens, d // G), dtype=torch.uint8, device=device)
+        self.assign = torch.empty((max(T, 1), heads, cap_tokens), dtype=torch.uint8, device=device)
+        self.centroids = torch.empty((self.n_chunks, max(T, 1), heads, K, d), dtype=_dtype_of(cfg),
+                                     device=device)
+        assert self.codes.numel() == nb[0] and self.scales.numel() == nb[1]
+        assert T == 0 or (self.assign.numel() == nb[2]
+                          and self.centroids.numel() * self.centroids.element_size() == nb[3])
+        self.view = L.qvg_cache_view(self.codes.data_ptr(), self.scales.data_ptr(),
+                                     self.assign.data_ptr(), self.centroids.data_ptr(),
+                                     cap_tokens, chunk_tokens, heads)
+
+    def bytes(self) -> int:
+        return sum(L.qvg_cache_view_bytes(self.cfg, self.heads, self.cap, self.chunk_tokens))
+
+
+class CentroidCache:
+    """Owner of a qvg_centroid_cache handle."""
+
+    def __init__(self, cfg: L.qvg_config, heads: int):
+        self.cfg, self.heads = cfg, heads
+        self.handle = L.qvg_centroid_cache_create(cfg, heads)
+
+    def reset(self) -> None:
+        L.qvg_centroid_cache_reset(self.handle)
+
+    def export(self, device, stream=None) -> torch.Tensor:
+        c = self.cfg
+        out = torch.empty((c.n_stages, self.heads, c.n_centroids, c.d), dtype=torch.float32, device=device)
+        L.qvg_centroid_cache_export(self.handle, out, stream or torch.cuda.current_stream())
+        return out
+
+    def load(self, src: torch.Tensor, stream=None) -> None:
+        L.qvg_centroid_cache_import(self.handle, src.contiguous(), stream or torch.cuda.current_stream())
+
+    def close(self) -> None:
+        if self.handle is not None:
+            L.qvg_centroid_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Encoder:
+    """Holds a workspace sized for (heads, max chunk tokens) and encodes chunks."""
+
+    def __init__(self, cfg: L.qvg_config, heads: int, max_tokens: int, device):
+        self.cfg, self.heads = cfg, heads
+        self.ws_bytes = L.qvg_encode_workspace_bytes(cfg, heads, max_tokens)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    def encode(self, x: torch.Tensor, dst: CompressedKV, chunk_index: int,
+               cache: CentroidCache | None = None, init: torch.Tensor | None = None, stream=None):
+        """x: [H][N][d] view whose rows are contiguous (a token slice of a larger
+        [H][Ntot][d] tensor is fine)."""
+        H, N, d = x.shape
+        assert x.stride(2) == 1 and x.stride(1) == d and x.dtype == _dtype_of(self.cfg)
+        L.qvg_encode_chunk(self.cfg, x, x.stride(0), H, N,
+                           None if init is None else init.contiguous(),
+                           None if cache is None else cache.handle, dst.view, chunk_index,
+                           self.ws, self.ws_bytes, stream or torch.cuda.current_stream())
+
+
+def decode(cfg: L.qvg_config, src: CompressedKV, tok_begin: int, tok_end: int,
+           out: torch.Tensor | None = None, out_dtype: str = "bf16", stream=None) -> torch.Tensor:
+    if out is None:
+        dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+        out = torch.empty((src.heads, tok_end - tok_begin, cfg.d), dtype=dt, device=src.codes.device)
+    odt = L.QVG_BF16 if out.dtype == torch.bfloat16 else L.QVG_F32
+    assert out.stride(2) == 1 and out.stride(1) == cfg.d
+    L.qvg_decode(cfg, src.view, tok_begin, tok_end, out, out.stride(0), odt,
+                 stream or torch.cuda.current_stream())
+    return out

@@ -1,0 +1,578 @@
+// C ABI of the Quant VideoGen KV-cache codec: argument validation, workspace
+// layout, the centroid cache object and the per-chunk stage loop.  Every step
+// of the codec runs in the gfx950 kernels behind qvg_launch.h.
+//
+// The stage loop follows the pages' progressive residual quantisation
+// (163.com article, section 4; gist.science German summary, section 2B): stage t
+// clusters R(t-1), stores C(t) and pi(t) and forms R(t) = R(t-1) - C(t)[pi(t)];
+// the last stage's residual goes straight into the 2-bit quantiser.  k-means
+// starts from the streaming centroid cache when it holds the previous chunk's
+// centroids (163.com article, section 5; German summary, section 2C).
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "qvg.h"
+#include "qvg_launch.h"
+
+struct qvg_centroid_cache {
+    int32_t d, n_centroids, n_stages, heads;
+    float *data;     // [T][H][K][d] fp32, device
+    int32_t valid;   // host-side: set when an encode through this cache is enqueued
+};
+
+namespace {
+
+using namespace qvg;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+size_t dtype_size(int dt) { return dt == QVG_BF16 ? 2 : 4; }
+
+qvg_status check_config(const qvg_config *c) {
+    if (!c) return QVG_ERR_INVALID_ARG;
+    if (c->reserved != 0) return QVG_ERR_INVALID_ARG;
+    if (c->d <= 0 || c->group_size <= 0) return QVG_ERR_INVALID_ARG;
+    if (c->n_centroids < 1 || c->n_centroids > QVG_MAX_CENTROIDS) return QVG_ERR_INVALID_ARG;
+    if (c->n_stages < 0 || c->n_stages > QVG_MAX_STAGES) return QVG_ERR_INVALID_ARG;
+    if (c->iters_cold < 0 || c->iters_warm < 0) return QVG_ERR_INVALID_ARG;
+    if (c->dtype != QVG_F32 && c->dtype != QVG_BF16) return QVG_ERR_INVALID_ARG;
+    if (c->d % c->group_size != 0) return QVG_ERR_INVALID_ARG;
+    if (c->d != 64 && c->d != 128) return QVG_ERR_UNSUPPORTED;
+    const int g = c->group_size;
+    if (g != 16 && g != 32 && g != 64 && g != 128) return QVG_ERR_UNSUPPORTED;
+    return QVG_OK;
+}
+
+qvg_status hip_status(hipError_t e) { return e == hipSuccess ? QVG_OK : QVG_ERR_HIP; }
+
+#define QVG_TRY(expr)                                  \
+    do {                                               \
+        qvg_status st_ = hip_status(expr);             \
+        if (st_ != QVG_OK) return st_;                 \
+    } while (0)
+
+// ---- per-kernel timing with HIP events (qvg_profile_*) ----------------------
+// While enabled, every launch is bracketed by two events recorded on the stream
+// it runs on, with the launch's algorithmic FLOPs and HBM bytes.
+struct ProfRecord {
+    const char *name;
+    hipEvent_t a, b;
+    double flops, bytes;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+    if (!g_prof_pool.empty()) {
+        hipEvent_t e = g_prof_pool.back();
+        g_prof_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+struct ProfScope {
+    ProfRecord rec{};
+    hipStream_t s;
+    bool on = false;
+    ProfScope(const char *name, hipStream_t st, double flops, double bytes) : s(st) {
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (!g_prof_on) return;
+        rec.name = name;
+        rec.a = prof_event();
+        rec.b = prof_event();
+        rec.flops = flops;
+        rec.bytes = bytes;
+        if (!rec.a || !rec.b) return;
+        on = hipEventRecord(rec.a, s) == hipSuccess;
+    }
+    ~ProfScope() {
+        if (!on) return;
+        std::lock_guard<std::mutex> lk(g_prof_mu);
+        if (hipEventRecord(rec.b, s) == hipSuccess) g_prof.push_back(rec);
+    }
+};
+
+#define QVG_LAUNCH(name, flops, bytes, expr)                   \
+    do {                                                       \
+        ProfScope prof_(name, s, (double)(flops), (double)(bytes)); \
+        QVG_TRY(expr);                                         \
+    } while (0)
+
+// Carves one workspace into the buffers of the encode stage loop.
+struct EncodeWorkspace {
+    size_t R = 0, Rb = 0, C = 0, Cb = 0, cn = 0, counts = 0, offsets = 0, order = 0, idx = 0, total = 0;
+    bool has_R = false, has_Rb = false;
+
+    EncodeWorkspace(const qvg_config &c, int H, int N) {
+        const size_t D = c.d, K = c.n_centroids, Kp = padded_k(c.n_centroids);
+        const int T = c.n_stages;
+        if (T == 0) { total = 256; return; }
+        has_R = T >= 2;
+        has_Rb = T >= 2 || c.dtype == QVG_F32;
+        size_t off = 0;
+        auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
+        if (has_R) R = take((size_t)H * N * D * 4);
+        if (has_Rb) Rb = take((size_t)H * N * D * 2);
+        C = take((size_t)H * K * D * 4);
+        Cb = take((size_t)H * Kp * D * 2);
+        cn = take((size_t)H * Kp * 8);
+        counts = take((size_t)H * Kp * 4);
+        offsets = take((size_t)H * Kp * 4);
+        order = take((size_t)H * N * 4);
+        idx = take((size_t)H * K * 4);
+        total = off;
+    }
+};
+
+// Workspace of the stage-level k-means entry points.
+struct StageWorkspace {
+    size_t Xb = 0, C = 0, Cb = 0, cn = 0, counts = 0, offsets = 0, order = 0, total = 0;
+    StageWorkspace(int H, int N, int D, int K) {
+        const size_t Kp = padded_k(K);
+        size_t off = 0;
+        auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
+        Xb = take((size_t)H * N * D * 2);
+        C = take((size_t)H * K * D * 4);
+        Cb = take((size_t)H * Kp * D * 2);
+        cn = take((size_t)H * Kp * 8);
+        counts = take((size_t)H * Kp * 4);
+        offsets = take((size_t)H * Kp * 4);
+        order = take((size_t)H * N * 4);
+        total = off;
+    }
+};
+
+template <typename T>
+T *at(void *base, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(base) + off); }
+
+}  // namespace
+
+extern "C" {
+
+const char *qvg_status_string(qvg_status s) {
+    switch (s) {
+        case QVG_OK: return "QVG_OK";
+        case QVG_ERR_INVALID_ARG: return "QVG_ERR_INVALID_ARG";
+        case QVG_ERR_UNSUPPORTED: return "QVG_ERR_UNSUPPORTED";
+        case QVG_ERR_WORKSPACE: return "QVG_ERR_WORKSPACE";
+        case QVG_ERR_STATE: return "QVG_ERR_STATE";
+        case QVG_ERR_HIP: return "QVG_ERR_HIP";
+        case QVG_ERR_OOM: return "QVG_ERR_OOM";
+        default: return "QVG_ERR_UNKNOWN";
+    }
+}
+
+qvg_status qvg_config_validate(const qvg_config *cfg) { return check_config(cfg); }
+
+qvg_status qvg_chunk_bytes(const qvg_config *cfg, int32_t heads, int32_t n_tokens, uint64_t out[4]) {
+    qvg_status st = check_config(cfg);
+    if (st != QVG_OK) return st;
+    if (heads < 1 || n_tokens < 1 || !out) return QVG_ERR_INVALID_ARG;
+    const uint64_t H = heads, N = n_tokens, D = cfg->d;
+    out[0] = H * N * D / 4;
+    out[1] = H * N * D / cfg->group_size;
+    out[2] = (uint64_t)cfg->n_stages * H * N;
+    out[3] = (uint64_t)cfg->n_stages * H * cfg->n_centroids * D * dtype_size(cfg->dtype);
+    return QVG_OK;
+}
+
+qvg_status qvg_cache_view_bytes(const qvg_config *cfg, int32_t heads, int64_t cap_tokens, int32_t chunk_tokens,
+                                uint64_t out[4]) {
+    qvg_status st = check_config(cfg);
+    if (st != QVG_OK) return st;
+    if (heads < 1 || cap_tokens < 1 || chunk_tokens < 1 || !out) return QVG_ERR_INVALID_ARG;
+    const uint64_t H = heads, N = cap_tokens, D = cfg->d;
+    const uint64_t chunks = (cap_tokens + chunk_tokens - 1) / chunk_tokens;
+    out[0] = H * N * D / 4;
+    out[1] = H * N * D / cfg->group_size;
+    out[2] = (uint64_t)cfg->n_stages * H * N;
+    out[3] = chunks * cfg->n_stages * H * cfg->n_centroids * D * dtype_size(cfg->dtype);
+    return QVG_OK;
+}
+
+qvg_status qvg_encode_workspace_bytes(const qvg_config *cfg, int32_t heads, int32_t n_tokens, uint64_t *bytes) {
+    qvg_status st = check_config(cfg);
+    if (st != QVG_OK) return st;
+    if (heads < 1 || n_tokens < 1 || !bytes) return QVG_ERR_INVALID_ARG;
+    *bytes = EncodeWorkspace(*cfg, heads, n_tokens).total;
+    return QVG_OK;
+}
+
+qvg_status qvg_stage_workspace_bytes(int32_t heads, int32_t n_tokens, int32_t d, int32_t n_centroids,
+                                     uint64_t *bytes) {
+    if (heads < 1 || n_tokens < 1 || n_centroids < 1 || n_centroids > QVG_MAX_CENTROIDS || !bytes)
+        return QVG_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return QVG_ERR_UNSUPPORTED;
+    *bytes = StageWorkspace(heads, n_tokens, d, n_centroids).total;
+    return QVG_OK;
+}
+
+qvg_status qvg_centroid_cache_create(const qvg_config *cfg, int32_t heads, qvg_centroid_cache **out) {
+    qvg_status st = check_config(cfg);
+    if (st != QVG_OK) return st;
+    if (heads < 1 || !out) return QVG_ERR_INVALID_ARG;
+    *out = nullptr;
+    qvg_centroid_cache *c = new (std::nothrow) qvg_centroid_cache;
+    if (!c) return QVG_ERR_OOM;
+    c->d = cfg->d;
+    c->n_centroids = cfg->n_centroids;
+    c->n_stages = cfg->n_stages;
+    c->heads = heads;
+    c->data = nullptr;
+    c->valid = 0;
+    const size_t bytes = (size_t)cfg->n_stages * heads * cfg->n_centroids * cfg->d * sizeof(float);
+    if (bytes && hipMalloc((void **)&c->data, bytes) != hipSuccess) {
+        delete c;
+        return QVG_ERR_OOM;
+    }
+    *out = c;
+    return QVG_OK;
+}
+
+qvg_status qvg_centroid_cache_reset(qvg_centroid_cache *cache) {
+    if (!cache) return QVG_ERR_INVALID_ARG;
+    cache->valid = 0;
+    return QVG_OK;
+}
+
+qvg_status qvg_centroid_cache_destroy(qvg_centroid_cache *cache) {
+    if (!cache) return QVG_OK;
+    qvg_status st = QVG_OK;
+    if (cache->data && hipFree(cache->data) != hipSuccess) st = QVG_ERR_HIP;
+    delete cache;
+    return st;
+}
+
+qvg_status qvg_centroid_cache_data(qvg_centroid_cache *cache, float **centroids, int32_t *valid) {
+    if (!cache || !centroids || !valid) return QVG_ERR_INVALID_ARG;
+    *centroids = cache->data;
+    *valid = cache->valid;
+    return QVG_OK;
+}
+
+static size_t cache_bytes(const qvg_centroid_cache *c) {
+    return (size_t)c->n_stages * c->heads * c->n_centroids * c->d * sizeof(float);
+}
+
+qvg_status qvg_centroid_cache_export(qvg_centroid_cache *cache, float *dst, void *stream) {
+    if (!cache || !dst) return QVG_ERR_INVALID_ARG;
+    if (!cache->valid) return QVG_ERR_STATE;
+    const size_t bytes = cache_bytes(cache);
+    if (bytes)
+        QVG_TRY(hipMemcpyAsync(dst, cache->data, bytes, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)));
+    return QVG_OK;
+}
+
+qvg_status qvg_centroid_cache_import(qvg_centroid_cache *cache, const float *src, void *stream) {
+    if (!cache || !src) return QVG_ERR_INVALID_ARG;
+    const size_t bytes = cache_bytes(cache);
+    if (bytes)
+        QVG_TRY(hipMemcpyAsync(cache->data, src, bytes, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(stream)));
+    cache->valid = 1;
+    return QVG_OK;
+}
+
+qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head_stride, int32_t heads,
+                            int32_t n_tokens, const float *init_centroids, qvg_centroid_cache *cache,
+                            const qvg_cache_view *dst, int32_t chunk_index, void *workspace,
+                            uint64_t workspace_bytes, void *stream) {
+    qvg_status st = check_config(cfg);
+    if (st != QVG_OK) return st;
+    const int H = heads, N = n_tokens, D = cfg->d, K = cfg->n_centroids, T = cfg->n_stages, G = cfg->group_size;
+    const int Kp = padded_k(K);
+    const size_t esz = dtype_size(cfg->dtype);
+    if (H < 1 || N < 1 || !x || !aligned16(x)) return QVG_ERR_INVALID_ARG;
+    if (x_head_stride < (int64_t)N * D || (x_head_stride * (int64_t)esz) % 16 != 0) return QVG_ERR_INVALID_ARG;
+    if (!dst || dst->heads != H || dst->chunk_tokens < 1 || dst->cap_tokens < 1) return QVG_ERR_INVALID_ARG;
+    if (chunk_index < 0 || N > dst->chunk_tokens) return QVG_ERR_INVALID_ARG;
+    const int64_t tok0 = (int64_t)chunk_index * dst->chunk_tokens;
+    if (tok0 + N > dst->cap_tokens) return QVG_ERR_INVALID_ARG;
+    if (!dst->codes || !dst->scales || !aligned16(dst->codes)) return QVG_ERR_INVALID_ARG;
+    if (T > 0 && (!dst->assign || !dst->centroids || !aligned16(dst->centroids))) return QVG_ERR_INVALID_ARG;
+    if (init_centroids && !aligned16(init_centroids)) return QVG_ERR_INVALID_ARG;
+    if (cache && (cache->heads != H || cache->d != D || cache->n_centroids != K || cache->n_stages != T))
+        return QVG_ERR_STATE;
+    const EncodeWorkspace ws(*cfg, H, N);
+    if (!workspace || !aligned16(workspace)) return QVG_ERR_INVALID_ARG;
+    if (workspace_bytes < ws.total) return QVG_ERR_WORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t cap = dst->cap_tokens;
+    const int64_t rstride = (int64_t)N * D;
+    const double HND = (double)H * N * D;
+    float *R = ws.has_R ? at<float>(workspace, ws.R) : nullptr;
+    uint16_t *Rb = ws.has_Rb ? at<uint16_t>(workspace, ws.Rb) : nullptr;
+
+    if (T == 0) {
+        QVG_LAUNCH("group_quant", 0, HND * esz + HND / 4 + HND / G,
+                   launch_residual(D, QUANT_ONLY, x, cfg->dtype, x_head_stride, H, N, nullptr, DT_F32, 0, nullptr, 0,
+                                   nullptr, nullptr, 0, dst->codes + tok0 * (D / 4), dst->scales + tok0 * (D / G),
+                                   cap, G, s));
+        if (cache) cache->valid = 1;
+        return QVG_OK;
+    }
+
+    float *C = at<float>(workspace, ws.C);
+    uint16_t *Cb = at<uint16_t>(workspace, ws.Cb);
+    double *cn = at<double>(workspace, ws.cn);
+    int32_t *counts = at<int32_t>(workspace, ws.counts);
+    int32_t *offsets = at<int32_t>(workspace, ws.offsets);
+    int32_t *order = at<int32_t>(workspace, ws.order);
+    int32_t *idx = at<int32_t>(workspace, ws.idx);
+    const bool warm_cache = cache && cache->valid;
+
+    for (int t = 1; t <= T; ++t) {
+        // R(t-1): the input for stage 1, the fp32 workspace afterwards
+        const void *src = t == 1 ? x : (const void *)R;
+        const int src_dt = t == 1 ? cfg->dtype : QVG_F32;
+        const int64_t src_hs = t == 1 ? x_head_stride : rstride;
+        // bf16 operand of the distance products
+        const uint16_t *opnd;
+        int64_t op_hs;
+        if (t == 1 && cfg->dtype == QVG_BF16) {
+            opnd = static_cast<const uint16_t *>(x);
+            op_hs = x_head_stride;
+        } else {
+            if (t == 1)
+                QVG_LAUNCH("cast_bf16", 0, HND * 6,
+                           launch_cast_bf16(static_cast<const float *>(x), x_head_stride, H, N, D, Rb, s));
+            opnd = Rb;
+            op_hs = rstride;
+        }
+        uint8_t *pi = dst->assign + (size_t)(t - 1) * H * cap + tok0;
+        const size_t slice = (size_t)(t - 1) * H * K * D;
+        const float *warm = init_centroids ? init_centroids + slice : (warm_cache ? cache->data + slice : nullptr);
+        const int iters = warm ? cfg->iters_warm : cfg->iters_cold;
+        const double src_esz = t == 1 ? (double)esz : 4.0;
+        const double table = (double)H * Kp * (D * 2 + 8);
+        const double assign_flops = 2.0 * H * N * K * D, assign_bytes = HND * 2 + H * N + table;
+        const double update_bytes = HND * src_esz + H * N * 4.0 + (double)H * K * D * 4 + table;
+        if (!warm) QVG_LAUNCH("forgy", 0, H * K * 4.0, launch_forgy(H, N, K, cfg->seed, t, idx, s));
+        QVG_LAUNCH("init_centroids", 0, (double)H * K * D * (src_esz + 4) + table,
+                   launch_init_centroids(D, H, K, src, src_dt, src_hs, idx, warm, C, Cb, cn, s));
+        for (int it = 0; it < iters; ++it) {
+            QVG_LAUNCH("assign", assign_flops, assign_bytes,
+                       launch_assign(D, H, N, opnd, op_hs, Cb, cn, Kp, pi, cap, s));
+            QVG_LAUNCH("bucket", 0, H * N * 6.0 + H * Kp * 8.0,
+                       launch_bucket(H, N, Kp, pi, cap, counts, offsets, order, s));
+            QVG_LAUNCH("update", HND, update_bytes,
+                       launch_update(D, H, N, K, src, src_dt, src_hs, counts, offsets, order, C, Cb, cn, s));
+        }
+        QVG_LAUNCH("assign", assign_flops, assign_bytes, launch_assign(D, H, N, opnd, op_hs, Cb, cn, Kp, pi, cap, s));
+        void *cslot = static_cast<char *>(dst->centroids) +
+                      (((size_t)chunk_index * T + (t - 1)) * H * K * D) * esz;
+        QVG_LAUNCH("store_centroids", 0, (double)H * K * D * (4 + esz + (cache ? 4 : 0)),
+                   launch_store_centroids(D, H, K, C, cfg->dtype, cslot, cache ? cache->data + slice : nullptr, s));
+        // the residual uses the stored centroids: the bf16 operand table for bf16
+        // tensors (identical values), the fp32 table otherwise
+        const void *cent = cfg->dtype == QVG_BF16 ? (const void *)Cb : (const void *)C;
+        const int cent_rows = cfg->dtype == QVG_BF16 ? Kp : K;
+        if (t < T) {
+            QVG_LAUNCH("residual", HND, HND * (src_esz + 6) + H * N + (double)H * K * D * esz,
+                       launch_residual(D, RES_WRITE, src, src_dt, src_hs, H, N, cent, cfg->dtype, cent_rows, pi, cap,
+                                       R, Rb, rstride, nullptr, nullptr, 0, G, s));
+        } else {
+            QVG_LAUNCH("residual_quant", HND, HND * src_esz + H * N + (double)H * K * D * esz + HND / 4 + HND / G,
+                       launch_residual(D, RES_QUANT, src, src_dt, src_hs, H, N, cent, cfg->dtype, cent_rows, pi, cap,
+                                       nullptr, nullptr, 0, dst->codes + tok0 * (D / 4),
+                                       dst->scales + tok0 * (D / G), cap, G, s));
+        }
+    }
+    if (cache) cache->valid = 1;
+    return QVG_OK;
+}
+
+qvg_status qvg_decode(const qvg_config *cfg, const qvg_cache_view *src, int64_t tok_begin, int64_t tok_end,
+                      void *out, int64_t out_head_stride, int32_t out_dtype, void *stream) {
+    qvg_status st = check_config(cfg);
+    if (st != QVG_OK) return st;
+    if (!src || src->heads < 1 || src->chunk_tokens < 1 || src->cap_tokens < 1) return QVG_ERR_INVALID_ARG;
+    if (tok_begin < 0 || tok_end <= tok_begin || tok_end > src->cap_tokens) return QVG_ERR_INVALID_ARG;
+    if (!src->codes || !src->scales || !aligned16(src->codes)) return QVG_ERR_INVALID_ARG;
+    if (cfg->n_stages > 0 && (!src->assign || !src->centroids || !aligned16(src->centroids)))
+        return QVG_ERR_INVALID_ARG;
+    if (out_dtype != QVG_F32 && out_dtype != QVG_BF16) return QVG_ERR_INVALID_ARG;
+    const int64_t ntok = tok_end - tok_begin;
+    if (!out || !aligned16(out) || out_head_stride < ntok * cfg->d ||
+        (out_head_stride * (int64_t)dtype_size(out_dtype)) % 16 != 0)
+        return QVG_ERR_INVALID_ARG;
+    if (ntok * (cfg->d / 16) / 256 + 1 > (int64_t)UINT32_MAX / src->heads) return QVG_ERR_UNSUPPORTED;
+    DecodeArgs a;
+    a.codes = src->codes;
+    a.scales = src->scales;
+    a.assign = src->assign;
+    a.cent = src->centroids;
+    a.cent_dtype = cfg->dtype;
+    a.cap = src->cap_tokens;
+    a.chunk_tokens = src->chunk_tokens;
+    a.H = src->heads;
+    a.K = cfg->n_centroids;
+    a.T = cfg->n_stages;
+    a.G = cfg->group_size;
+    a.D = cfg->d;
+    a.tok_begin = tok_begin;
+    a.ntok = ntok;
+    a.out = out;
+    a.out_dtype = out_dtype;
+    a.out_hs = out_head_stride;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t chunks = (tok_end - 1) / a.chunk_tokens - tok_begin / a.chunk_tokens + 1;
+    const double bytes = (double)a.H * ntok * (a.D / 4 + a.D / a.G + a.T + a.D * dtype_size(out_dtype)) +
+                         (double)chunks * a.T * a.H * a.K * a.D * dtype_size(cfg->dtype);
+    QVG_LAUNCH("decode", (double)a.H * ntok * a.D * (a.T + 1), bytes, launch_decode(a, s));
+    return QVG_OK;
+}
+
+qvg_status qvg_kmeans_assign(const void *x, int32_t x_dtype, int64_t x_head_stride, const float *centroids,
+                             int32_t heads, int32_t n_tokens, int32_t d, int32_t n_centroids, uint8_t *assign_out,
+                             int64_t assign_head_stride, void *workspace, uint64_t workspace_bytes, void *stream) {
+    if (heads < 1 || n_tokens < 1 || n_centroids < 1 || n_centroids > QVG_MAX_CENTROIDS) return QVG_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return QVG_ERR_UNSUPPORTED;
+    if (x_dtype != QVG_F32 && x_dtype != QVG_BF16) return QVG_ERR_INVALID_ARG;
+    if (!x || !aligned16(x) || !centroids || !aligned16(centroids) || !assign_out) return QVG_ERR_INVALID_ARG;
+    if (x_head_stride < (int64_t)n_tokens * d || (x_head_stride * (int64_t)dtype_size(x_dtype)) % 16 != 0)
+        return QVG_ERR_INVALID_ARG;
+    if (assign_head_stride < n_tokens) return QVG_ERR_INVALID_ARG;
+    const StageWorkspace ws(heads, n_tokens, d, n_centroids);
+    if (!workspace || !aligned16(workspace)) return QVG_ERR_INVALID_ARG;
+    if (workspace_bytes < ws.total) return QVG_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t *opnd = static_cast<const uint16_t *>(x);
+    int64_t op_hs = x_head_stride;
+    if (x_dtype == QVG_F32) {
+        uint16_t *xb = at<uint16_t>(workspace, ws.Xb);
+        QVG_LAUNCH("cast_bf16", 0, (double)heads * n_tokens * d * 6,
+                   launch_cast_bf16(static_cast<const float *>(x), x_head_stride, heads, n_tokens, d, xb, s));
+        opnd = xb;
+        op_hs = (int64_t)n_tokens * d;
+    }
+    float *C = at<float>(workspace, ws.C);
+    uint16_t *Cb = at<uint16_t>(workspace, ws.Cb);
+    double *cn = at<double>(workspace, ws.cn);
+    const int Kp = padded_k(n_centroids);
+    const double table = (double)heads * Kp * (d * 2 + 8);
+    QVG_LAUNCH("init_centroids", 0, (double)heads * n_centroids * d * 8 + table,
+               launch_init_centroids(d, heads, n_centroids, nullptr, DT_F32, 0, nullptr, centroids, C, Cb, cn, s));
+    QVG_LAUNCH("assign", 2.0 * heads * n_tokens * n_centroids * d, (double)heads * n_tokens * (d * 2 + 1) + table,
+               launch_assign(d, heads, n_tokens, opnd, op_hs, Cb, cn, Kp, assign_out, assign_head_stride, s));
+    return QVG_OK;
+}
+
+qvg_status qvg_centroid_update(const void *x, int32_t x_dtype, int64_t x_head_stride, const uint8_t *assign,
+                               int64_t assign_head_stride, int32_t heads, int32_t n_tokens, int32_t d,
+                               int32_t n_centroids, float *centroids, int32_t *counts_out, void *workspace,
+                               uint64_t workspace_bytes, void *stream) {
+    if (heads < 1 || n_tokens < 1 || n_centroids < 1 || n_centroids > QVG_MAX_CENTROIDS) return QVG_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return QVG_ERR_UNSUPPORTED;
+    if (x_dtype != QVG_F32 && x_dtype != QVG_BF16) return QVG_ERR_INVALID_ARG;
+    if (!x || !aligned16(x) || !centroids || !aligned16(centroids) || !assign) return QVG_ERR_INVALID_ARG;
+    if (x_head_stride < (int64_t)n_tokens * d || (x_head_stride * (int64_t)dtype_size(x_dtype)) % 16 != 0)
+        return QVG_ERR_INVALID_ARG;
+    if (assign_head_stride < n_tokens) return QVG_ERR_INVALID_ARG;
+    const StageWorkspace ws(heads, n_tokens, d, n_centroids);
+    if (!workspace || !aligned16(workspace)) return QVG_ERR_INVALID_ARG;
+    if (workspace_bytes < ws.total) return QVG_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int Kp = padded_k(n_centroids);
+    int32_t *counts = at<int32_t>(workspace, ws.counts);
+    int32_t *offsets = at<int32_t>(workspace, ws.offsets);
+    int32_t *order = at<int32_t>(workspace, ws.order);
+    const double HND = (double)heads * n_tokens * d;
+    QVG_LAUNCH("bucket", 0, heads * n_tokens * 6.0 + heads * Kp * 8.0,
+               launch_bucket(heads, n_tokens, Kp, assign, assign_head_stride, counts, offsets, order, s));
+    QVG_LAUNCH("update", HND,
+               HND * dtype_size(x_dtype) + heads * n_tokens * 4.0 + (double)heads * n_centroids * d * 4 +
+                   (double)heads * Kp * (d * 2 + 8),
+               launch_update(d, heads, n_tokens, n_centroids, x, x_dtype, x_head_stride, counts, offsets, order,
+                          centroids, at<uint16_t>(workspace, ws.Cb), at<double>(workspace, ws.cn), s));
+    if (counts_out)
+        QVG_TRY(hipMemcpy2DAsync(counts_out, (size_t)n_centroids * 4, counts, (size_t)Kp * 4, (size_t)n_centroids * 4,
+                                 heads, hipMemcpyDeviceToDevice, s));
+    return QVG_OK;
+}
+
+qvg_status qvg_group_quant(const float *r, int64_t r_head_stride, int32_t heads, int32_t n_tokens, int32_t d,
+                           int32_t group_size, uint8_t *codes, uint8_t *scales, void *stream) {
+    if (heads < 1 || n_tokens < 1 || group_size < 1) return QVG_ERR_INVALID_ARG;
+    if (d % group_size != 0) return QVG_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return QVG_ERR_UNSUPPORTED;
+    if (group_size != 16 && group_size != 32 && group_size != 64 && group_size != 128) return QVG_ERR_UNSUPPORTED;
+    if (!r || !aligned16(r) || !codes || !aligned16(codes) || !scales) return QVG_ERR_INVALID_ARG;
+    if (r_head_stride < (int64_t)n_tokens * d || (r_head_stride * 4) % 16 != 0) return QVG_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const double HND = (double)heads * n_tokens * d;
+    QVG_LAUNCH("group_quant", 0, HND * 4 + HND / 4 + HND / group_size,
+               launch_residual(d, QUANT_ONLY, r, QVG_F32, r_head_stride, heads, n_tokens, nullptr, DT_F32, 0, nullptr,
+                               0, nullptr, nullptr, 0, codes, scales, n_tokens, group_size, s));
+    return QVG_OK;
+}
+
+qvg_status qvg_profile_enable(int32_t on) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (on) {
+        for (auto &r : g_prof) {
+            g_prof_pool.push_back(r.a);
+            g_prof_pool.push_back(r.b);
+        }
+        g_prof.clear();
+    }
+    g_prof_on = on != 0;
+    return QVG_OK;
+}
+
+qvg_status qvg_profile_read(qvg_kernel_stat *out, int32_t max_entries, int32_t *n_entries) {
+    if (!n_entries || max_entries < 0 || (max_entries > 0 && !out)) return QVG_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    std::vector<qvg_kernel_stat> acc;
+    for (const auto &r : g_prof) {
+        if (hipEventSynchronize(r.b) != hipSuccess) return QVG_ERR_HIP;
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return QVG_ERR_HIP;
+        qvg_kernel_stat *e = nullptr;
+        for (auto &x : acc)
+            if (strncmp(x.name, r.name, sizeof x.name) == 0) e = &x;
+        if (!e) {
+            acc.emplace_back();
+            e = &acc.back();
+            memset(e, 0, sizeof *e);
+            strncpy(e->name, r.name, sizeof e->name - 1);
+        }
+        e->launches += 1;
+        e->total_ms += ms;
+        e->flops += r.flops;
+        e->bytes += r.bytes;
+    }
+    *n_entries = (int32_t)acc.size();
+    for (int32_t i = 0; i < max_entries && i < (int32_t)acc.size(); ++i) out[i] = acc[i];
+    return QVG_OK;
+}
+
+qvg_status qvg_dequant_reconstruct(const qvg_config *cfg, int32_t heads, int32_t n_tokens, const uint8_t *codes,
+                                   const uint8_t *scales, const uint8_t *assign, const void *centroids, void *out,
+                                   int32_t out_dtype, void *stream) {
+    qvg_status st = check_config(cfg);
+    if (st != QVG_OK) return st;
+    if (heads < 1 || n_tokens < 1) return QVG_ERR_INVALID_ARG;
+    qvg_cache_view v;
+    v.codes = const_cast<uint8_t *>(codes);
+    v.scales = const_cast<uint8_t *>(scales);
+    v.assign = const_cast<uint8_t *>(assign);
+    v.centroids = const_cast<void *>(centroids);
+    v.cap_tokens = n_tokens;
+    v.chunk_tokens = n_tokens;
+    v.heads = heads;
+    return qvg_decode(cfg, &v, 0, n_tokens, out, (int64_t)n_tokens * cfg->d, out_dtype, stream);
+}
+
+}  // extern "C"

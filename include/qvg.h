@@ -1,0 +1,262 @@
+/*
+ * qvg.h - C ABI of the Quant VideoGen (QVG) KV-cache codec for AMD MI355X (gfx950).
+ *
+ * The codec compresses the key or value cache of an autoregressive video
+ * diffusion model chunk by chunk and rebuilds it for attention:
+ *
+ *   encode (per head, per chunk of a few latent frames):
+ *     semantic-aware smoothing  = k-means over the chunk's d-dim token rows,
+ *                                 subtract each row's centroid;
+ *     progressive residual stages t = 1..T: R(0) = X, stage t clusters R(t-1)
+ *                                 and yields R(t), centroids C(t), assignment pi(t);
+ *     2-bit group quantisation of R(T) with FP8 E4M3 per-group scales.
+ *   decode: dequantise R(T) and add back C(T)[pi(T)] + ... + C(1)[pi(1)] in one pass.
+ *
+ * Sources: "Quant VideoGen: Auto-Regressive Long Video Generation via 2-Bit
+ * KV-Cache Quantization" as summarised by the 163.com article (sections 3-5 and 7),
+ * and by gist.science (German and Portuguese technical summaries, sections 2A-2C).
+ *
+ * Conventions (all entry points):
+ *  - Every function returns a qvg_status (int32_t).  Arguments are validated on
+ *    the host before anything is launched; a rejected call launches nothing and
+ *    leaves every buffer untouched.  A failed launch returns QVG_ERR_HIP.  A fault
+ *    inside a kernel surfaces at the caller's next synchronisation.
+ *  - Device pointers are caller-owned (allocated by the caller, e.g. through
+ *    PyTorch) and must be 16-byte aligned; head strides are in elements and must
+ *    keep every row 16-byte aligned.  The library allocates device memory only in
+ *    qvg_centroid_cache_create and frees it in qvg_centroid_cache_destroy.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is enqueued
+ *    asynchronously on it; the library never synchronises the device.  Calls that
+ *    share a cache, a destination or a workspace must be ordered on one stream.
+ *  - Input values must be finite.
+ *  - Layouts are row-major; "[H][N][d]" means head-major, then token, then channel.
+ *  - dtype codes: QVG_F32 = fp32, QVG_BF16 = bfloat16 (raw 16-bit storage).
+ */
+#ifndef QVG_H
+#define QVG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t qvg_status;
+enum {
+    QVG_OK = 0,
+    QVG_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size or range        */
+    QVG_ERR_UNSUPPORTED = -2, /* a configuration the kernels do not implement      */
+    QVG_ERR_WORKSPACE = -3,   /* workspace smaller than the *_workspace_bytes query */
+    QVG_ERR_STATE = -4,       /* cache bound to another (config, heads)             */
+    QVG_ERR_HIP = -5,         /* a HIP runtime call or launch failed                */
+    QVG_ERR_OOM = -6          /* device allocation failed (cache creation)          */
+};
+
+enum { QVG_F32 = 0, QVG_BF16 = 1 };
+
+#define QVG_MAX_CENTROIDS 256 /* assignments are stored as uint8 (163.com, section 7) */
+#define QVG_MAX_STAGES 8
+
+/* Codec settings.  The pages fix 256 centroids with uint8 assignments and group
+ * sizes 16 or 64 (163.com article, section 7); the rest are this library's
+ * readings (cold start = Forgy rows from a SplitMix64-keyed shuffle; a fixed
+ * number of Lloyd rounds, then one final assignment).
+ *   d            head dimension: 64 or 128
+ *   n_centroids  K, 1..256
+ *   n_stages     T, 0..8 (T = 0 quantises X directly: the round-to-nearest baseline)
+ *   group_size   G in {16, 32, 64, 128}, dividing d (channels per scale)
+ *   iters_cold   Lloyd rounds when the chunk starts from the seeded draw (>= 0)
+ *   iters_warm   Lloyd rounds when it starts from cached/given centroids (>= 0)
+ *   seed         codec seed; the cold draw of (head h, stage t) is keyed by
+ *                ((seed * 65536 + h) * 64 + t) mod 2^64
+ *   dtype        QVG_BF16 or QVG_F32: the input X and the stored centroids       */
+typedef struct {
+    int32_t d;
+    int32_t n_centroids;
+    int32_t n_stages;
+    int32_t group_size;
+    int32_t iters_cold;
+    int32_t iters_warm;
+    uint64_t seed;
+    int32_t dtype;
+    int32_t reserved; /* must be 0 */
+} qvg_config;
+
+/* The compressed cache of one tensor (K or V) of one layer, caller-allocated.
+ *   codes      [H][cap_tokens][d/4]       uint8, four 2-bit codes per byte, lowest channel in bits 0-1
+ *   scales     [H][cap_tokens][d/G]       uint8, FP8 E4M3FN (OCP) per-group scales
+ *   assign     [T][H][cap_tokens]         uint8 centroid index per token and stage
+ *   centroids  [n_chunks][T][H][K][d]     dtype (bf16 or fp32) stored centroids,
+ *              n_chunks = ceil(cap_tokens / chunk_tokens)
+ * Chunk c holds tokens [c * chunk_tokens, min((c + 1) * chunk_tokens, cap_tokens)).
+ * Buffer sizes: qvg_cache_view_bytes.                                           */
+typedef struct {
+    uint8_t *codes;
+    uint8_t *scales;
+    uint8_t *assign;
+    void *centroids;
+    int64_t cap_tokens;
+    int32_t chunk_tokens;
+    int32_t heads;
+} qvg_cache_view;
+
+/* Streaming centroid cache (163.com article, section 5; gist.science summaries,
+ * section 2C): the final fp32 centroids of every (stage, head) of the last
+ * encoded chunk, used to start the next chunk's k-means.  Opaque. */
+typedef struct qvg_centroid_cache qvg_centroid_cache;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *qvg_status_string(qvg_status status);
+
+/* Validates a configuration without touching the GPU: QVG_OK, QVG_ERR_INVALID_ARG
+ * (out-of-range field) or QVG_ERR_UNSUPPORTED (valid but not implemented). */
+qvg_status qvg_config_validate(const qvg_config *cfg);
+
+/* Bytes one encoded chunk of `heads` x `n_tokens` occupies, by component:
+ * out[0] codes = H*N*d/4, out[1] scales = H*N*d/G, out[2] assignments = T*H*N,
+ * out[3] centroids = T*H*K*d*sizeof(dtype).  Host only. */
+qvg_status qvg_chunk_bytes(const qvg_config *cfg, int32_t heads, int32_t n_tokens, uint64_t out[4]);
+
+/* Sizes of the four buffers of a qvg_cache_view holding `cap_tokens` tokens per
+ * head in chunks of `chunk_tokens`: out[0..3] = codes, scales, assign, centroids.
+ * Host only. */
+qvg_status qvg_cache_view_bytes(const qvg_config *cfg, int32_t heads, int64_t cap_tokens,
+                                int32_t chunk_tokens, uint64_t out[4]);
+
+/* Device workspace qvg_encode_chunk needs for `heads` x `n_tokens`.  Host only. */
+qvg_status qvg_encode_workspace_bytes(const qvg_config *cfg, int32_t heads, int32_t n_tokens,
+                                      uint64_t *bytes);
+
+/* Creates a centroid cache for (cfg, heads) on the current device: one fp32
+ * [T][H][K][d] buffer, marked empty.  QVG_ERR_OOM if the allocation fails. */
+qvg_status qvg_centroid_cache_create(const qvg_config *cfg, int32_t heads, qvg_centroid_cache **out);
+
+/* Marks the cache empty: the next encode through it starts cold. */
+qvg_status qvg_centroid_cache_reset(qvg_centroid_cache *cache);
+
+/* Frees the cache (NULL is accepted).  The caller must make sure no enqueued
+ * work still uses it. */
+qvg_status qvg_centroid_cache_destroy(qvg_centroid_cache *cache);
+
+/* Device pointer to the cache's fp32 [T][H][K][d] centroids and whether they are
+ * valid (1) or not (0).  For inspection and checkpointing. */
+qvg_status qvg_centroid_cache_data(qvg_centroid_cache *cache, float **centroids, int32_t *valid);
+
+/* Checkpointing of the streaming state: copies the cache's fp32 [T][H][K][d]
+ * centroids to / from a caller-owned device buffer on `stream`.  Import marks the
+ * cache valid (the next encode through it starts warm); export of an empty cache
+ * is QVG_ERR_STATE. */
+qvg_status qvg_centroid_cache_export(qvg_centroid_cache *cache, float *dst, void *stream);
+qvg_status qvg_centroid_cache_import(qvg_centroid_cache *cache, const float *src, void *stream);
+
+/* Encodes one chunk of one tensor and writes it into chunk `chunk_index` of `dst`
+ * (163.com article, sections 3-5; gist.science German summary, sections 2A-2C).
+ *   x               device [H][N][d] in cfg->dtype; head h starts at x + h * x_head_stride
+ *                   elements, rows of d contiguous; x_head_stride >= N*d
+ *   heads, n_tokens H = dst->heads, 1 <= N <= dst->chunk_tokens; a chunk shorter than
+ *                   chunk_tokens must be the last one the view can hold
+ *   init_centroids  NULL, or device fp32 [T][H][K][d] starting centroids used
+ *                   like a warm cache (iters_warm rounds)
+ *   cache           NULL (cold start, nothing recorded) or a cache created for
+ *                   (cfg, heads): if it holds centroids they start the k-means
+ *                   (iters_warm rounds), otherwise the seeded draw does
+ *                   (iters_cold); afterwards it holds this chunk's final fp32
+ *                   centroids.  init_centroids, when given, wins over the cache
+ *                   for the start but the cache is still updated.
+ *   workspace       device scratch of at least qvg_encode_workspace_bytes; its
+ *                   contents on entry do not matter
+ * Writes codes, scales, assignments of tokens [chunk_index*chunk_tokens, +N) and
+ * the chunk's centroid block.  QVG_ERR_STATE if `cache` was created for another
+ * (cfg, heads); QVG_ERR_WORKSPACE if workspace_bytes is too small. */
+qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head_stride,
+                            int32_t heads, int32_t n_tokens, const float *init_centroids,
+                            qvg_centroid_cache *cache, const qvg_cache_view *dst,
+                            int32_t chunk_index, void *workspace, uint64_t workspace_bytes,
+                            void *stream);
+
+/* Rebuilds tokens [tok_begin, tok_end) of every head from `src` in one fused pass
+ * (163.com article, sections 4-5: reconstruction in reverse stage order; fused
+ * dequantise-and-centroid kernel; gist.science summaries, section 2C):
+ *   y = (q - 1.5) * scale, then y += C(t)[pi(t)] for t = T .. 1 in fp32,
+ *   written as out_dtype (bf16 round-to-nearest-even, or fp32).
+ *   out   device [H][tok_end - tok_begin][d]; head h at out + h * out_head_stride elements
+ * Requires 0 <= tok_begin < tok_end <= src->cap_tokens; the tokens must have been
+ * encoded. */
+qvg_status qvg_decode(const qvg_config *cfg, const qvg_cache_view *src, int64_t tok_begin,
+                      int64_t tok_end, void *out, int64_t out_head_stride, int32_t out_dtype,
+                      void *stream);
+
+/* ---- stage-level entry points (same conventions), for parity checks and profiling ---- */
+
+/* Workspace the stage-level k-means calls need for (heads, n_tokens, d, K). Host only. */
+qvg_status qvg_stage_workspace_bytes(int32_t heads, int32_t n_tokens, int32_t d,
+                                     int32_t n_centroids, uint64_t *bytes);
+
+/* k-means assignment step (163.com article, section 3; German summary, section 2A):
+ * pi[h][n] = argmin_k |c_k|^2 - 2 <x_n, c_k> with both operands rounded to bf16 and
+ * the products accumulated in fp32 on the matrix cores; ties go to the lowest k.
+ *   x          device [H][N][d] (x_dtype), head stride x_head_stride elements
+ *   centroids  device fp32 [H][K][d]
+ *   assign_out device uint8 [H][N], head stride assign_head_stride */
+qvg_status qvg_kmeans_assign(const void *x, int32_t x_dtype, int64_t x_head_stride,
+                             const float *centroids, int32_t heads, int32_t n_tokens, int32_t d,
+                             int32_t n_centroids, uint8_t *assign_out, int64_t assign_head_stride,
+                             void *workspace, uint64_t workspace_bytes, void *stream);
+
+/* k-means update step (same sections): every centroid with at least one token
+ * becomes the mean of its tokens' unrounded rows (sum in fp64 in ascending token
+ * order, one rounding to fp32); a centroid with none keeps its value.
+ *   centroids  device fp32 [H][K][d], read and overwritten
+ *   counts_out NULL or device int32 [H][K] tokens per centroid */
+qvg_status qvg_centroid_update(const void *x, int32_t x_dtype, int64_t x_head_stride,
+                               const uint8_t *assign, int64_t assign_head_stride, int32_t heads,
+                               int32_t n_tokens, int32_t d, int32_t n_centroids, float *centroids,
+                               int32_t *counts_out, void *workspace, uint64_t workspace_bytes,
+                               void *stream);
+
+/* 2-bit group quantisation (163.com article, section 5): per token and group of G
+ * channels, a = max|r|, scale = E4M3FN(a / 1.5) saturating at 448,
+ * q = [r >= -s] + [r >= 0] + [r >= s], four codes per byte.
+ *   r      device fp32 [H][N][d], head stride r_head_stride elements
+ *   codes  device uint8 [H][N][d/4];  scales device uint8 [H][N][d/G] */
+qvg_status qvg_group_quant(const float *r, int64_t r_head_stride, int32_t heads, int32_t n_tokens,
+                           int32_t d, int32_t group_size, uint8_t *codes, uint8_t *scales,
+                           void *stream);
+
+/* Fused dequantise-and-reconstruct of one chunk's raw arrays (the kernel behind
+ * qvg_decode):
+ *   codes [H][N][d/4], scales [H][N][d/G], assign [T][H][N] uint8,
+ *   centroids [T][H][K][d] (cfg->dtype)  ->  out [H][N][d] (out_dtype), contiguous. */
+qvg_status qvg_dequant_reconstruct(const qvg_config *cfg, int32_t heads, int32_t n_tokens,
+                                   const uint8_t *codes, const uint8_t *scales,
+                                   const uint8_t *assign, const void *centroids, void *out,
+                                   int32_t out_dtype, void *stream);
+
+/* ---- profiling aid: per-kernel timing with HIP events ---- */
+
+/* One kernel's totals since profiling was enabled: launches, summed duration
+ * (ms, between HIP events recorded on the launch stream around each launch),
+ * and the launches' algorithmic work (FLOPs and HBM bytes the operation must
+ * move, counted once). */
+typedef struct {
+    char name[32];
+    int64_t launches;
+    double total_ms;
+    double flops;
+    double bytes;
+} qvg_kernel_stat;
+
+/* on != 0: drop earlier records and bracket every following launch with two
+ * events; on == 0: stop recording (records are kept for qvg_profile_read).
+ * Process-wide; adds two event records per launch while on. */
+qvg_status qvg_profile_enable(int32_t on);
+
+/* Waits for the recorded events and writes up to max_entries per-kernel totals;
+ * *n_entries receives the number of distinct kernels recorded. */
+qvg_status qvg_profile_read(qvg_kernel_stat *out, int32_t max_entries, int32_t *n_entries);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QVG_H */

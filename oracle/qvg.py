@@ -208,13 +208,15 @@ def _store(C: np.ndarray, dtype: str) -> np.ndarray:
 
 def encode_chunk(X: np.ndarray, cfg: CodecConfig, cache: Optional[np.ndarray] = None,
                  init: Optional[np.ndarray] = None, mode: str = "parity",
-                 keep_residuals: bool = False, iters: Optional[int] = None) -> Encoded:
+                 keep_residuals: bool = False, iters: Optional[int] = None,
+                 head_offset: int = 0) -> Encoded:
     """Encode one chunk X [H][N][d] (float32 array holding the input values).
 
     cache: [T][H][K][d] float32 centroids of the previous chunk (warm start,
     iters_warm rounds) or None (cold start: Forgy rows, iters_cold rounds).
     init: explicit starting centroids [T][H][K][d], used like a cache.
-    iters: overrides the round count (tests)."""
+    iters: overrides the round count (tests).
+    head_offset: global index of X's first head (it keys the cold-start draw)."""
     X = np.asarray(X, dtype=F32)
     H, N, d = X.shape
     K, T, G = cfg.n_centroids, cfg.n_stages, cfg.group_size
@@ -235,7 +237,7 @@ def encode_chunk(X: np.ndarray, cfg: CodecConfig, cache: Optional[np.ndarray] = 
             if start is not None:
                 C0 = np.asarray(start[t - 1, h], np.float64)
             else:
-                C0 = R[forgy_indices(N, K, cfg.seed, h, t)]
+                C0 = R[forgy_indices(N, K, cfg.seed, head_offset + h, t)]
             C, lab, hist = lloyd(R, C0, n_it, mode)
             sse[t - 1][h] = hist
             Cs = _store(C, cfg.dtype) if mode == "parity" else C

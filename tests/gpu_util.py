@@ -1,0 +1,97 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI
+and bring results back as NumPy arrays; compare with the oracle under the
+parity rules."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synthkv
+
+DEV = "cuda:0"
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def lib():
+    import bit_vector_quantization_amd as q
+
+    return q
+
+
+def ocfg(p: synthkv.Preset, tensor: str, **kw) -> oracle.CodecConfig:
+    c = dict(d=p.d, n_centroids=p.n_centroids, n_stages=p.n_stages, group_size=p.group_size,
+             iters_cold=p.iters_cold, iters_warm=p.iters_warm, seed=p.codec_seed(tensor), dtype=p.dtype)
+    c.update(kw)
+    return oracle.CodecConfig(**c)
+
+
+def gcfg(oc: oracle.CodecConfig):
+    q = lib()
+    return q.config(oc.d, oc.n_centroids, oc.n_stages, oc.group_size, oc.iters_cold, oc.iters_warm,
+                    oc.seed, oc.dtype)
+
+
+def to_dev(X: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(X, dtype=np.float32))
+    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32).to(DEV)
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy()
+
+
+def gpu_encode_chunks(oc: oracle.CodecConfig, X: np.ndarray, chunk_tokens: int, use_cache=True,
+                      init: np.ndarray | None = None):
+    """Encode X [H][Ntot][d] chunk by chunk on the GPU; returns the CompressedKV."""
+    q = lib()
+    H, Ntot, d = X.shape
+    cfg = gcfg(oc)
+    xd = to_dev(X, oc.dtype)
+    dst = q.CompressedKV(cfg, H, Ntot, chunk_tokens, DEV)
+    enc = q.Encoder(cfg, H, min(chunk_tokens, Ntot), DEV)
+    cache = q.CentroidCache(cfg, H) if use_cache else None
+    ini = None if init is None else torch.from_numpy(np.ascontiguousarray(init, np.float32)).to(DEV)
+    for c in range(-(-Ntot // chunk_tokens)):
+        b, e = c * chunk_tokens, min((c + 1) * chunk_tokens, Ntot)
+        enc.encode(xd[:, b:e], dst, c, cache=cache, init=ini)
+    torch.cuda.synchronize()
+    return dst, cache
+
+
+def fetch(dst, chunk: int, oc: oracle.CodecConfig):
+    """Chunk `chunk` of a CompressedKV as oracle-shaped arrays."""
+    b, e = chunk * dst.chunk_tokens, min((chunk + 1) * dst.chunk_tokens, dst.cap)
+    T = oc.n_stages
+    return dict(codes=to_np(dst.codes[:, b:e]), scales=to_np(dst.scales[:, b:e]),
+                assign=to_np(dst.assign[:T, :, b:e]), centroids=to_np(dst.centroids[chunk, :T]))
+
+
+def distance_table(Xop: np.ndarray, C: np.ndarray) -> np.ndarray:
+    """|c|^2 - 2<x, c> in float64 on bf16-rounded operands."""
+    xb, cb = oracle.bf16_round(Xop), oracle.bf16_round(C)
+    return (cb * cb).sum(1)[None, :] - 2.0 * xb @ cb.T
+
+
+def gap_ok(Xop: np.ndarray, C: np.ndarray, got: np.ndarray, ref: np.ndarray, rel=1e-4):
+    """Where labels differ, the two choices' distances must be within `rel` of
+    |x_b|^2 + max(|c_g|^2, |c_o|^2).  Returns (n_mismatch, worst relative gap)."""
+    mis = np.nonzero(got != ref)[0]
+    if len(mis) == 0:
+        return 0, 0.0
+    xb, cb = oracle.bf16_round(Xop[mis]), oracle.bf16_round(C)
+    cn = (cb * cb).sum(1)
+    D = cn[None, :] - 2.0 * xb @ cb.T
+    g, o = got[mis].astype(int), ref[mis].astype(int)
+    r = np.arange(len(mis))
+    gap = np.abs(D[r, g] - D[r, o])
+    scale = (xb * xb).sum(1) + np.maximum(cn[g], cn[o])
+    return len(mis), float((gap / scale).max())
