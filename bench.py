@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Throughput of the QVG KV-cache codec hot path on one MI355X.
+
+One step = the whole hot path over one 13B-video-model-shaped layer: K and V,
+40 heads x 128 dims, 38,000 tokens (about 5 s of 480p video) in 9 chunks of 3
+latent frames (the last one 560 tokens).  Each tensor is encoded chunk by chunk
+through the streaming centroid cache (first chunk cold: Forgy start, 10 Lloyd
+rounds; later chunks warm: 3 rounds; 256 centroids, 2 progressive stages, 2-bit
+codes in groups of 64 with E4M3 scales), then the fused decode rebuilds the
+whole cache in bf16.  The cache is reset at the start of every step.
+
+`value` is KV vectors encoded per second of step time (a vector = one head's
+128-dim key or value row of one token; 3.04 M per step).  The inputs are
+generated on the device before timing and stay resident in HBM.
+
+Also reported on the same line: encode-only and warm-chunk rates, the fused
+decode's algorithmic GB/s (timed with HIP events around each decode launch on
+its stream), a per-kernel breakdown from the library's event profiler, the
+roofline of the dominant kernel, the long-horizon decode stress (12 heads,
+700 frames, 1.09 M tokens) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix, TFLOP/s
+METRIC = "KV tokens encoded/s (d=128, 256 centroids) + fused decode GB/s vs HBM peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--profile-steps", type=int, default=2,
+                    help="extra steps run with the library's per-kernel event profiler")
+    ap.add_argument("--stress-reps", type=int, default=20,
+                    help="timed decodes of the 1.09M-token cache (0 skips the stress part)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=3, help="heads in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes(H, ntok, d, G, T, K, chunks, out_bytes=2, cent_bytes=2):
+    """Algorithmic HBM bytes of one fused decode: codes, scales, assignments and
+    every touched chunk's centroid tables read once, the output written once."""
+    return H * ntok * (d // 4 + d // G + T + d * out_bytes) + chunks * T * H * K * d * cent_bytes
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this codec shards by head with no exchange, "
+              "so only --gpus 1 is run here", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import bit_vector_quantization_amd as q
+    import synthkv
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    dev = "cuda:0"
+    p = synthkv.PRESETS[3]
+    H, Ntot, d = p.heads, p.n_tokens, p.d
+    K, T, G = p.n_centroids, p.n_stages, p.group_size
+    stream = torch.cuda.current_stream()
+
+    log("generating the layer's K and V on the device")
+    X = {t: torch.cat(list(synthkv.gen_torch(p, t, dev)), dim=1).contiguous() for t in ("K", "V")}
+    torch.cuda.synchronize()
+    cfg = {t: q.config(d, K, T, G, p.iters_cold, p.iters_warm, p.codec_seed(t), p.dtype) for t in ("K", "V")}
+    dst = {t: q.CompressedKV(cfg[t], H, Ntot, p.chunk_tokens, dev) for t in ("K", "V")}
+    cache = {t: q.CentroidCache(cfg[t], H) for t in ("K", "V")}
+    enc = q.Encoder(cfg["K"], H, p.chunk_tokens, dev)
+    out = {t: torch.empty((H, Ntot, d), dtype=torch.bfloat16, device=dev) for t in ("K", "V")}
+    n_chunks = p.n_chunks
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step(marks):
+        for t in ("K", "V"):
+            cache[t].reset()
+            marks.append(("enc", t, -1, ev()))
+            for c in range(n_chunks):
+                b, e = p.chunk_range(c)
+                enc.encode(X[t][:, b:e], dst[t], c, cache=cache[t], stream=stream)
+                marks.append(("enc", t, c, ev()))
+        for t in ("K", "V"):
+            marks.append(("dec0", t, 0, ev()))
+            q.decode(cfg[t], dst[t], 0, Ntot, out=out[t], stream=stream)
+            marks.append(("dec1", t, 0, ev()))
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step([])
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    all_marks = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        m = []
+        step(m)
+        all_marks.append(m)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # event breakdown of the timed steps
+    cold_ms = warm_ms = rag_ms = enc_ms = dec_ms = 0.0
+    dec_launches = 0
+    for m in all_marks:
+        idx = {(k, t, c): e for k, t, c, e in m}
+        for t in ("K", "V"):
+            prev = idx[("enc", t, -1)]
+            for c in range(n_chunks):
+                cur = idx[("enc", t, c)]
+                dt = prev.elapsed_time(cur)
+                b, e = p.chunk_range(c)
+                if c == 0:
+                    cold_ms += dt
+                elif e - b == p.chunk_tokens:
+                    warm_ms += dt
+                else:
+                    rag_ms += dt
+                enc_ms += dt
+                prev = cur
+            dec_ms += idx[("dec0", t, 0)].elapsed_time(idx[("dec1", t, 0)])
+            dec_launches += 1
+    S = args.steps
+    vec_step = 2 * H * Ntot
+    n_warm = sum(1 for c in range(n_chunks) if p.chunk_range(c)[1] - p.chunk_range(c)[0] == p.chunk_tokens) - 1
+    dec_b = decode_bytes(H, Ntot, d, G, T, K, n_chunks)
+    dec_avg_ms = dec_ms / dec_launches
+    decode_gbs = dec_b / (dec_avg_ms * 1e-3) / 1e9
+
+    # reference copy bandwidth on the same tensors (torch copy kernel)
+    src, cpy = out["K"], torch.empty_like(out["K"])
+    for _ in range(3):
+        cpy.copy_(src)
+    e0 = ev()
+    for _ in range(10):
+        cpy.copy_(src)
+    e1 = ev()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 2 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+
+    # per-kernel breakdown with the library's event profiler
+    kernels = {}
+    if args.profile_steps > 0:
+        log(f"profiling {args.profile_steps} steps with per-launch events")
+        q.qvg_profile_enable(True)
+        t1 = time.perf_counter()
+        for _ in range(args.profile_steps):
+            step([])
+        torch.cuda.synchronize()
+        prof_ms_step = (time.perf_counter() - t1) * 1e3 / args.profile_steps
+        q.qvg_profile_enable(False)
+        raw = q.qvg_profile_read()
+        for name, r in raw.items():
+            kernels[name] = dict(launches_per_step=r["launches"] / args.profile_steps,
+                                 avg_us=round(r["avg_ms"] * 1e3, 3),
+                                 ms_per_step=round(r["total_ms"] / args.profile_steps, 4),
+                                 tflops=round(r["flops"] / (r["total_ms"] * 1e-3) / 1e12, 2) if r["flops"] else 0.0,
+                                 gbs=round(r["bytes"] / (r["total_ms"] * 1e-3) / 1e9, 1))
+    else:
+        prof_ms_step = None
+
+    # roofline of the dominant kernel
+    if kernels:
+        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    else:
+        dom = "decode"
+    if dom == "decode":
+        achieved = dec_b / (dec_avg_ms * 1e-3) / 1e9
+        roof = dict(kernel="decode", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    avg_launch_us=round(dec_avg_ms * 1e3, 2), algorithmic_bytes_per_launch=int(dec_b),
+                    timed="HIP events around every decode launch of the timed steps")
+    else:
+        r = raw[dom]
+        if dom == "assign":
+            achieved = r["flops"] / (r["total_ms"] * 1e-3) / 1e12
+            roof = dict(kernel=dom, bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS,
+                        unit="TFLOP/s", frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None)
+        else:
+            achieved = r["bytes"] / (r["total_ms"] * 1e-3) / 1e9
+            roof = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
+        roof.update(avg_launch_us=round(r["avg_ms"] * 1e3, 2),
+                    algorithmic_per_launch=(r["flops"] if dom == "assign" else r["bytes"]) / r["launches"],
+                    timed="HIP events around every launch of the profiled steps (library event profiler)")
+
+    # long-horizon decode stress: 12 heads x 128, 700 frames (1,092,000 tokens)
+    stress = None
+    if args.stress_reps > 0:
+        stress = run_stress(q, synthkv, torch, dev, stream, args.stress_reps)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(p, args.cpu_heads, ms_per_step, vec_step)
+
+    line = {
+        "metric": METRIC,
+        "value": round(vec_step / (ms_per_step * 1e-3), 1),
+        "unit": "KV vectors/s (vector = one head's 128-dim key or value row of one token)",
+        "n_gpus": 1, "steps": S, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded spatio-temporally redundant KV, generated on the device)",
+        "config": {"workload": "13B-shaped layer: K and V, 40 heads x 128, 38,000 tokens in 9 chunks of "
+                               "3 frames (last 560), streaming centroid cache, then full-cache fused decode",
+                   "heads": H, "tokens": Ntot, "d": d, "centroids": K, "stages": T, "group_size": G,
+                   "chunk_tokens": p.chunk_tokens, "iters_cold": p.iters_cold, "iters_warm": p.iters_warm},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "encode": {"ms_per_step": round(enc_ms / S, 4),
+                   "vectors_per_s": round(vec_step / (enc_ms / S * 1e-3), 1),
+                   "warm_chunk_ms": round(warm_ms / (S * 2 * n_warm), 4),
+                   "warm_vectors_per_s": round(H * p.chunk_tokens / (warm_ms / (S * 2 * n_warm) * 1e-3), 1),
+                   "cold_chunk_ms": round(cold_ms / (S * 2), 4),
+                   "ragged_chunk_ms": round(rag_ms / (S * 2), 4)},
+        "decode": {"launch_us": round(dec_avg_ms * 1e3, 2), "algorithmic_bytes": int(dec_b),
+                   "gbs": round(decode_gbs, 1), "frac_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4),
+                   "copy_kernel_gbs": round(copy_gbs, 1)},
+        "decode_stress": stress,
+        "kernels": kernels,
+        "profiled_ms_per_step": None if prof_ms_step is None else round(prof_ms_step, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_stress(q, synthkv, torch, dev, stream, reps):
+    p = synthkv.PRESETS[5]
+    H, Ntot, d, K, T, G = p.heads, p.n_tokens, p.d, p.n_centroids, p.n_stages, p.group_size
+    log(f"decode stress: generating and encoding {p.n_chunks} chunks x 2 tensors ({Ntot} tokens, {H} heads)")
+    t0 = time.perf_counter()
+    outs, res = {}, {}
+    total_b = 0
+    for t in ("K", "V"):
+        cfg = q.config(d, K, T, G, p.iters_cold, p.iters_warm, p.codec_seed(t), p.dtype)
+        dst = q.CompressedKV(cfg, H, Ntot, p.chunk_tokens, dev)
+        cache = q.CentroidCache(cfg, H)
+        enc = q.Encoder(cfg, H, p.chunk_tokens, dev)
+        for c, x in enumerate(synthkv.gen_torch(p, t, dev, frames_per_call=p.chunk_frames)):
+            enc.encode(x, dst, c, cache=cache, stream=stream)
+            if c % 50 == 0:
+                torch.cuda.synchronize()
+                log(f"  {t} chunk {c}/{p.n_chunks}")
+        torch.cuda.synchronize()
+        res[t] = (cfg, dst)
+        outs[t] = torch.empty((H, Ntot, d), dtype=torch.bfloat16, device=dev)
+        total_b += decode_bytes(H, Ntot, d, G, T, K, p.n_chunks)
+        del cache, enc
+    prep_s = time.perf_counter() - t0
+    log(f"decode stress: {reps} timed K+V decodes of the whole cache")
+    for _ in range(2):
+        for t in ("K", "V"):
+            q.decode(res[t][0], res[t][1], 0, Ntot, out=outs[t], stream=stream)
+    times = []
+    for _ in range(reps):
+        for t in ("K", "V"):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            q.decode(res[t][0], res[t][1], 0, Ntot, out=outs[t], stream=stream)
+            b.record(stream)
+            times.append((a, b))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in times) / reps      # K + V per rep
+    gbs = total_b / (ms * 1e-3) / 1e9
+    return {"workload": "K and V, 12 heads x 128, 700 frames of 30x52 (1,092,000 tokens, 234 chunks), "
+                        "2 stages, 256 centroids, G=64; fused decode of the whole cache",
+            "kv_decode_ms": round(ms, 4), "algorithmic_bytes": int(total_b), "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "reps": reps, "setup_s": round(prep_s, 1)}
+
+
+def cpu_baseline(p, heads, gpu_ms_step, vec_step):
+    """The oracle (NumPy, fp64) on heads 0..heads-1 of the same layer: chunk 0
+    cold, chunk 1 warm, and the decode of both, for K and V; extrapolated to
+    the step's mix of 1 cold + 7 warm + 1 ragged chunk and the full decode."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import synthkv
+
+    log(f"cpu baseline: oracle on {heads} heads x 2 chunks x K,V")
+    cold = warm = dec = 0.0
+    for t in ("K", "V"):
+        X = synthkv.gen_numpy(p, t, heads=heads, n_tokens=2 * p.chunk_tokens)
+        oc = oracle.CodecConfig(d=p.d, n_centroids=p.n_centroids, n_stages=p.n_stages, group_size=p.group_size,
+                                iters_cold=p.iters_cold, iters_warm=p.iters_warm, seed=p.codec_seed(t),
+                                dtype=p.dtype)
+        t0 = time.perf_counter()
+        e0 = oracle.encode_chunk(X[:, :p.chunk_tokens], oc)
+        t1 = time.perf_counter()
+        e1 = oracle.encode_chunk(X[:, p.chunk_tokens:], oc, cache=e0.cache)
+        t2 = time.perf_counter()
+        oracle.decode(e0, p.group_size, "bf16")
+        oracle.decode(e1, p.group_size, "bf16")
+        t3 = time.perf_counter()
+        cold += t1 - t0
+        warm += t2 - t1
+        dec += t3 - t2
+    per_head_tensor = lambda s: s / (2 * heads)
+    rag = (p.n_tokens - (p.n_chunks - 1) * p.chunk_tokens) / p.chunk_tokens
+    n_warm = p.n_chunks - 2
+    est = 2 * p.heads * (per_head_tensor(cold) + (n_warm + rag) * per_head_tensor(warm)
+                         + (p.n_chunks - 1 + rag) / 2 * per_head_tensor(dec))
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(vec_step / est, 1), "unit": "KV vectors/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"heads 0..{heads - 1} of K and V: chunk 0 cold + chunk 1 warm encode + their decode "
+                      f"({cold + warm + dec:.1f} s measured), extrapolated to one step "
+                      f"(1 cold + {n_warm} warm + 1 ragged chunk x 40 heads x 2 tensors + full decode)",
+            "measured_s": round(cold + warm + dec, 2), "est_step_s": round(est, 2),
+            "gpu_speedup": round(est / (gpu_ms_step * 1e-3), 1),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+if __name__ == "__main__":
+    main()

@@ -98,8 +98,11 @@ def _load() -> ctypes.CDLL:
 LIB = _load()
 
 
-def status_string(status: int) -> str:
+def qvg_status_string(status: int) -> str:
     return LIB.qvg_status_string(status).decode()
+
+
+status_string = qvg_status_string
 
 
 def _check(status: int, what: str) -> None:
