@@ -29,8 +29,8 @@ Readings taken where the pages are silent (each is also used by the HIP path):
   of Lloyd iterations is run, then one final assignment; ties go to the lowest
   centroid index; an empty cluster keeps its previous centroid.
 * Distances ``|c|^2 - 2<x, c>`` use operands rounded to bf16 ("parity" mode);
-  the centroid update averages the unrounded rows, the sum taken in float64 in
-  ascending token order and the mean rounded once to float32.
+  the centroid update averages the unrounded rows: their exact sum rounded to
+  float64, divided by the count in float64, rounded to float32.
 * Centroids are stored in the input's precision (bf16 for bf16 tensors, fp32
   for fp32); the residual is taken against the stored centroids, in fp32.
 * Quantiser: contiguous groups of G channels within a token row; scale
@@ -105,22 +105,29 @@ def assign(R: np.ndarray, C: np.ndarray, mode: str = "parity") -> np.ndarray:
     return lab
 
 
+def exact_column_sums(rows: np.ndarray) -> np.ndarray:
+    """Sum of each column, computed exactly and rounded once to float64
+    (math.fsum is exactly rounded), so the result does not depend on order."""
+    return np.array([math.fsum(rows[:, j]) for j in range(rows.shape[1])], dtype=np.float64)
+
+
 def update(R: np.ndarray, lab: np.ndarray, C_prev: np.ndarray,
            mode: str = "parity") -> Tuple[np.ndarray, np.ndarray]:
     """New centroid = mean of the rows assigned to it; an empty cluster keeps
-    its previous centroid.  Returns (centroids, counts)."""
+    its previous centroid.  The sum of the rows is exact (rounded once to
+    float64), divided by the count in float64 and, in parity mode, rounded once
+    more to float32.  Returns (centroids, counts)."""
     R = np.asarray(R, np.float64)
     K = C_prev.shape[0]
     C = np.array(C_prev, dtype=np.float64, copy=True)
     counts = np.bincount(lab, minlength=K)
-    order = np.argsort(lab, kind="stable")           # ascending token order per cluster
+    order = np.argsort(lab, kind="stable")
     starts = np.concatenate([[0], np.cumsum(counts)])
     for k in range(K):
         if counts[k] == 0:
             continue
         rows = R[order[starts[k]:starts[k + 1]]]
-        s = np.cumsum(rows, axis=0)[-1]              # sequential float64 sum
-        mean = s / counts[k]
+        mean = exact_column_sums(rows) / counts[k]
         C[k] = mean.astype(F32) if mode == "parity" else mean
     return C, counts
 

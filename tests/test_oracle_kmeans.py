@@ -72,19 +72,37 @@ def test_empty_cluster_keeps_previous_centroid():
     np.testing.assert_allclose(C[0], [1 / 3, 1 / 3])
 
 
-def test_parity_update_is_the_rounded_exact_mean():
+def _rounded_mean(rows):
+    """fp32(fp64(fp64(exact sum) / n)) from rational arithmetic."""
+    exact = sum((Fraction(float(v)) for v in rows), Fraction(0))
+    return np.float32(np.float64(float(exact)) / np.float64(len(rows)))
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp32-cancelling"])
+def test_parity_update_is_the_rounded_exact_mean(kind):
     rng = np.random.default_rng(3)
-    X = bf16_round(rng.standard_normal((500, 16)) * np.array([1.0] * 15 + [300.0]))
+    if kind == "bf16":
+        X = bf16_round(rng.standard_normal((500, 16)) * np.array([1.0] * 15 + [300.0]))
+    else:
+        # fp32 rows whose sums cancel: big values of both signs plus tiny ones
+        X = (rng.standard_normal((500, 16)) * rng.choice([1e-6, 1.0, 1e4], size=(500, 16))).astype(np.float32)
+        X = X.astype(np.float64)
     lab = rng.integers(0, 7, size=500)
     C, counts = update(X, lab, np.zeros((7, 16)), "parity")
     for k in range(7):
         rows = X[lab == k]
         for j in range(16):
-            exact = sum((Fraction(float(v)) for v in rows[:, j]), Fraction(0)) / len(rows)
-            got = Fraction(float(C[k, j]))
-            assert float(C[k, j]) == float(np.float32(C[k, j]))          # an fp32 value
-            ulp = abs(float(np.spacing(np.float32(float(exact)))))
-            assert abs(got - exact) <= Fraction(ulp) * Fraction(1, 2) * (1 + Fraction(1, 1 << 20))
+            assert np.float32(C[k, j]) == _rounded_mean(rows[:, j]), (k, j)
+
+
+def test_update_does_not_depend_on_row_order():
+    rng = np.random.default_rng(4)
+    X = (rng.standard_normal((300, 8)) * rng.choice([1e-7, 1.0, 1e5], size=(300, 8))).astype(np.float32)
+    lab = rng.integers(0, 3, size=300)
+    perm = rng.permutation(300)
+    a, _ = update(X.astype(np.float64), lab, np.zeros((3, 8)), "parity")
+    b, _ = update(X[perm].astype(np.float64), lab[perm], np.zeros((3, 8)), "parity")
+    np.testing.assert_array_equal(a, b)
 
 
 def test_brute_force_optimum_on_separated_blobs():
