@@ -2,12 +2,14 @@
 """Throughput of the QVG KV-cache codec hot path on one MI355X.
 
 One step = the whole hot path over one 13B-video-model-shaped layer: K and V,
-40 heads x 128 dims, 38,000 tokens (about 5 s of 480p video) in 9 chunks of 3
-latent frames (the last one 560 tokens).  Each tensor is encoded chunk by chunk
-through the streaming centroid cache (first chunk cold: Forgy start, 10 Lloyd
-rounds; later chunks warm: 3 rounds; 256 centroids, 2 progressive stages, 2-bit
-codes in groups of 64 with E4M3 scales), then the fused decode rebuilds the
-whole cache in bf16.  The cache is reset at the start of every step.
+40 heads x 128 dims each, 38,000 tokens (about 5 s of 480p video) in 9 chunks
+of 3 latent frames (the last one 560 tokens).  The layer's KV cache is one
+[2][40][38000][128] buffer, so K and V form one 80-head tensor with a uniform
+head stride: each chunk is encoded by one call through the streaming centroid
+cache (first chunk cold: Forgy start, 10 Lloyd rounds; later chunks warm: 3
+rounds; 256 centroids, 2 progressive stages, 2-bit codes in groups of 64 with
+E4M3 scales), then one fused decode rebuilds the whole cache in bf16.  The
+centroid cache is reset at the start of every step.
 
 `value` is KV vectors encoded per second of step time (a vector = one head's
 128-dim key or value row of one token; 3.04 M per step).  The inputs are
@@ -75,13 +77,19 @@ def main():
     stream = torch.cuda.current_stream()
 
     log("generating the layer's K and V on the device")
-    X = {t: torch.cat(list(synthkv.gen_torch(p, t, dev)), dim=1).contiguous() for t in ("K", "V")}
+    # the layer's KV cache as one [2][H][N][d] buffer: K and V form one tensor of
+    # 2H heads with a uniform head stride, encoded and decoded by single calls
+    X = torch.empty((2, H, Ntot, d), dtype=torch.bfloat16, device=dev)
+    for i, t in enumerate(("K", "V")):
+        X[i] = torch.cat(list(synthkv.gen_torch(p, t, dev)), dim=1)
+    X = X.view(2 * H, Ntot, d)
     torch.cuda.synchronize()
-    cfg = {t: q.config(d, K, T, G, p.iters_cold, p.iters_warm, p.codec_seed(t), p.dtype) for t in ("K", "V")}
-    dst = {t: q.CompressedKV(cfg[t], H, Ntot, p.chunk_tokens, dev) for t in ("K", "V")}
-    cache = {t: q.CentroidCache(cfg[t], H) for t in ("K", "V")}
-    enc = q.Encoder(cfg["K"], H, p.chunk_tokens, dev)
-    out = {t: torch.empty((H, Ntot, d), dtype=torch.bfloat16, device=dev) for t in ("K", "V")}
+    HK = 2 * H
+    cfg = q.config(d, K, T, G, p.iters_cold, p.iters_warm, p.codec_seed("K"), p.dtype)
+    dst = q.CompressedKV(cfg, HK, Ntot, p.chunk_tokens, dev)
+    cache = q.CentroidCache(cfg, HK)
+    enc = q.Encoder(cfg, HK, p.chunk_tokens, dev)
+    out = torch.empty((HK, Ntot, d), dtype=torch.bfloat16, device=dev)
     n_chunks = p.n_chunks
 
     def ev():
@@ -90,17 +98,15 @@ def main():
         return e
 
     def step(marks):
-        for t in ("K", "V"):
-            cache[t].reset()
-            marks.append(("enc", t, -1, ev()))
-            for c in range(n_chunks):
-                b, e = p.chunk_range(c)
-                enc.encode(X[t][:, b:e], dst[t], c, cache=cache[t], stream=stream)
-                marks.append(("enc", t, c, ev()))
-        for t in ("K", "V"):
-            marks.append(("dec0", t, 0, ev()))
-            q.decode(cfg[t], dst[t], 0, Ntot, out=out[t], stream=stream)
-            marks.append(("dec1", t, 0, ev()))
+        cache.reset()
+        marks.append(("enc", -1, ev()))
+        for c in range(n_chunks):
+            b, e = p.chunk_range(c)
+            enc.encode(X[:, b:e], dst, c, cache=cache, stream=stream)
+            marks.append(("enc", c, ev()))
+        marks.append(("dec0", 0, ev()))
+        q.decode(cfg, dst, 0, Ntot, out=out, stream=stream)
+        marks.append(("dec1", 0, ev()))
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -123,32 +129,31 @@ def main():
     cold_ms = warm_ms = rag_ms = enc_ms = dec_ms = 0.0
     dec_launches = 0
     for m in all_marks:
-        idx = {(k, t, c): e for k, t, c, e in m}
-        for t in ("K", "V"):
-            prev = idx[("enc", t, -1)]
-            for c in range(n_chunks):
-                cur = idx[("enc", t, c)]
-                dt = prev.elapsed_time(cur)
-                b, e = p.chunk_range(c)
-                if c == 0:
-                    cold_ms += dt
-                elif e - b == p.chunk_tokens:
-                    warm_ms += dt
-                else:
-                    rag_ms += dt
-                enc_ms += dt
-                prev = cur
-            dec_ms += idx[("dec0", t, 0)].elapsed_time(idx[("dec1", t, 0)])
-            dec_launches += 1
+        idx = {(k, c): e for k, c, e in m}
+        prev = idx[("enc", -1)]
+        for c in range(n_chunks):
+            cur = idx[("enc", c)]
+            dt = prev.elapsed_time(cur)
+            b, e = p.chunk_range(c)
+            if c == 0:
+                cold_ms += dt
+            elif e - b == p.chunk_tokens:
+                warm_ms += dt
+            else:
+                rag_ms += dt
+            enc_ms += dt
+            prev = cur
+        dec_ms += idx[("dec0", 0)].elapsed_time(idx[("dec1", 0)])
+        dec_launches += 1
     S = args.steps
-    vec_step = 2 * H * Ntot
+    vec_step = HK * Ntot
     n_warm = sum(1 for c in range(n_chunks) if p.chunk_range(c)[1] - p.chunk_range(c)[0] == p.chunk_tokens) - 1
-    dec_b = decode_bytes(H, Ntot, d, G, T, K, n_chunks)
+    dec_b = decode_bytes(HK, Ntot, d, G, T, K, n_chunks)
     dec_avg_ms = dec_ms / dec_launches
     decode_gbs = dec_b / (dec_avg_ms * 1e-3) / 1e9
 
     # reference copy bandwidth on the same tensors (torch copy kernel)
-    src, cpy = out["K"], torch.empty_like(out["K"])
+    src, cpy = out, torch.empty_like(out)
     for _ in range(3):
         cpy.copy_(src)
     e0 = ev()
@@ -218,18 +223,19 @@ def main():
         "n_gpus": 1, "steps": S, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded spatio-temporally redundant KV, generated on the device)",
-        "config": {"workload": "13B-shaped layer: K and V, 40 heads x 128, 38,000 tokens in 9 chunks of "
-                               "3 frames (last 560), streaming centroid cache, then full-cache fused decode",
-                   "heads": H, "tokens": Ntot, "d": d, "centroids": K, "stages": T, "group_size": G,
+        "config": {"workload": "13B-shaped layer: K and V (one [2][40][38000][128] buffer, 80 heads x 128), "
+                               "38,000 tokens in 9 chunks of 3 frames (last 560), streaming centroid cache, "
+                               "then full-cache fused decode",
+                   "heads": HK, "tokens": Ntot, "d": d, "centroids": K, "stages": T, "group_size": G,
                    "chunk_tokens": p.chunk_tokens, "iters_cold": p.iters_cold, "iters_warm": p.iters_warm},
         "roofline": roof,
         "cpu_baseline": cpu,
         "encode": {"ms_per_step": round(enc_ms / S, 4),
                    "vectors_per_s": round(vec_step / (enc_ms / S * 1e-3), 1),
-                   "warm_chunk_ms": round(warm_ms / (S * 2 * n_warm), 4),
-                   "warm_vectors_per_s": round(H * p.chunk_tokens / (warm_ms / (S * 2 * n_warm) * 1e-3), 1),
-                   "cold_chunk_ms": round(cold_ms / (S * 2), 4),
-                   "ragged_chunk_ms": round(rag_ms / (S * 2), 4)},
+                   "warm_chunk_ms": round(warm_ms / (S * n_warm), 4),
+                   "warm_vectors_per_s": round(HK * p.chunk_tokens / (warm_ms / (S * n_warm) * 1e-3), 1),
+                   "cold_chunk_ms": round(cold_ms / S, 4),
+                   "ragged_chunk_ms": round(rag_ms / S, 4)},
         "decode": {"launch_us": round(dec_avg_ms * 1e3, 2), "algorithmic_bytes": int(dec_b),
                    "gbs": round(decode_gbs, 1), "frac_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4),
                    "copy_kernel_gbs": round(copy_gbs, 1)},
@@ -243,44 +249,41 @@ def main():
 def run_stress(q, synthkv, torch, dev, stream, reps):
     p = synthkv.PRESETS[5]
     H, Ntot, d, K, T, G = p.heads, p.n_tokens, p.d, p.n_centroids, p.n_stages, p.group_size
-    log(f"decode stress: generating and encoding {p.n_chunks} chunks x 2 tensors ({Ntot} tokens, {H} heads)")
+    HK = 2 * H
+    log(f"decode stress: generating and encoding {p.n_chunks} chunks of K+V ({Ntot} tokens, {HK} heads)")
     t0 = time.perf_counter()
-    outs, res = {}, {}
-    total_b = 0
-    for t in ("K", "V"):
-        cfg = q.config(d, K, T, G, p.iters_cold, p.iters_warm, p.codec_seed(t), p.dtype)
-        dst = q.CompressedKV(cfg, H, Ntot, p.chunk_tokens, dev)
-        cache = q.CentroidCache(cfg, H)
-        enc = q.Encoder(cfg, H, p.chunk_tokens, dev)
-        for c, x in enumerate(synthkv.gen_torch(p, t, dev, frames_per_call=p.chunk_frames)):
-            enc.encode(x, dst, c, cache=cache, stream=stream)
-            if c % 50 == 0:
-                torch.cuda.synchronize()
-                log(f"  {t} chunk {c}/{p.n_chunks}")
-        torch.cuda.synchronize()
-        res[t] = (cfg, dst)
-        outs[t] = torch.empty((H, Ntot, d), dtype=torch.bfloat16, device=dev)
-        total_b += decode_bytes(H, Ntot, d, G, T, K, p.n_chunks)
-        del cache, enc
+    cfg = q.config(d, K, T, G, p.iters_cold, p.iters_warm, p.codec_seed("K"), p.dtype)
+    dst = q.CompressedKV(cfg, HK, Ntot, p.chunk_tokens, dev)
+    cache = q.CentroidCache(cfg, HK)
+    enc = q.Encoder(cfg, HK, p.chunk_tokens, dev)
+    gk = synthkv.gen_torch(p, "K", dev, frames_per_call=p.chunk_frames)
+    gv = synthkv.gen_torch(p, "V", dev, frames_per_call=p.chunk_frames)
+    for c, (xk, xv) in enumerate(zip(gk, gv)):
+        enc.encode(torch.cat([xk, xv], dim=0), dst, c, cache=cache, stream=stream)
+        if c % 50 == 0:
+            torch.cuda.synchronize()
+            log(f"  chunk {c}/{p.n_chunks}")
+    torch.cuda.synchronize()
+    del cache, enc
+    out = torch.empty((HK, Ntot, d), dtype=torch.bfloat16, device=dev)
+    total_b = decode_bytes(HK, Ntot, d, G, T, K, p.n_chunks)
     prep_s = time.perf_counter() - t0
-    log(f"decode stress: {reps} timed K+V decodes of the whole cache")
+    log(f"decode stress: {reps} timed decodes of the whole cache")
     for _ in range(2):
-        for t in ("K", "V"):
-            q.decode(res[t][0], res[t][1], 0, Ntot, out=outs[t], stream=stream)
+        q.decode(cfg, dst, 0, Ntot, out=out, stream=stream)
     times = []
     for _ in range(reps):
-        for t in ("K", "V"):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            q.decode(res[t][0], res[t][1], 0, Ntot, out=outs[t], stream=stream)
-            b.record(stream)
-            times.append((a, b))
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        q.decode(cfg, dst, 0, Ntot, out=out, stream=stream)
+        b.record(stream)
+        times.append((a, b))
     torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b) for a, b in times) / reps      # K + V per rep
+    ms = sum(a.elapsed_time(b) for a, b in times) / reps
     gbs = total_b / (ms * 1e-3) / 1e9
-    return {"workload": "K and V, 12 heads x 128, 700 frames of 30x52 (1,092,000 tokens, 234 chunks), "
-                        "2 stages, 256 centroids, G=64; fused decode of the whole cache",
+    return {"workload": "K and V as one 24-head tensor, 128 dims, 700 frames of 30x52 (1,092,000 tokens, "
+                        "234 chunks), 2 stages, 256 centroids, G=64; fused decode of the whole cache",
             "kv_decode_ms": round(ms, 4), "algorithmic_bytes": int(total_b), "gbs": round(gbs, 1),
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "reps": reps, "setup_s": round(prep_s, 1)}
 

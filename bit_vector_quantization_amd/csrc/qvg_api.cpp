@@ -109,49 +109,55 @@ struct ProfScope {
         QVG_TRY(expr);                                         \
     } while (0)
 
-// Carves one workspace into the buffers of the encode stage loop.
+// Carves one workspace into the buffers of the encode stage loop.  The
+// residuals R(t) are never stored: each kernel rebuilds them from the input
+// and the earlier stages' stored centroids and assignments.
 struct EncodeWorkspace {
-    size_t R = 0, Rb = 0, C = 0, Cb = 0, cn = 0, counts = 0, offsets = 0, order = 0, idx = 0, total = 0;
-    bool has_R = false, has_Rb = false;
+    size_t C = 0, Cb = 0, cn = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, total = 0;
 
     EncodeWorkspace(const qvg_config &c, int H, int N) {
         const size_t D = c.d, K = c.n_centroids, Kp = padded_k(c.n_centroids);
         const int T = c.n_stages;
         if (T == 0) { total = 256; return; }
-        has_R = T >= 2;
-        has_Rb = T >= 2 || c.dtype == QVG_F32;
         size_t off = 0;
         auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
-        if (has_R) R = take((size_t)H * N * D * 4);
-        if (has_Rb) Rb = take((size_t)H * N * D * 2);
         C = take((size_t)H * K * D * 4);
         Cb = take((size_t)H * Kp * D * 2);
         cn = take((size_t)H * Kp * 8);
-        counts = take((size_t)H * Kp * 4);
+        cnt = take((size_t)2 * H * Kp * 4);
+        fill = take((size_t)2 * H * Kp * 4);
         offsets = take((size_t)H * Kp * 4);
         order = take((size_t)H * N * 4);
-        idx = take((size_t)H * K * 4);
+        idx = take((size_t)T * H * K * 4);
         total = off;
     }
 };
 
 // Workspace of the stage-level k-means entry points.
 struct StageWorkspace {
-    size_t Xb = 0, C = 0, Cb = 0, cn = 0, counts = 0, offsets = 0, order = 0, total = 0;
+    size_t C = 0, Cb = 0, cn = 0, cnt = 0, fill = 0, offsets = 0, order = 0, total = 0;
     StageWorkspace(int H, int N, int D, int K) {
         const size_t Kp = padded_k(K);
         size_t off = 0;
         auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
-        Xb = take((size_t)H * N * D * 2);
         C = take((size_t)H * K * D * 4);
         Cb = take((size_t)H * Kp * D * 2);
         cn = take((size_t)H * Kp * 8);
-        counts = take((size_t)H * Kp * 4);
+        cnt = take((size_t)H * Kp * 4);
+        fill = take((size_t)H * Kp * 4);
         offsets = take((size_t)H * Kp * 4);
         order = take((size_t)H * N * 4);
         total = off;
     }
 };
+
+Src plain_src(const void *x, int64_t x_hs) {
+    Src s{};
+    s.x = x;
+    s.x_hs = x_hs;
+    s.P = 0;
+    return s;
+}
 
 template <typename T>
 T *at(void *base, size_t off) { return reinterpret_cast<T *>(static_cast<char *>(base) + off); }
@@ -309,16 +315,13 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t cap = dst->cap_tokens;
-    const int64_t rstride = (int64_t)N * D;
     const double HND = (double)H * N * D;
-    float *R = ws.has_R ? at<float>(workspace, ws.R) : nullptr;
-    uint16_t *Rb = ws.has_Rb ? at<uint16_t>(workspace, ws.Rb) : nullptr;
 
+    const Src src0 = plain_src(x, x_head_stride);
     if (T == 0) {
         QVG_LAUNCH("group_quant", 0, HND * esz + HND / 4 + HND / G,
-                   launch_residual(D, QUANT_ONLY, x, cfg->dtype, x_head_stride, H, N, nullptr, DT_F32, 0, nullptr, 0,
-                                   nullptr, nullptr, 0, dst->codes + tok0 * (D / 4), dst->scales + tok0 * (D / G),
-                                   cap, G, s));
+                   launch_quant(D, cfg->dtype, H, N, src0, nullptr, 0, nullptr, 0, dst->codes + tok0 * (D / 4),
+                                dst->scales + tok0 * (D / G), cap, G, s));
         if (cache) cache->valid = 1;
         return QVG_OK;
     }
@@ -326,67 +329,59 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
     float *C = at<float>(workspace, ws.C);
     uint16_t *Cb = at<uint16_t>(workspace, ws.Cb);
     double *cn = at<double>(workspace, ws.cn);
-    int32_t *counts = at<int32_t>(workspace, ws.counts);
+    int32_t *cnt[2] = {at<int32_t>(workspace, ws.cnt), at<int32_t>(workspace, ws.cnt) + (size_t)H * Kp};
+    int32_t *fill[2] = {at<int32_t>(workspace, ws.fill), at<int32_t>(workspace, ws.fill) + (size_t)H * Kp};
     int32_t *offsets = at<int32_t>(workspace, ws.offsets);
     int32_t *order = at<int32_t>(workspace, ws.order);
     int32_t *idx = at<int32_t>(workspace, ws.idx);
     const bool warm_cache = cache && cache->valid;
+    const bool need_draw = !init_centroids && !warm_cache;
+    if (need_draw) QVG_LAUNCH("forgy", 0, (double)T * H * K * 4, launch_forgy(T, H, N, K, cfg->seed, idx, s));
 
+    // R(t-1) is rebuilt from x and the stored centroids / assignments of stages 1..t-1
+    Src src = src0;
+    src.pi_hs = cap;
+    src.K = K;
+    const double table = (double)H * Kp * (D * 2 + 8);
     for (int t = 1; t <= T; ++t) {
-        // R(t-1): the input for stage 1, the fp32 workspace afterwards
-        const void *src = t == 1 ? x : (const void *)R;
-        const int src_dt = t == 1 ? cfg->dtype : QVG_F32;
-        const int64_t src_hs = t == 1 ? x_head_stride : rstride;
-        // bf16 operand of the distance products
-        const uint16_t *opnd;
-        int64_t op_hs;
-        if (t == 1 && cfg->dtype == QVG_BF16) {
-            opnd = static_cast<const uint16_t *>(x);
-            op_hs = x_head_stride;
-        } else {
-            if (t == 1)
-                QVG_LAUNCH("cast_bf16", 0, HND * 6,
-                           launch_cast_bf16(static_cast<const float *>(x), x_head_stride, H, N, D, Rb, s));
-            opnd = Rb;
-            op_hs = rstride;
-        }
         uint8_t *pi = dst->assign + (size_t)(t - 1) * H * cap + tok0;
         const size_t slice = (size_t)(t - 1) * H * K * D;
         const float *warm = init_centroids ? init_centroids + slice : (warm_cache ? cache->data + slice : nullptr);
         const int iters = warm ? cfg->iters_warm : cfg->iters_cold;
-        const double src_esz = t == 1 ? (double)esz : 4.0;
-        const double table = (double)H * Kp * (D * 2 + 8);
-        const double assign_flops = 2.0 * H * N * K * D, assign_bytes = HND * 2 + H * N + table;
-        const double update_bytes = HND * src_esz + H * N * 4.0 + (double)H * K * D * 4 + table;
-        if (!warm) QVG_LAUNCH("forgy", 0, H * K * 4.0, launch_forgy(H, N, K, cfg->seed, t, idx, s));
-        QVG_LAUNCH("init_centroids", 0, (double)H * K * D * (src_esz + 4) + table,
-                   launch_init_centroids(D, H, K, src, src_dt, src_hs, idx, warm, C, Cb, cn, s));
+        // algorithmic traffic: the input row plus one assignment byte per earlier stage
+        const double row_bytes = HND * esz + (double)H * N * (t - 1);
+        const double assign_flops = 2.0 * H * N * K * D;
+        QVG_LAUNCH("init_centroids", 0, (double)H * K * D * (esz + 4) + table,
+                   launch_init_centroids(D, cfg->dtype, H, K, src, idx + (size_t)(t - 1) * H * K, warm, C, Cb, cn,
+                                         cnt[0], fill[0], s));
         for (int it = 0; it < iters; ++it) {
-            QVG_LAUNCH("assign", assign_flops, assign_bytes,
-                       launch_assign(D, H, N, opnd, op_hs, Cb, cn, Kp, pi, cap, s));
-            QVG_LAUNCH("bucket", 0, H * N * 6.0 + H * Kp * 8.0,
-                       launch_bucket(H, N, Kp, pi, cap, counts, offsets, order, s));
-            QVG_LAUNCH("update", HND, update_bytes,
-                       launch_update(D, H, N, K, src, src_dt, src_hs, counts, offsets, order, C, Cb, cn, s));
+            const int c = it & 1;
+            QVG_LAUNCH("assign", assign_flops, row_bytes + H * N + table,
+                       launch_assign(D, cfg->dtype, H, N, src, Cb, cn, Kp, pi, cap, cnt[c], s));
+            QVG_LAUNCH("scatter", 0, H * N * 5.0 + H * Kp * 8.0,
+                       launch_scatter(H, N, Kp, pi, cap, cnt[c], fill[c], offsets, order, s));
+            QVG_LAUNCH("update", HND, row_bytes + H * N * 4.0 + (double)H * K * D * 4 + table,
+                       launch_update(D, cfg->dtype, H, N, K, src, cnt[c], offsets, order, C, Cb, cn, cnt[c ^ 1],
+                                     fill[c ^ 1], s));
         }
-        QVG_LAUNCH("assign", assign_flops, assign_bytes, launch_assign(D, H, N, opnd, op_hs, Cb, cn, Kp, pi, cap, s));
+        QVG_LAUNCH("assign", assign_flops, row_bytes + H * N + table,
+                   launch_assign(D, cfg->dtype, H, N, src, Cb, cn, Kp, pi, cap, nullptr, s));
         void *cslot = static_cast<char *>(dst->centroids) +
                       (((size_t)chunk_index * T + (t - 1)) * H * K * D) * esz;
         QVG_LAUNCH("store_centroids", 0, (double)H * K * D * (4 + esz + (cache ? 4 : 0)),
                    launch_store_centroids(D, H, K, C, cfg->dtype, cslot, cache ? cache->data + slice : nullptr, s));
-        // the residual uses the stored centroids: the bf16 operand table for bf16
-        // tensors (identical values), the fp32 table otherwise
-        const void *cent = cfg->dtype == QVG_BF16 ? (const void *)Cb : (const void *)C;
-        const int cent_rows = cfg->dtype == QVG_BF16 ? Kp : K;
         if (t < T) {
-            QVG_LAUNCH("residual", HND, HND * (src_esz + 6) + H * N + (double)H * K * D * esz,
-                       launch_residual(D, RES_WRITE, src, src_dt, src_hs, H, N, cent, cfg->dtype, cent_rows, pi, cap,
-                                       R, Rb, rstride, nullptr, nullptr, 0, G, s));
+            src.cent[t - 1] = cslot;
+            src.pi[t - 1] = pi;
+            src.P = t;
         } else {
-            QVG_LAUNCH("residual_quant", HND, HND * src_esz + H * N + (double)H * K * D * esz + HND / 4 + HND / G,
-                       launch_residual(D, RES_QUANT, src, src_dt, src_hs, H, N, cent, cfg->dtype, cent_rows, pi, cap,
-                                       nullptr, nullptr, 0, dst->codes + tok0 * (D / 4),
-                                       dst->scales + tok0 * (D / G), cap, G, s));
+            // the residual uses the stored centroids: the bf16 operand table for bf16
+            // tensors (identical values), the fp32 table otherwise
+            const void *cent = cfg->dtype == QVG_BF16 ? (const void *)Cb : (const void *)C;
+            const int cent_rows = cfg->dtype == QVG_BF16 ? Kp : K;
+            QVG_LAUNCH("residual_quant", HND * T, row_bytes + H * N + (double)H * K * D * esz + HND / 4 + HND / G,
+                       launch_quant(D, cfg->dtype, H, N, src, cent, cent_rows, pi, cap, dst->codes + tok0 * (D / 4),
+                                    dst->scales + tok0 * (D / G), cap, G, s));
         }
     }
     if (cache) cache->valid = 1;
@@ -448,24 +443,19 @@ qvg_status qvg_kmeans_assign(const void *x, int32_t x_dtype, int64_t x_head_stri
     if (!workspace || !aligned16(workspace)) return QVG_ERR_INVALID_ARG;
     if (workspace_bytes < ws.total) return QVG_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const uint16_t *opnd = static_cast<const uint16_t *>(x);
-    int64_t op_hs = x_head_stride;
-    if (x_dtype == QVG_F32) {
-        uint16_t *xb = at<uint16_t>(workspace, ws.Xb);
-        QVG_LAUNCH("cast_bf16", 0, (double)heads * n_tokens * d * 6,
-                   launch_cast_bf16(static_cast<const float *>(x), x_head_stride, heads, n_tokens, d, xb, s));
-        opnd = xb;
-        op_hs = (int64_t)n_tokens * d;
-    }
+    const Src src = plain_src(x, x_head_stride);
     float *C = at<float>(workspace, ws.C);
     uint16_t *Cb = at<uint16_t>(workspace, ws.Cb);
     double *cn = at<double>(workspace, ws.cn);
     const int Kp = padded_k(n_centroids);
     const double table = (double)heads * Kp * (d * 2 + 8);
     QVG_LAUNCH("init_centroids", 0, (double)heads * n_centroids * d * 8 + table,
-               launch_init_centroids(d, heads, n_centroids, nullptr, DT_F32, 0, nullptr, centroids, C, Cb, cn, s));
-    QVG_LAUNCH("assign", 2.0 * heads * n_tokens * n_centroids * d, (double)heads * n_tokens * (d * 2 + 1) + table,
-               launch_assign(d, heads, n_tokens, opnd, op_hs, Cb, cn, Kp, assign_out, assign_head_stride, s));
+               launch_init_centroids(d, x_dtype, heads, n_centroids, src, nullptr, centroids, C, Cb, cn, nullptr,
+                                     nullptr, s));
+    QVG_LAUNCH("assign", 2.0 * heads * n_tokens * n_centroids * d,
+               (double)heads * n_tokens * (d * dtype_size(x_dtype) + 1) + table,
+               launch_assign(d, x_dtype, heads, n_tokens, src, Cb, cn, Kp, assign_out, assign_head_stride, nullptr,
+                             s));
     return QVG_OK;
 }
 
@@ -485,19 +475,25 @@ qvg_status qvg_centroid_update(const void *x, int32_t x_dtype, int64_t x_head_st
     if (workspace_bytes < ws.total) return QVG_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int Kp = padded_k(n_centroids);
-    int32_t *counts = at<int32_t>(workspace, ws.counts);
+    int32_t *cnt = at<int32_t>(workspace, ws.cnt);
+    int32_t *fill = at<int32_t>(workspace, ws.fill);
     int32_t *offsets = at<int32_t>(workspace, ws.offsets);
     int32_t *order = at<int32_t>(workspace, ws.order);
     const double HND = (double)heads * n_tokens * d;
-    QVG_LAUNCH("bucket", 0, heads * n_tokens * 6.0 + heads * Kp * 8.0,
-               launch_bucket(heads, n_tokens, Kp, assign, assign_head_stride, counts, offsets, order, s));
+    QVG_LAUNCH("zero", 0, heads * Kp * 8.0, launch_zero(cnt, (int64_t)heads * Kp, s));
+    QVG_LAUNCH("zero", 0, heads * Kp * 8.0, launch_zero(fill, (int64_t)heads * Kp, s));
+    QVG_LAUNCH("count", 0, (double)heads * n_tokens + heads * Kp * 4.0,
+               launch_count(heads, n_tokens, Kp, assign, assign_head_stride, cnt, s));
+    QVG_LAUNCH("scatter", 0, heads * n_tokens * 5.0 + heads * Kp * 8.0,
+               launch_scatter(heads, n_tokens, Kp, assign, assign_head_stride, cnt, fill, offsets, order, s));
     QVG_LAUNCH("update", HND,
                HND * dtype_size(x_dtype) + heads * n_tokens * 4.0 + (double)heads * n_centroids * d * 4 +
                    (double)heads * Kp * (d * 2 + 8),
-               launch_update(d, heads, n_tokens, n_centroids, x, x_dtype, x_head_stride, counts, offsets, order,
-                          centroids, at<uint16_t>(workspace, ws.Cb), at<double>(workspace, ws.cn), s));
+               launch_update(d, x_dtype, heads, n_tokens, n_centroids, plain_src(x, x_head_stride), cnt, offsets,
+                             order, centroids, at<uint16_t>(workspace, ws.Cb), at<double>(workspace, ws.cn), nullptr,
+                             nullptr, s));
     if (counts_out)
-        QVG_TRY(hipMemcpy2DAsync(counts_out, (size_t)n_centroids * 4, counts, (size_t)Kp * 4, (size_t)n_centroids * 4,
+        QVG_TRY(hipMemcpy2DAsync(counts_out, (size_t)n_centroids * 4, cnt, (size_t)Kp * 4, (size_t)n_centroids * 4,
                                  heads, hipMemcpyDeviceToDevice, s));
     return QVG_OK;
 }
@@ -513,8 +509,8 @@ qvg_status qvg_group_quant(const float *r, int64_t r_head_stride, int32_t heads,
     hipStream_t s = static_cast<hipStream_t>(stream);
     const double HND = (double)heads * n_tokens * d;
     QVG_LAUNCH("group_quant", 0, HND * 4 + HND / 4 + HND / group_size,
-               launch_residual(d, QUANT_ONLY, r, QVG_F32, r_head_stride, heads, n_tokens, nullptr, DT_F32, 0, nullptr,
-                               0, nullptr, nullptr, 0, codes, scales, n_tokens, group_size, s));
+               launch_quant(d, QVG_F32, heads, n_tokens, plain_src(r, r_head_stride), nullptr, 0, nullptr, 0, codes,
+                            scales, n_tokens, group_size, s));
     return QVG_OK;
 }
 

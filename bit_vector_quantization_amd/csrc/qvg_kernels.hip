@@ -114,35 +114,105 @@ __device__ __forceinline__ void store16_f32(float *p, const float (&v)[16]) {
     for (int i = 0; i < 4; ++i) q[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
 }
 
+template <typename T>
+__device__ __forceinline__ void load8(const T *p, float (&v)[8]);
+
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, float (&v)[8]) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(p);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float(w[i] << 16);
+        v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+}
+
+template <>
+__device__ __forceinline__ void load8<float>(const float *p, float (&v)[8]) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Channels [c0, c0 + 8) of row n of head h of R(P): the input minus the stored
+// centroids of the P earlier stages, subtracted in stage order in fp32.
+template <int D, typename KVT>
+__device__ __forceinline__ void src_row8(const Src &s, int h, int64_t n, int c0, float (&v)[8]) {
+    load8<KVT>(static_cast<const KVT *>(s.x) + (size_t)h * s.x_hs + (size_t)n * D + c0, v);
+#pragma unroll
+    for (int p = 0; p < MAX_PREV; ++p) {
+        if (p < s.P) {
+            const int k = s.pi[p][(size_t)h * s.pi_hs + n];
+            float c[8];
+            load8<KVT>(static_cast<const KVT *>(s.cent[p]) + ((size_t)h * s.K + k) * D + c0, c);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = v[i] - c[i];
+        }
+    }
+}
+
+// The same 8 channels rounded to bf16 and packed for the matrix cores.
+template <int D, typename KVT>
+__device__ __forceinline__ uint4 src_row8_bf16(const Src &s, int h, int64_t n, int c0) {
+    if constexpr (sizeof(KVT) == 2) {
+        if (s.P == 0)   // the input itself is the operand
+            return *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(s.x) + (size_t)h * s.x_hs +
+                                                    (size_t)n * D + c0);
+    }
+    float v[8];
+    src_row8<D, KVT>(s, h, n, c0, v);
+    return make_uint4(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16),
+                      f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16), f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16));
+}
+
+#define QVG_DISPATCH_DT(D, dtype, ...)                          \
+    do {                                                        \
+        if (D == 128) {                                         \
+            constexpr int DD = 128;                             \
+            if (dtype == DT_BF16) { using KVT = uint16_t; __VA_ARGS__; } \
+            else { using KVT = float; __VA_ARGS__; }           \
+        } else {                                                \
+            constexpr int DD = 64;                              \
+            if (dtype == DT_BF16) { using KVT = uint16_t; __VA_ARGS__; } \
+            else { using KVT = float; __VA_ARGS__; }           \
+        }                                                       \
+    } while (0)
+
 // ---------------------------------------------------------------------------
 // cold start: Forgy rows from a keyed partial Fisher-Yates shuffle
 // ---------------------------------------------------------------------------
 
-// SplitMix64 (Steele, Lea & Flood, OOPSLA 2014).
-__device__ __forceinline__ uint64_t splitmix64(uint64_t &s) {
-    s += 0x9E3779B97F4A7C15ull;
-    uint64_t z = s;
+constexpr uint64_t SPLITMIX_GAMMA = 0x9E3779B97F4A7C15ull;
+
+// SplitMix64 (Steele, Lea & Flood, OOPSLA 2014): output i of a stream keyed by
+// `key` is the finaliser applied to key + (i + 1) * gamma.
+__device__ __forceinline__ uint64_t splitmix64_at(uint64_t key, uint64_t i) {
+    uint64_t z = key + (i + 1) * SPLITMIX_GAMMA;
     z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
     z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
     return z ^ (z >> 31);
 }
 
-// One wave per head.  Step i of the shuffle swaps a[i] with a[j], j = i + r mod
-// (N - i); only displaced positions are kept, in a small LDS table searched by
-// the whole wave, so the cost does not depend on N.
-constexpr int FORGY_TABLE = 256;   // at most one new displaced position per step, K <= 256 steps
+constexpr int FORGY_TABLE = 256;   // K <= 256 steps, at most one new displaced position each
 
-__global__ __launch_bounds__(64) void k_forgy(int N, int K, uint64_t seed, int stage, int32_t *idx) {
+// One wave per (head, stage).  Step i of the shuffle swaps a[i] with a[j_i],
+// j_i = i + r_i mod (N - i).  The draws are independent of the shuffle, so the
+// wave computes all j_i at once; the swaps then run in order, keeping only the
+// displaced positions in a small LDS table searched by the whole wave.
+__global__ __launch_bounds__(64) void k_forgy(int H, int N, int K, uint64_t seed, int32_t *idx) {
     __shared__ int32_t keys[FORGY_TABLE];
     __shared__ int32_t vals[FORGY_TABLE];
     __shared__ int32_t sel[FORGY_TABLE];
-    const int h = blockIdx.x, lane = threadIdx.x;
-    uint64_t st = (seed * 65536ull + (uint64_t)h) * 64ull + (uint64_t)stage;
+    __shared__ int32_t jv[FORGY_TABLE];
+    const int h = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+    const uint64_t key = (seed * 65536ull + (uint64_t)h) * 64ull + (uint64_t)(t + 1);
     const int steps = K < N ? K : N;
+    for (int i = lane; i < steps; i += 64) jv[i] = i + (int)(splitmix64_at(key, (uint64_t)i) % (uint64_t)(N - i));
+    __syncthreads();
     int n_ent = 0;
     for (int i = 0; i < steps; ++i) {
-        const uint64_t r = splitmix64(st);
-        const int j = i + (int)(r % (uint64_t)(N - i));
+        const int j = jv[i];
         int vi_l = i, vj_l = j, ej_l = -1;
         bool fi = false, fj = false;
         for (int e = lane; e < n_ent; e += 64) {
@@ -164,108 +234,71 @@ __global__ __launch_bounds__(64) void k_forgy(int N, int K, uint64_t seed, int s
         __syncthreads();
     }
     // fewer tokens than centroids: entry k repeats entry k mod N
-    int32_t *out = idx + (size_t)h * K;
+    int32_t *out = idx + ((size_t)t * H + h) * K;
     for (int k = lane; k < K; k += 64) out[k] = sel[k < steps ? k : k % N];
 }
 
-hipError_t launch_forgy(int H, int N, int K, uint64_t seed, int stage, int32_t *idx, hipStream_t s) {
-    hipLaunchKernelGGL(k_forgy, dim3(H), dim3(64), 0, s, N, K, seed, stage, idx);
+hipError_t launch_forgy(int T, int H, int N, int K, uint64_t seed, int32_t *idx, hipStream_t s) {
+    hipLaunchKernelGGL(k_forgy, dim3(H, T), dim3(64), 0, s, H, N, K, seed, idx);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// starting centroids -> C (fp32), Cb (bf16 operand), cnorm = |Cb|^2 (fp64; exact for
-// the value ranges met in practice, every square of a bf16 being exact)
+// centroid rows: C (fp32), Cb (bf16 operand), cnorm = |Cb|^2 (fp64)
 // ---------------------------------------------------------------------------
 
-template <int D, typename SrcT>
-__device__ __forceinline__ void load_row_part(const SrcT *row, int lane, float (&v)[D / 64]);
-
-template <>
-__device__ __forceinline__ void load_row_part<128, uint16_t>(const uint16_t *row, int lane, float (&v)[2]) {
-    uint32_t w = reinterpret_cast<const uint32_t *>(row)[lane];
-    v[0] = __uint_as_float(w << 16);
-    v[1] = __uint_as_float(w & 0xFFFF0000u);
-}
-template <>
-__device__ __forceinline__ void load_row_part<128, float>(const float *row, int lane, float (&v)[2]) {
-    float2 f = reinterpret_cast<const float2 *>(row)[lane];
-    v[0] = f.x;
-    v[1] = f.y;
-}
-template <>
-__device__ __forceinline__ void load_row_part<64, uint16_t>(const uint16_t *row, int lane, float (&v)[1]) {
-    v[0] = bf16_to_f32(row[lane]);
-}
-template <>
-__device__ __forceinline__ void load_row_part<64, float>(const float *row, int lane, float (&v)[1]) {
-    v[0] = row[lane];
-}
-
-// Writes one centroid row (C, Cb, cnorm) from the lane's D/64 values.
+// Lanes 0 .. D/8-1 of a wave own 8 channels each of centroid k of head h.
 template <int D>
-__device__ __forceinline__ void write_centroid(int h, int k, int K, int Kp, int lane, const float (&v)[D / 64],
-                                               float *C, uint16_t *Cb, double *cnorm) {
-    constexpr int P = D / 64;
+__device__ __forceinline__ void write_centroid8(int h, int k, int K, int Kp, int lane, const float (&v)[8],
+                                                float *C, uint16_t *Cb, double *cnorm) {
     double sq = 0.0;
-    uint32_t b[P];
+    if (lane < D / 8) {
+        uint32_t b[8];
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-        b[i] = f32_to_bf16(v[i]);
-        double bd = (double)bf16_to_f32(b[i]);
-        sq += bd * bd;
-    }
-    float *c = C + ((size_t)h * K + k) * D + lane * P;
-    uint16_t *cb = Cb + ((size_t)h * Kp + k) * D + lane * P;
-    if constexpr (P == 2) {
-        reinterpret_cast<float2 *>(c)[0] = make_float2(v[0], v[1]);
-        reinterpret_cast<uint32_t *>(cb)[0] = b[0] | (b[1] << 16);
-    } else {
-        c[0] = v[0];
-        cb[0] = (uint16_t)b[0];
+        for (int i = 0; i < 8; ++i) {
+            b[i] = f32_to_bf16(v[i]);
+            const double bd = (double)bf16_to_f32(b[i]);
+            sq += bd * bd;
+        }
+        float4 *c = reinterpret_cast<float4 *>(C + ((size_t)h * K + k) * D + lane * 8);
+        c[0] = make_float4(v[0], v[1], v[2], v[3]);
+        c[1] = make_float4(v[4], v[5], v[6], v[7]);
+        *reinterpret_cast<uint4 *>(Cb + ((size_t)h * Kp + k) * D + lane * 8) =
+            make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
     }
     sq = wave_sum(sq);
     if (lane == 0) cnorm[(size_t)h * Kp + k] = sq;
 }
 
-template <int D, typename SrcT>
-__global__ __launch_bounds__(64) void k_init_centroids(int K, int Kp, const SrcT *src, int64_t src_hs,
-                                                       const int32_t *idx, const float *warm, float *C,
-                                                       uint16_t *Cb, double *cnorm) {
-    constexpr int P = D / 64;
+template <int D, typename KVT>
+__global__ __launch_bounds__(64) void k_init_centroids(int K, int Kp, Src src, const int32_t *idx, const float *warm,
+                                                       float *C, uint16_t *Cb, double *cnorm, int32_t *cnt0,
+                                                       int32_t *fill0) {
     const int k = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+    if (lane == 0 && cnt0) {
+        cnt0[(size_t)h * Kp + k] = 0;
+        fill0[(size_t)h * Kp + k] = 0;
+    }
     if (k >= K) {  // padding rows: never chosen
-        uint16_t *cb = Cb + ((size_t)h * Kp + k) * D + lane * P;
-#pragma unroll
-        for (int i = 0; i < P; ++i) cb[i] = 0;
+        if (lane < D / 8) *reinterpret_cast<uint4 *>(Cb + ((size_t)h * Kp + k) * D + lane * 8) = make_uint4(0, 0, 0, 0);
         if (lane == 0) cnorm[(size_t)h * Kp + k] = __builtin_inf();
         return;
     }
-    float v[P];
-    if (warm) {
-        const float *w = warm + ((size_t)h * K + k) * D;
-        load_row_part<D, float>(w, lane, v);
-    } else {
-        const int n = idx[(size_t)h * K + k];
-        load_row_part<D, SrcT>(src + (size_t)h * src_hs + (size_t)n * D, lane, v);
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (lane < D / 8) {
+        if (warm) load8<float>(warm + ((size_t)h * K + k) * D + lane * 8, v);
+        else src_row8<D, KVT>(src, h, idx[(size_t)h * K + k], lane * 8, v);
     }
-    write_centroid<D>(h, k, K, Kp, lane, v, C, Cb, cnorm);
+    write_centroid8<D>(h, k, K, Kp, lane, v, C, Cb, cnorm);
 }
 
-hipError_t launch_init_centroids(int D, int H, int K, const void *src, int src_dtype, int64_t src_hs,
-                                 const int32_t *idx, const float *warm, float *C, uint16_t *Cb, double *cnorm,
-                                 hipStream_t s) {
+hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src, const int32_t *idx,
+                                 const float *warm, float *C, uint16_t *Cb, double *cnorm, int32_t *cnt0,
+                                 int32_t *fill0, hipStream_t s) {
     const int Kp = padded_k(K);
-    dim3 g(Kp, H), b(64);
-#define QVG_INIT(DD, TT)                                                                                      \
-    hipLaunchKernelGGL((k_init_centroids<DD, TT>), g, b, 0, s, K, Kp, (const TT *)src, src_hs, idx, warm, C, \
-                       Cb, cnorm)
-    if (D == 128) {
-        if (src_dtype == DT_BF16) QVG_INIT(128, uint16_t); else QVG_INIT(128, float);
-    } else {
-        if (src_dtype == DT_BF16) QVG_INIT(64, uint16_t); else QVG_INIT(64, float);
-    }
-#undef QVG_INIT
+    QVG_DISPATCH_DT(D, dtype,
+                    hipLaunchKernelGGL((k_init_centroids<DD, KVT>), dim3(Kp, H), dim3(64), 0, s, K, Kp, src, idx,
+                                       warm, C, Cb, cnorm, cnt0, fill0));
     return hipGetLastError();
 }
 
@@ -278,50 +311,47 @@ hipError_t launch_init_centroids(int D, int H, int K, const void *src, int src_d
 // Lane l feeds row/column (l % 16) and channels 8*(l/16) .. +7 of the k-step for
 // both operands, so the two sides pair the same channels whatever the order of
 // the hardware's reduction.  The 16x16 result leaves centroid 4*(l/16)+r of
-// token l%16 in accumulator r of lane l, so each lane keeps the two smallest
-// fp32 distances of one token over its centroids and four lanes merge them.
+// token l%16 in accumulator r of lane l, so each lane keeps the two nearest of
+// its centroids for one token and four lanes merge them.
 //
 // fp32 accumulation can misorder two centroids whose distances differ by a few
-// fp32 ulps.  The final choice between the two best is therefore made on exact
-// distances: every bf16 x bf16 product is exact in fp64 and the 128-term sums
-// and |c|^2 are exact in fp64 for the value ranges met in practice, so the
-// decision is that of the exactly computed |c|^2 - 2<x, c>, lowest index on ties.
+// fp32 ulps.  The final choice between the two best is therefore made on fp64
+// distances: every bf16 x bf16 product is exact in fp64 and the sums are exact
+// for the value ranges met in practice, so the decision is that of the exact
+// |c|^2 - 2<x, c>, lowest index on ties.
 //
-// A workgroup is 4 waves x 64 tokens; the head's bf16 centroid table (swizzled
-// 16-byte chunks) and its norms (fp32 and fp64) sit in LDS.
+// A workgroup is 4 waves x 64 tokens of one head; the head's bf16 centroid
+// table (swizzled 16-byte chunks) and its norms (fp32 and fp64) sit in LDS.
+// The table is fetched with all of a thread's loads in flight at once, and the
+// four token blocks of a wave run as four independent accumulator chains.
 
 constexpr int ASSIGN_TB = 4;  // 16-token blocks per wave
 
-__device__ __forceinline__ bool lex_less(float a, int ka, float b, int kb) {
-    return a < b || (a == b && ka < kb);
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void k_assign(const uint16_t *__restrict__ xb, int64_t x_hs, int N,
-                                                const uint16_t *__restrict__ Cb, const double *__restrict__ cnorm,
-                                                int Kp, uint8_t *__restrict__ pi, int64_t pi_hs) {
-    constexpr int KS = D / 32;   // k-steps
-    constexpr int CH = D / 8;    // 16-byte chunks per row
+template <int D, typename KVT>
+__global__ __launch_bounds__(256) void k_assign(Src src, int N, const uint16_t *__restrict__ Cb,
+                                                const double *__restrict__ cnorm, int Kp, uint8_t *__restrict__ pi,
+                                                int64_t pi_hs, int32_t *__restrict__ counts) {
+    constexpr int KS = D / 32;          // k-steps
+    constexpr int CH = D / 8;           // 16-byte chunks per row
+    constexpr int STAGE = 256 * CH / 256;  // table chunks per thread at 256 centroids
     extern __shared__ uint4 lds[];
     const int h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, r16 = lane & 15;
 
+    // centroid table: every load in flight before the first LDS write
     const uint4 *csrc = reinterpret_cast<const uint4 *>(Cb + (size_t)h * Kp * D);
-    for (int i = tid; i < Kp * CH; i += 256) {
-        int row = i / CH, q = i - row * CH;
-        lds[row * CH + (q ^ (row & (CH - 1)))] = csrc[i];
+    const int nch = Kp * CH;
+    uint4 st[STAGE];
+#pragma unroll
+    for (int u = 0; u < STAGE; ++u) {
+        const int i = tid + 256 * u;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (i < nch) v = csrc[i];
+        st[u] = v;
     }
-    double *lcn64 = reinterpret_cast<double *>(lds + Kp * CH);
-    float *lcn = reinterpret_cast<float *>(lcn64 + Kp);
-    for (int i = tid; i < Kp; i += 256) {
-        const double c = cnorm[(size_t)h * Kp + i];
-        lcn64[i] = c;
-        lcn[i] = (float)c;
-    }
-
+    // token operands
     const int tok0 = blockIdx.x * (64 * ASSIGN_TB) + wave * 64;
-    const uint16_t *xh = xb + (size_t)h * x_hs;
     bf16x8_t bt[ASSIGN_TB][KS];
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
@@ -329,19 +359,56 @@ __global__ __launch_bounds__(256) void k_assign(const uint16_t *__restrict__ xb,
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (n < N) v = *reinterpret_cast<const uint4 *>(xh + (size_t)n * D + 32 * s + 8 * g);
+            if (n < N) v = src_row8_bf16<D, KVT>(src, h, n, 32 * s + 8 * g);
             bt[b][s] = __builtin_bit_cast(bf16x8_t, v);
         }
     }
-    __syncthreads();
-
-    float v1[ASSIGN_TB], v2[ASSIGN_TB];
-    int k1[ASSIGN_TB], k2[ASSIGN_TB];
+#pragma unroll
+    for (int u = 0; u < STAGE; ++u) {
+        const int i = tid + 256 * u;
+        if (i < nch) {
+            const int row = i / CH, q = i - row * CH;
+            lds[row * CH + (q ^ (row & (CH - 1)))] = st[u];
+        }
+    }
+    double *lcn64 = reinterpret_cast<double *>(lds + Kp * CH);
+    float *lhcn = reinterpret_cast<float *>(lcn64 + Kp);
+    if (tid < Kp) {
+        const double c = cnorm[(size_t)h * Kp + tid];
+        lcn64[tid] = c;
+        lhcn[tid] = -0.5f * (float)c;
+    }
+    // per token: hb = -(|x|^2 (1 + 2^-16) + 2^-100) / 2, so that every accumulator
+    // below, dot - (|c|^2 + B) / 2 = -(|x - c|^2 + margin) / 2, is negative (a
+    // near-zero distance that rounds positive still ranks first)
+    float hb[ASSIGN_TB];
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
-        v1[b] = v2[b] = __builtin_inff();
-        k1[b] = k2[b] = 0;
+        float xx = 0.f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const uint4 xv = __builtin_bit_cast(uint4, bt[b][s]);
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = __uint_as_float(xw[i] << 16), hi = __uint_as_float(xw[i] & 0xFFFF0000u);
+                xx = fmaf(lo, lo, xx);
+                xx = fmaf(hi, hi, xx);
+            }
+        }
+        xx += __shfl_xor(xx, 16);
+        xx += __shfl_xor(xx, 32);
+        hb[b] = -0.5f * fmaf(xx, 0x1.0001p+0f, 0x1p-100f);
     }
+    __syncthreads();
+
+    // The two best centroids of each (lane, token) as packed keys: the bits of
+    // a negative fp32 value grow with its magnitude, so bits(acc) with the low
+    // byte replaced by the centroid index orders like the distance (to 15
+    // mantissa bits) with ties going to the lower index.
+    uint32_t q1[ASSIGN_TB], q2[ASSIGN_TB];
+#pragma unroll
+    for (int b = 0; b < ASSIGN_TB; ++b) q1[b] = q2[b] = 0xFFFFFFFFu;
 
     const int ncb = Kp / 16;
     for (int cb = 0; cb < ncb; ++cb) {
@@ -350,45 +417,36 @@ __global__ __launch_bounds__(256) void k_assign(const uint16_t *__restrict__ xb,
 #pragma unroll
         for (int s = 0; s < KS; ++s)
             a[s] = __builtin_bit_cast(bf16x8_t, lds[row * CH + ((4 * s + g) ^ (row & (CH - 1)))]);
-        const float4 cn = *reinterpret_cast<const float4 *>(lcn + cb * 16 + 4 * g);
-        const float cnv[4] = {cn.x, cn.y, cn.z, cn.w};
+        const float4 cn = *reinterpret_cast<const float4 *>(lhcn + cb * 16 + 4 * g);
+        f32x4_t acc[ASSIGN_TB];
+#pragma unroll
+        for (int b = 0; b < ASSIGN_TB; ++b) acc[b] = f32x4_t{cn.x + hb[b], cn.y + hb[b], cn.z + hb[b], cn.w + hb[b]};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int b = 0; b < ASSIGN_TB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bt[b][s], acc[b], 0, 0, 0);
+        const uint32_t kb = (uint32_t)(cb * 16 + 4 * g);
 #pragma unroll
         for (int b = 0; b < ASSIGN_TB; ++b) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < KS; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bt[b][s], acc, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                // centroids reach a lane in increasing index order: strict < keeps the lower index
-                const float d = cnv[r] - 2.0f * acc[r];
-                const int k = cb * 16 + 4 * g + r;
-                const bool lt1 = d < v1[b], lt2 = d < v2[b];
-                v2[b] = lt1 ? v1[b] : (lt2 ? d : v2[b]);
-                k2[b] = lt1 ? k1[b] : (lt2 ? k : k2[b]);
-                v1[b] = lt1 ? d : v1[b];
-                k1[b] = lt1 ? k : k1[b];
+                const uint32_t key = (__float_as_uint(acc[b][r]) & 0xFFFFFF00u) | (kb + r);
+                q2[b] = min(q2[b], max(q1[b], key));
+                q1[b] = min(q1[b], key);
             }
         }
     }
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
-        // merge the four lanes' top-2 lists of each token
+        // merge the four lanes' top-2 keys of each token
 #pragma unroll
         for (int o = 16; o <= 32; o <<= 1) {
-            const float w1 = __shfl_xor(v1[b], o), w2 = __shfl_xor(v2[b], o);
-            const int j1 = __shfl_xor(k1[b], o), j2 = __shfl_xor(k2[b], o);
-            if (lex_less(w1, j1, v1[b], k1[b])) {
-                if (!lex_less(v1[b], k1[b], w2, j2)) { v2[b] = w2; k2[b] = j2; }
-                else { v2[b] = v1[b]; k2[b] = k1[b]; }
-                v1[b] = w1;
-                k1[b] = j1;
-            } else if (lex_less(w1, j1, v2[b], k2[b])) {
-                v2[b] = w1;
-                k2[b] = j1;
-            }
+            const uint32_t w1 = __shfl_xor(q1[b], o), w2 = __shfl_xor(q2[b], o);
+            q2[b] = min(max(q1[b], w1), min(q2[b], w2));
+            q1[b] = min(q1[b], w1);
         }
-        // exact distances of the two candidates: each lane sums its 32 channels
-        const int c1 = k1[b], c2 = k2[b];
+        // fp64 distances of the two candidates: each lane sums its 32 channels
+        const int c1 = (int)(q1[b] & 0xFFu), c2 = (int)(q2[b] & 0xFFu);
         double p1 = 0.0, p2 = 0.0;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -400,7 +458,8 @@ __global__ __launch_bounds__(256) void k_assign(const uint16_t *__restrict__ xb,
             const uint32_t bw[4] = {a2.x, a2.y, a2.z, a2.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const double xl = (double)__uint_as_float(xw[i] << 16), xh2 = (double)__uint_as_float(xw[i] & 0xFFFF0000u);
+                const double xl = (double)__uint_as_float(xw[i] << 16);
+                const double xh2 = (double)__uint_as_float(xw[i] & 0xFFFF0000u);
                 p1 = fma(xl, (double)__uint_as_float(aw[i] << 16), p1);
                 p1 = fma(xh2, (double)__uint_as_float(aw[i] & 0xFFFF0000u), p1);
                 p2 = fma(xl, (double)__uint_as_float(bw[i] << 16), p2);
@@ -414,44 +473,53 @@ __global__ __launch_bounds__(256) void k_assign(const uint16_t *__restrict__ xb,
         const double e1 = lcn64[c1] - 2.0 * p1, e2 = lcn64[c2] - 2.0 * p2;
         const int best = (e2 < e1 || (e2 == e1 && c2 < c1)) ? c2 : c1;
         const int n = tok0 + 16 * b + r16;
-        if (g == 0 && n < N) pi[(size_t)h * pi_hs + n] = (uint8_t)best;
+        if (g == 0 && n < N) {
+            pi[(size_t)h * pi_hs + n] = (uint8_t)best;
+            if (counts) atomicAdd(&counts[(size_t)h * Kp + best], 1);
+        }
     }
 }
 
-hipError_t launch_assign(int D, int H, int N, const uint16_t *xb, int64_t x_hs, const uint16_t *Cb,
-                         const double *cnorm, int Kp, uint8_t *pi, int64_t pi_hs, hipStream_t s) {
+hipError_t launch_assign(int D, int dtype, int H, int N, const Src &src, const uint16_t *Cb, const double *cnorm,
+                         int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts, hipStream_t s) {
     const size_t lds = (size_t)Kp * D * 2 + (size_t)Kp * 12;
     dim3 g((N + 64 * ASSIGN_TB - 1) / (64 * ASSIGN_TB), H), b(256);
-    if (D == 128) {
-        (void)hipFuncSetAttribute((const void *)k_assign<128>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(k_assign<128>, g, b, lds, s, xb, x_hs, N, Cb, cnorm, Kp, pi, pi_hs);
-    } else {
-        (void)hipFuncSetAttribute((const void *)k_assign<64>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        hipLaunchKernelGGL(k_assign<64>, g, b, lds, s, xb, x_hs, N, Cb, cnorm, Kp, pi, pi_hs);
-    }
+    QVG_DISPATCH_DT(D, dtype, {
+        (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+        hipLaunchKernelGGL((k_assign<DD, KVT>), g, b, lds, s, src, N, Cb, cnorm, Kp, pi, pi_hs, counts);
+    });
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// update, part 1: stable counting sort of each head's tokens by centroid
+// update, part 1: group each head's tokens by centroid
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void k_bucket(int N, int Kp, const uint8_t *pi, int64_t pi_hs, int32_t *counts,
-                                                int32_t *offsets, int32_t *order) {
-    __shared__ int32_t cnt[256];
+__global__ __launch_bounds__(256) void k_count(int N, int Kp, const uint8_t *pi, int64_t pi_hs, int32_t *counts) {
+    const int h = blockIdx.y;
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    if (n < N) atomicAdd(&counts[(size_t)h * Kp + pi[(size_t)h * pi_hs + n]], 1);
+}
+
+hipError_t launch_count(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, int32_t *counts, hipStream_t s) {
+    hipLaunchKernelGGL(k_count, dim3((N + 255) / 256, H), dim3(256), 0, s, N, Kp, pi, pi_hs, counts);
+    return hipGetLastError();
+}
+
+// Each block recomputes the head's exclusive prefix of the counts (256 values)
+// and places its tokens with one atomic per token.
+__global__ __launch_bounds__(256) void k_scatter(int N, int Kp, const uint8_t *pi, int64_t pi_hs,
+                                                 const int32_t *counts, int32_t *fill, int32_t *offsets,
+                                                 int32_t *order) {
     __shared__ int32_t off[256];
     __shared__ int32_t wsum[4];
-    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const uint8_t *p = pi + (size_t)h * pi_hs;
-    cnt[tid] = 0;
-    __syncthreads();
-    for (int n = tid; n < N; n += 256) atomicAdd(&cnt[p[n]], 1);
-    __syncthreads();
-    const int v = cnt[tid];
+    const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int v = tid < Kp ? counts[(size_t)h * Kp + tid] : 0;
     int x = v;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o);
+        const int y = __shfl_up(x, o);
         if (lane >= o) x += y;
     }
     if (lane == 63) wsum[wave] = x;
@@ -460,108 +528,121 @@ __global__ __launch_bounds__(256) void k_bucket(int N, int Kp, const uint8_t *pi
     for (int w = 0; w < wave; ++w) add += wsum[w];
     const int excl = x + add - v;
     off[tid] = excl;
-    if (tid < Kp) {
-        counts[(size_t)h * Kp + tid] = v;
-        offsets[(size_t)h * Kp + tid] = excl;
-    }
+    if (blockIdx.x == 0 && tid < Kp) offsets[(size_t)h * Kp + tid] = excl;
     __syncthreads();
-    if (wave != 0) return;
-    // one wave places the tokens in order, 64 at a time; equal keys in a batch
-    // are ranked by lane (match on all 8 key bits)
-    const uint64_t lt = (1ull << lane) - 1ull;
-    int32_t *ord = order + (size_t)h * N;
-    for (int base = 0; base < N; base += 64) {
-        const int n = base + lane;
-        const bool valid = n < N;
-        const int k = valid ? p[n] : 0;
-        uint64_t peers = __ballot(valid);
-#pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-            const bool on = (k >> bit) & 1;
-            const uint64_t bb = __ballot(valid && on);
-            peers &= on ? bb : ~bb;
-        }
-        const int rank = __popcll(peers & lt);
-        int pos = 0;
-        if (valid) pos = off[k] + rank;
-        __builtin_amdgcn_wave_barrier();
-        if (valid) {
-            ord[pos] = n;
-            if (rank == 0) off[k] += __popcll(peers);
-        }
-        __builtin_amdgcn_wave_barrier();
+    const int n = blockIdx.x * 256 + tid;
+    if (n < N) {
+        const int k = pi[(size_t)h * pi_hs + n];
+        const int pos = atomicAdd(&fill[(size_t)h * Kp + k], 1);
+        order[(size_t)h * N + off[k] + pos] = n;
     }
 }
 
-hipError_t launch_bucket(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, int32_t *counts, int32_t *offsets,
-                         int32_t *order, hipStream_t s) {
-    hipLaunchKernelGGL(k_bucket, dim3(H), dim3(256), 0, s, N, Kp, pi, pi_hs, counts, offsets, order);
+hipError_t launch_scatter(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, const int32_t *counts,
+                          int32_t *fill, int32_t *offsets, int32_t *order, hipStream_t s) {
+    hipLaunchKernelGGL(k_scatter, dim3((N + 255) / 256, H), dim3(256), 0, s, N, Kp, pi, pi_hs, counts, fill,
+                       offsets, order);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// update, part 2: mean of each centroid's rows, fp64 in ascending token order
+// update, part 2: exact mean of each centroid's rows
 // ---------------------------------------------------------------------------
+//
+// One wave per (centroid, head), four per block.  D/8 lanes cover a row, so a
+// wave reads 512/D rows per load and keeps four such loads in flight; each
+// lane keeps its 8 channels as (sum, error) pairs grown with the error-free
+// two-sum, so every partial sum is exact for the value ranges met in practice
+// and the order the rows arrive in does not matter.  The row slots are merged
+// with lane shuffles; the exact total is rounded once to fp64, divided by the
+// count and rounded to fp32.
 
-template <int D, typename SrcT>
-__global__ __launch_bounds__(256) void k_update(int N, int K, int Kp, const SrcT *src, int64_t src_hs,
-                                                const int32_t *counts, const int32_t *offsets,
-                                                const int32_t *order, float *C, uint16_t *Cb, double *cnorm) {
-    constexpr int P = D / 64;
-    const int h = blockIdx.y, lane = threadIdx.x & 63;
-    const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (k >= K) return;
-    const int cnt = counts[(size_t)h * Kp + k];
-    if (cnt == 0) return;  // empty cluster keeps its centroid
-    const int32_t *ord = order + (size_t)h * N + offsets[(size_t)h * Kp + k];
-    const SrcT *xh = src + (size_t)h * src_hs;
-    double acc[P];
-#pragma unroll
-    for (int i = 0; i < P; ++i) acc[i] = -0.0;   // -0 + x == x for every x
-    for (int i0 = 0; i0 < cnt; i0 += 64) {
-        const int m = cnt - i0 < 64 ? cnt - i0 : 64;
-        const int my = lane < m ? ord[i0 + lane] : 0;
-        int j = 0;
-        for (; j + 8 <= m; j += 8) {
-            float v[8][P];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int n = __shfl(my, j + u);
-                load_row_part<D, SrcT>(xh + (size_t)n * D, lane, v[u]);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int i = 0; i < P; ++i) acc[i] += (double)v[u][i];
-        }
-        for (; j < m; ++j) {
-            float v[P];
-            const int n = __shfl(my, j);
-            load_row_part<D, SrcT>(xh + (size_t)n * D, lane, v);
-#pragma unroll
-            for (int i = 0; i < P; ++i) acc[i] += (double)v[i];
-        }
-    }
-    float mean[P];
-#pragma unroll
-    for (int i = 0; i < P; ++i) mean[i] = (float)(acc[i] / (double)cnt);
-    write_centroid<D>(h, k, K, Kp, lane, mean, C, Cb, cnorm);
+__device__ __forceinline__ void two_sum(double &s, double &e, double x) {
+    const double t = s + x;
+    const double bp = t - s;
+    e += (s - (t - bp)) + (x - bp);
+    s = t;
 }
 
-hipError_t launch_update(int D, int H, int N, int K, const void *src, int src_dtype, int64_t src_hs,
-                         const int32_t *counts, const int32_t *offsets, const int32_t *order, float *C,
-                         uint16_t *Cb, double *cnorm, hipStream_t s) {
-    const int Kp = padded_k(K);
-    dim3 g((K + 3) / 4, H), b(256);
-#define QVG_UPD(DD, TT)                                                                                     \
-    hipLaunchKernelGGL((k_update<DD, TT>), g, b, 0, s, N, K, Kp, (const TT *)src, src_hs, counts, offsets, \
-                       order, C, Cb, cnorm)
-    if (D == 128) {
-        if (src_dtype == DT_BF16) QVG_UPD(128, uint16_t); else QVG_UPD(128, float);
-    } else {
-        if (src_dtype == DT_BF16) QVG_UPD(64, uint16_t); else QVG_UPD(64, float);
+template <int D, typename KVT>
+__global__ __launch_bounds__(256) void k_update(Src src, int N, int K, int Kp, const int32_t *counts,
+                                                const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb,
+                                                double *cnorm, int32_t *zero_cnt, int32_t *zero_fill) {
+    constexpr int LPR = D / 8;        // lanes per row
+    constexpr int RPI = 64 / LPR;     // rows per load
+    constexpr int UNROLL = 4;
+    const int lane = threadIdx.x & 63;
+    const int k = blockIdx.x * 4 + (threadIdx.x >> 6), h = blockIdx.y;
+    if (k >= K) return;
+    if (lane == 0 && zero_cnt) {
+        zero_cnt[(size_t)h * Kp + k] = 0;
+        zero_fill[(size_t)h * Kp + k] = 0;
     }
-#undef QVG_UPD
+    const int cnt = counts[(size_t)h * Kp + k];
+    if (cnt == 0) return;   // empty cluster keeps its centroid
+    const int32_t *ord = order + (size_t)h * N + offsets[(size_t)h * Kp + k];
+    const int slot = lane / LPR, c0 = (lane % LPR) * 8;
+    double hs[8], es[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { hs[i] = 0.0; es[i] = 0.0; }
+    for (int i0 = 0; i0 < cnt; i0 += 64) {
+        const int m = cnt - i0 < 64 ? cnt - i0 : 64;
+        const int mine = lane < m ? ord[i0 + lane] : 0;
+        for (int j0 = 0; j0 < m; j0 += RPI * UNROLL) {
+            float v[UNROLL][8];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int j = j0 + u * RPI + slot;
+                const int n = __shfl(mine, j < 64 ? j : 63);
+                if (j < m) src_row8<D, KVT>(src, h, n, c0, v[u]);
+            }
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                if (j0 + u * RPI + slot < m) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) two_sum(hs[i], es[i], (double)v[u][i]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double oh = __shfl_xor(hs[i], o), oe = __shfl_xor(es[i], o);
+            two_sum(hs[i], es[i], oh);
+            es[i] += oe;
+        }
+    }
+    double sq = 0.0;
+    if (slot == 0) {
+        float mean[8];
+        uint32_t b[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            mean[i] = (float)((hs[i] + es[i]) / (double)cnt);
+            b[i] = f32_to_bf16(mean[i]);
+            const double bd = (double)bf16_to_f32(b[i]);
+            sq += bd * bd;
+        }
+        float4 *c = reinterpret_cast<float4 *>(C + ((size_t)h * K + k) * D + c0);
+        c[0] = make_float4(mean[0], mean[1], mean[2], mean[3]);
+        c[1] = make_float4(mean[4], mean[5], mean[6], mean[7]);
+        *reinterpret_cast<uint4 *>(Cb + ((size_t)h * Kp + k) * D + c0) =
+            make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
+    }
+#pragma unroll
+    for (int o = 1; o < LPR; o <<= 1) sq += __shfl_xor(sq, o);
+    if (lane == 0) cnorm[(size_t)h * Kp + k] = sq;
+}
+
+hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, const int32_t *counts,
+                         const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb, double *cnorm,
+                         int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s) {
+    const int Kp = padded_k(K);
+    QVG_DISPATCH_DT(D, dtype,
+                    hipLaunchKernelGGL((k_update<DD, KVT>), dim3((K + 3) / 4, H), dim3(256), 0, s, src, N, K, Kp,
+                                       counts, offsets, order, C, Cb, cnorm, zero_cnt, zero_fill));
     return hipGetLastError();
 }
 
@@ -592,17 +673,15 @@ hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype
 }
 
 // ---------------------------------------------------------------------------
-// stage residual, optionally fused with the 2-bit group quantiser
+// last stage's residual and the 2-bit group quantiser
 // ---------------------------------------------------------------------------
 //
 // One thread owns 16 consecutive channels of one token; the G/16 threads of a
 // group are adjacent lanes and combine their maxima with lane shuffles.
 
-template <int D, int MODE, typename SrcT, typename CentT>
-__global__ __launch_bounds__(256) void k_residual(const SrcT *src, int64_t src_hs, int N, const CentT *cent,
-                                                  int cent_rows, const uint8_t *pi, int64_t pi_hs, float *R,
-                                                  uint16_t *Rb, int64_t r_hs, uint8_t *codes, uint8_t *scales,
-                                                  int64_t q_cap, int G) {
+template <int D, typename KVT, bool CENT>
+__global__ __launch_bounds__(256) void k_quant(Src src, int N, const KVT *cent, int cent_rows, const uint8_t *pi,
+                                               int64_t pi_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap, int G) {
     constexpr int SL = D / 16;
     constexpr int TPB = 256 / SL;
     const int h = blockIdx.y;
@@ -610,68 +689,51 @@ __global__ __launch_bounds__(256) void k_residual(const SrcT *src, int64_t src_h
     const int n = blockIdx.x * TPB + threadIdx.x / SL;
     if (n >= N) return;   // whole groups leave together (SL divides 64)
     float r[16];
-    load16<SrcT>(src + (size_t)h * src_hs + (size_t)n * D + 16 * j, r);
-    if constexpr (MODE != QUANT_ONLY) {
+    {
+        float a[8], b[8];
+        src_row8<D, KVT>(src, h, n, 16 * j, a);
+        src_row8<D, KVT>(src, h, n, 16 * j + 8, b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { r[i] = a[i]; r[8 + i] = b[i]; }
+    }
+    if constexpr (CENT) {
         const int k = pi[(size_t)h * pi_hs + n];
         float c[16];
-        load16<CentT>(cent + ((size_t)h * cent_rows + k) * D + 16 * j, c);
+        load16<KVT>(cent + ((size_t)h * cent_rows + k) * D + 16 * j, c);
 #pragma unroll
         for (int i = 0; i < 16; ++i) r[i] = r[i] - c[i];
     }
-    if constexpr (MODE == RES_WRITE) {
-        const size_t off = (size_t)h * r_hs + (size_t)n * D + 16 * j;
-        store16_f32(R + off, r);
-        store16_bf16(Rb + off, r);
-    } else {
-        float a = 0.f;
+    float a = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(r[i]));
-        const int lanes = G >> 4;
-        for (int o = 1; o < lanes; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
-        const uint32_t sc = e4m3_encode_nonneg(a / 1.5f);
-        const float s = e4m3_decode(sc);
-        uint32_t w = 0;
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(r[i]));
+    const int lanes = G >> 4;
+    for (int o = 1; o < lanes; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+    const uint32_t sc = e4m3_encode_nonneg(a / 1.5f);
+    const float s = e4m3_decode(sc);
+    uint32_t w = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint32_t q = (uint32_t)(r[i] >= -s) + (uint32_t)(r[i] >= 0.f) + (uint32_t)(r[i] >= s);
-            w |= q << (2 * i);
-        }
-        const size_t row = (size_t)h * q_cap + n;
-        reinterpret_cast<uint32_t *>(codes + row * (D / 4))[j] = w;
-        if ((j & (lanes - 1)) == 0) scales[row * (D / G) + (16 * j) / G] = (uint8_t)sc;
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t q = (uint32_t)(r[i] >= -s) + (uint32_t)(r[i] >= 0.f) + (uint32_t)(r[i] >= s);
+        w |= q << (2 * i);
     }
+    const size_t row = (size_t)h * q_cap + n;
+    reinterpret_cast<uint32_t *>(codes + row * (D / 4))[j] = w;
+    if ((j & (lanes - 1)) == 0) scales[row * (D / G) + (16 * j) / G] = (uint8_t)sc;
 }
 
-hipError_t launch_residual(int D, int mode, const void *src, int src_dtype, int64_t src_hs, int H, int N,
-                           const void *cent, int cent_dtype, int cent_rows, const uint8_t *pi, int64_t pi_hs,
-                           float *R, uint16_t *Rb, int64_t r_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap,
-                           int G, hipStream_t s) {
+hipError_t launch_quant(int D, int dtype, int H, int N, const Src &src, const void *cent, int cent_rows,
+                        const uint8_t *pi, int64_t pi_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap, int G,
+                        hipStream_t s) {
     const int TPB = 256 / (D / 16);
     dim3 g((N + TPB - 1) / TPB, H), b(256);
-#define QVG_RES(DD, MM, ST, CT)                                                                                \
-    hipLaunchKernelGGL((k_residual<DD, MM, ST, CT>), g, b, 0, s, (const ST *)src, src_hs, N, (const CT *)cent, \
-                       cent_rows, pi, pi_hs, R, Rb, r_hs, codes, scales, q_cap, G)
-#define QVG_RES_C(DD, MM, ST)                                      \
-    do {                                                           \
-        if (cent_dtype == DT_BF16) QVG_RES(DD, MM, ST, uint16_t); \
-        else QVG_RES(DD, MM, ST, float);                           \
-    } while (0)
-#define QVG_RES_S(DD, MM)                                          \
-    do {                                                           \
-        if (src_dtype == DT_BF16) QVG_RES_C(DD, MM, uint16_t);     \
-        else QVG_RES_C(DD, MM, float);                             \
-    } while (0)
-#define QVG_RES_M(DD)                                              \
-    do {                                                           \
-        if (mode == RES_WRITE) QVG_RES_S(DD, RES_WRITE);           \
-        else if (mode == RES_QUANT) QVG_RES_S(DD, RES_QUANT);      \
-        else QVG_RES_S(DD, QUANT_ONLY);                            \
-    } while (0)
-    if (D == 128) QVG_RES_M(128); else QVG_RES_M(64);
-#undef QVG_RES_M
-#undef QVG_RES_S
-#undef QVG_RES_C
-#undef QVG_RES
+    QVG_DISPATCH_DT(D, dtype, {
+        if (cent)
+            hipLaunchKernelGGL((k_quant<DD, KVT, true>), g, b, 0, s, src, N, (const KVT *)cent, cent_rows, pi, pi_hs,
+                               codes, scales, q_cap, G);
+        else
+            hipLaunchKernelGGL((k_quant<DD, KVT, false>), g, b, 0, s, src, N, (const KVT *)nullptr, 0, pi, pi_hs,
+                               codes, scales, q_cap, G);
+    });
     return hipGetLastError();
 }
 
@@ -743,24 +805,16 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 -> bf16 operand copy
+// zero fill
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void k_cast_bf16(const float *x, int64_t x_hs, int N, int D, uint16_t *out) {
-    const int h = blockIdx.y;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;   // index of 4 values
-    const int64_t total4 = (int64_t)N * D / 4;
-    if (i >= total4) return;
-    const float4 v = reinterpret_cast<const float4 *>(x + (size_t)h * x_hs)[i];
-    const uint32_t lo = f32_to_bf16(v.x) | (f32_to_bf16(v.y) << 16);
-    const uint32_t hi = f32_to_bf16(v.z) | (f32_to_bf16(v.w) << 16);
-    reinterpret_cast<uint2 *>(out + (size_t)h * N * D)[i] = make_uint2(lo, hi);
+__global__ __launch_bounds__(256) void k_zero(int32_t *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0;
 }
 
-hipError_t launch_cast_bf16(const float *x, int64_t x_hs, int H, int N, int D, uint16_t *out, hipStream_t s) {
-    const int64_t total4 = (int64_t)N * D / 4;
-    dim3 g((unsigned)((total4 + 255) / 256), H), b(256);
-    hipLaunchKernelGGL(k_cast_bf16, g, b, 0, s, x, x_hs, N, D, out);
+hipError_t launch_zero(int32_t *p, int64_t n, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 
