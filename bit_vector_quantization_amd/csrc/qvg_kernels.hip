@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "qvg_launch.h"
 
 namespace qvg {
@@ -325,33 +327,33 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
 // The table is fetched with all of a thread's loads in flight at once, and the
 // four token blocks of a wave run as four independent accumulator chains.
 
-constexpr int ASSIGN_TB = 4;  // 16-token blocks per wave
+constexpr int ASSIGN_TB = 4;          // 16-token blocks per wave
+constexpr int TILE = 16 * ASSIGN_TB;   // tokens per wave
 
+// Second smallest of {a, b, c} (given a <= b).
+__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm volatile("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// One wave: the nearest centroid of TILE tokens starting at tok0.
+//
+// The fp32 ranking is exact except between centroids whose distances are
+// within the accumulation error.  v_mfma_f32_16x16x32_bf16 adds its 32 products
+// pairwise with fp32 rounding (an in-kernel probe shows partial sums rounded at
+// fp32 precision), so with the four chained instructions every accumulator is
+// within about 24 ulp of (|x|^2 + |c|^2); a token whose two best distances are
+// more than 2^-16 (|x|^2 + max |c|^2) apart (plus the 2^-15 resolution of the
+// packed keys) keeps the fp32 winner.  The few others are re-decided on fp64
+// distances, 16 lanes per token.
 template <int D, typename KVT>
-__global__ __launch_bounds__(256) void k_assign(Src src, int N, const uint16_t *__restrict__ Cb,
-                                                const double *__restrict__ cnorm, int Kp, uint8_t *__restrict__ pi,
-                                                int64_t pi_hs, int32_t *__restrict__ counts) {
-    constexpr int KS = D / 32;          // k-steps
-    constexpr int CH = D / 8;           // 16-byte chunks per row
-    constexpr int STAGE = 256 * CH / 256;  // table chunks per thread at 256 centroids
-    extern __shared__ uint4 lds[];
-    const int h = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 4, r16 = lane & 15;
-
-    // centroid table: every load in flight before the first LDS write
-    const uint4 *csrc = reinterpret_cast<const uint4 *>(Cb + (size_t)h * Kp * D);
-    const int nch = Kp * CH;
-    uint4 st[STAGE];
-#pragma unroll
-    for (int u = 0; u < STAGE; ++u) {
-        const int i = tid + 256 * u;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (i < nch) v = csrc[i];
-        st[u] = v;
-    }
-    // token operands
-    const int tok0 = blockIdx.x * (64 * ASSIGN_TB) + wave * 64;
+__device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int tok0, const uint4 *lds,
+                                            const double *lcn64, const float *lhcn, int32_t *list, int Kp,
+                                            uint8_t *pi, int64_t pi_hs, int32_t *counts) {
+    constexpr int KS = D / 32;
+    constexpr int CH = D / 8;
+    const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
     bf16x8_t bt[ASSIGN_TB][KS];
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
@@ -363,28 +365,13 @@ __global__ __launch_bounds__(256) void k_assign(Src src, int N, const uint16_t *
             bt[b][s] = __builtin_bit_cast(bf16x8_t, v);
         }
     }
-#pragma unroll
-    for (int u = 0; u < STAGE; ++u) {
-        const int i = tid + 256 * u;
-        if (i < nch) {
-            const int row = i / CH, q = i - row * CH;
-            lds[row * CH + (q ^ (row & (CH - 1)))] = st[u];
-        }
-    }
-    double *lcn64 = reinterpret_cast<double *>(lds + Kp * CH);
-    float *lhcn = reinterpret_cast<float *>(lcn64 + Kp);
-    if (tid < Kp) {
-        const double c = cnorm[(size_t)h * Kp + tid];
-        lcn64[tid] = c;
-        lhcn[tid] = -0.5f * (float)c;
-    }
     // per token: hb = -(|x|^2 (1 + 2^-16) + 2^-100) / 2, so that every accumulator
     // below, dot - (|c|^2 + B) / 2 = -(|x - c|^2 + margin) / 2, is negative (a
     // near-zero distance that rounds positive still ranks first)
-    float hb[ASSIGN_TB];
+    float xx[ASSIGN_TB], hb[ASSIGN_TB];
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
-        float xx = 0.f;
+        float t = 0.f;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const uint4 xv = __builtin_bit_cast(uint4, bt[b][s]);
@@ -392,16 +379,15 @@ __global__ __launch_bounds__(256) void k_assign(Src src, int N, const uint16_t *
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float lo = __uint_as_float(xw[i] << 16), hi = __uint_as_float(xw[i] & 0xFFFF0000u);
-                xx = fmaf(lo, lo, xx);
-                xx = fmaf(hi, hi, xx);
+                t = fmaf(lo, lo, t);
+                t = fmaf(hi, hi, t);
             }
         }
-        xx += __shfl_xor(xx, 16);
-        xx += __shfl_xor(xx, 32);
-        hb[b] = -0.5f * fmaf(xx, 0x1.0001p+0f, 0x1p-100f);
+        t += __shfl_xor(t, 16);
+        t += __shfl_xor(t, 32);
+        xx[b] = t;
+        hb[b] = -0.5f * fmaf(t, 0x1.0001p+0f, 0x1p-100f);
     }
-    __syncthreads();
-
     // The two best centroids of each (lane, token) as packed keys: the bits of
     // a negative fp32 value grow with its magnitude, so bits(acc) with the low
     // byte replaced by the centroid index orders like the distance (to 15
@@ -409,7 +395,6 @@ __global__ __launch_bounds__(256) void k_assign(Src src, int N, const uint16_t *
     uint32_t q1[ASSIGN_TB], q2[ASSIGN_TB];
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) q1[b] = q2[b] = 0xFFFFFFFFu;
-
     const int ncb = Kp / 16;
     for (int cb = 0; cb < ncb; ++cb) {
         const int row = cb * 16 + r16;
@@ -424,35 +409,62 @@ __global__ __launch_bounds__(256) void k_assign(Src src, int N, const uint16_t *
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int b = 0; b < ASSIGN_TB; ++b) acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bt[b][s], acc[b], 0, 0, 0);
+            for (int b = 0; b < ASSIGN_TB; ++b)
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bt[b][s], acc[b], 0, 0, 0);
         const uint32_t kb = (uint32_t)(cb * 16 + 4 * g);
 #pragma unroll
         for (int b = 0; b < ASSIGN_TB; ++b) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const uint32_t key = (__float_as_uint(acc[b][r]) & 0xFFFFFF00u) | (kb + r);
-                q2[b] = min(q2[b], max(q1[b], key));
+                q2[b] = med3_u32(q1[b], q2[b], key);
                 q1[b] = min(q1[b], key);
             }
         }
     }
+    // merge the four lanes' top-2 keys of each token, settle the clear cases and
+    // list the near ties
+    int n_list = 0;
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
-        // merge the four lanes' top-2 keys of each token
 #pragma unroll
         for (int o = 16; o <= 32; o <<= 1) {
             const uint32_t w1 = __shfl_xor(q1[b], o), w2 = __shfl_xor(q2[b], o);
             q2[b] = min(max(q1[b], w1), min(q2[b], w2));
             q1[b] = min(q1[b], w1);
         }
-        // fp64 distances of the two candidates: each lane sums its 32 channels
         const int c1 = (int)(q1[b] & 0xFFu), c2 = (int)(q2[b] & 0xFFu);
+        const float a1 = __uint_as_float(q1[b] & 0xFFFFFF00u), a2 = __uint_as_float(q2[b] & 0xFFFFFF00u);
+        const float cn1 = -2.0f * lhcn[c1], cn2 = -2.0f * lhcn[c2];
+        const float tol = 0x1p-16f * (xx[b] + fmaxf(cn1, cn2)) + 0x1p-14f * (fabsf(a1) + fabsf(a2));
+        const bool tie = (a1 - a2) <= tol;   // half the distance gap, from the keys
+        const int n = tok0 + 16 * b + r16;
+        const bool mine = g == 0 && n < N;
+        if (mine && !tie) {
+            pi[(size_t)h * pi_hs + n] = (uint8_t)c1;
+            if (counts) atomicAdd(&counts[(size_t)h * Kp + c1], 1);
+        }
+        const uint64_t m = __ballot(mine && tie);
+        if (mine && tie) {
+            const int pos = n_list + __popcll(m & ((1ull << lane) - 1ull));
+            list[pos] = ((16 * b + r16) << 16) | (c1 << 8) | c2;
+        }
+        n_list += __popcll(m);
+    }
+    if (n_list == 0) return;
+    __builtin_amdgcn_wave_barrier();
+    // near ties: 16 lanes per token, each with 8 channels, fp64 distances
+    const int sub = lane & 15, grp = lane >> 4;
+    for (int j0 = 0; j0 < n_list; j0 += 4) {
+        const int j = j0 + grp;
+        const int e = list[j < n_list ? j : 0];
+        const int nl = e >> 16, c1 = (e >> 8) & 0xFF, c2 = e & 0xFF;
+        const int n = tok0 + nl;
         double p1 = 0.0, p2 = 0.0;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const uint4 xv = __builtin_bit_cast(uint4, bt[b][s]);
-            const uint4 a1 = lds[c1 * CH + ((4 * s + g) ^ (c1 & (CH - 1)))];
-            const uint4 a2 = lds[c2 * CH + ((4 * s + g) ^ (c2 & (CH - 1)))];
+        if (j < n_list && sub < CH) {
+            const uint4 xv = src_row8_bf16<D, KVT>(src, h, n, 8 * sub);
+            const uint4 a1 = lds[c1 * CH + (sub ^ (c1 & (CH - 1)))];
+            const uint4 a2 = lds[c2 * CH + (sub ^ (c2 & (CH - 1)))];
             const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
             const uint32_t aw[4] = {a1.x, a1.y, a1.z, a1.w};
             const uint32_t bw[4] = {a2.x, a2.y, a2.z, a2.w};
@@ -466,28 +478,70 @@ __global__ __launch_bounds__(256) void k_assign(Src src, int N, const uint16_t *
                 p2 = fma(xh2, (double)__uint_as_float(bw[i] & 0xFFFF0000u), p2);
             }
         }
-        p1 += __shfl_xor(p1, 16);
-        p2 += __shfl_xor(p2, 16);
-        p1 += __shfl_xor(p1, 32);
-        p2 += __shfl_xor(p2, 32);
-        const double e1 = lcn64[c1] - 2.0 * p1, e2 = lcn64[c2] - 2.0 * p2;
-        const int best = (e2 < e1 || (e2 == e1 && c2 < c1)) ? c2 : c1;
-        const int n = tok0 + 16 * b + r16;
-        if (g == 0 && n < N) {
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            p1 += __shfl_xor(p1, o);
+            p2 += __shfl_xor(p2, o);
+        }
+        if (j < n_list && sub == 0) {
+            const double e1 = lcn64[c1] - 2.0 * p1, e2 = lcn64[c2] - 2.0 * p2;
+            const int best = (e2 < e1 || (e2 == e1 && c2 < c1)) ? c2 : c1;
             pi[(size_t)h * pi_hs + n] = (uint8_t)best;
             if (counts) atomicAdd(&counts[(size_t)h * Kp + best], 1);
         }
     }
 }
 
+// A block is four waves x TILE tokens of one head; the head's bf16 centroid
+// table (swizzled 16-byte chunks) and its norms (fp32 and fp64) sit in LDS,
+// fetched with all of a thread's loads in flight at once.
+template <int D, typename KVT>
+__global__ __launch_bounds__(256) void k_assign(Src src, int H, int N, const uint16_t *__restrict__ Cb,
+                                                const double *__restrict__ cnorm, int Kp, uint8_t *__restrict__ pi,
+                                                int64_t pi_hs, int32_t *__restrict__ counts) {
+    constexpr int CH = D / 8;
+    constexpr int STAGE = 256 * CH / 256;   // table chunks per thread at 256 centroids
+    extern __shared__ uint4 lds[];
+    double *lcn64 = reinterpret_cast<double *>(lds + Kp * CH);
+    float *lhcn = reinterpret_cast<float *>(lcn64 + Kp);
+    int32_t *lists = reinterpret_cast<int32_t *>(lhcn + Kp);
+    const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
+    const uint4 *csrc = reinterpret_cast<const uint4 *>(Cb + (size_t)h * Kp * D);
+    const int nch = Kp * CH;
+    uint4 st[STAGE];
+#pragma unroll
+    for (int u = 0; u < STAGE; ++u) {
+        const int i = tid + 256 * u;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (i < nch) v = csrc[i];
+        st[u] = v;
+    }
+#pragma unroll
+    for (int u = 0; u < STAGE; ++u) {
+        const int i = tid + 256 * u;
+        if (i < nch) {
+            const int row = i / CH, q = i - row * CH;
+            lds[row * CH + (q ^ (row & (CH - 1)))] = st[u];
+        }
+    }
+    if (tid < Kp) {
+        const double c = cnorm[(size_t)h * Kp + tid];
+        lcn64[tid] = c;
+        lhcn[tid] = -0.5f * (float)c;
+    }
+    __syncthreads();
+    assign_wave<D, KVT>(src, h, N, (blockIdx.x * 4 + wave) * TILE, lds, lcn64, lhcn, lists + wave * TILE, Kp, pi,
+                        pi_hs, counts);
+}
+
 hipError_t launch_assign(int D, int dtype, int H, int N, const Src &src, const uint16_t *Cb, const double *cnorm,
                          int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts, hipStream_t s) {
-    const size_t lds = (size_t)Kp * D * 2 + (size_t)Kp * 12;
-    dim3 g((N + 64 * ASSIGN_TB - 1) / (64 * ASSIGN_TB), H), b(256);
+    const size_t lds = (size_t)Kp * D * 2 + (size_t)Kp * 12 + 4 * TILE * sizeof(int32_t);
+    dim3 g((N + 4 * TILE - 1) / (4 * TILE), H), b(256);
     QVG_DISPATCH_DT(D, dtype, {
         (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
-        hipLaunchKernelGGL((k_assign<DD, KVT>), g, b, lds, s, src, N, Cb, cnorm, Kp, pi, pi_hs, counts);
+        hipLaunchKernelGGL((k_assign<DD, KVT>), g, b, lds, s, src, H, N, Cb, cnorm, Kp, pi, pi_hs, counts);
     });
     return hipGetLastError();
 }
