@@ -21,6 +21,9 @@ ARCH = "gfx950"
 # that it does not know the feature, which is harmless.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # MFMA accumulators stay in ordinary VGPRs: the assign kernel reads
+             # every result with VALU instructions, and AGPR copies cost issue slots
+             "-mllvm", "-amdgpu-mfma-vgpr-form",
              "-Wall", "-Wno-unused-result"]
 
 

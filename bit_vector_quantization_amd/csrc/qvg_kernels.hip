@@ -17,7 +17,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <algorithm>
 
 #include "qvg_launch.h"
 
@@ -305,48 +304,55 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
 }
 
 // ---------------------------------------------------------------------------
-// assignment: distances on the matrix cores, exact decision between the two best
+// assignment: distances on the matrix cores, exact decision of near ties
 // ---------------------------------------------------------------------------
 //
-// D^T = Cb * Xb^T with v_mfma_f32_16x16x32_bf16: the A operand is a block of 16
-// centroids, the B operand a block of 16 tokens, 32 channels per instruction.
-// Lane l feeds row/column (l % 16) and channels 8*(l/16) .. +7 of the k-step for
-// both operands, so the two sides pair the same channels whatever the order of
-// the hardware's reduction.  The 16x16 result leaves centroid 4*(l/16)+r of
-// token l%16 in accumulator r of lane l, so each lane keeps the two nearest of
-// its centroids for one token and four lanes merge them.
+// v_mfma_f32_16x16x32_bf16 accumulates, per token and centroid,
+//   acc = <x, c> - |c|^2 / 2 - (|x|^2 (1 + 2^-12) + 2^-100) / 2
+//       = -(|x - c|^2 + 2^-12 |x|^2 + 2^-100) / 2,
+// negative and largest for the nearest centroid.  The A operand is a block of
+// 16 centroids, the B operand a block of 16 tokens, 32 channels per
+// instruction: lane l feeds row/column l % 16 with channels 8 (l / 16) .. +7
+// of the k-step on both sides, and the 16x16 result leaves centroid
+// 4 (l / 16) + r of token l % 16 in accumulator r of lane l.  The constant
+// terms enter as the instruction's C operand.
 //
-// fp32 accumulation can misorder two centroids whose distances differ by a few
-// fp32 ulps.  The final choice between the two best is therefore made on fp64
-// distances: every bf16 x bf16 product is exact in fp64 and the sums are exact
-// for the value ranges met in practice, so the decision is that of the exact
-// |c|^2 - 2<x, c>, lowest index on ties.
+// Each lane keeps the two largest accumulators of its token as keys: the
+// value with its low mantissa byte replaced by the centroid's number
+// (v_perm_b32).  Among negative floats a larger low byte is a smaller value,
+// so equal truncated values go to the lower number; v_med3_f32 keeps the two
+// best and four lanes merge.
 //
-// A workgroup is 4 waves x 64 tokens of one head; the head's bf16 centroid
-// table (swizzled 16-byte chunks) and its norms (fp32 and fp64) sit in LDS.
-// The table is fetched with all of a thread's loads in flight at once, and the
-// four token blocks of a wave run as four independent accumulator chains.
-
-constexpr int ASSIGN_TB = 4;          // 16-token blocks per wave
-constexpr int TILE = 16 * ASSIGN_TB;   // tokens per wave
-
-// Second smallest of {a, b, c} (given a <= b).
-__device__ __forceinline__ uint32_t med3_u32(uint32_t a, uint32_t b, uint32_t c) {
-    uint32_t r;
-    asm volatile("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-
-// One wave: the nearest centroid of TILE tokens starting at tok0.
+// Exactness.  The bf16 products are exact in fp32; the instruction adds them
+// and C with fp32 roundings along a shallow tree (an in-kernel probe shows the
+// partial sums rounded to fp32).  With four chained instructions every
+// accumulator is within 24 ulp (2^-18.4 relative) of
+//   S = |C| + sum |x_i c_i|  <=  |x|^2 + |c|^2 (about),
+// which keeps every value negative (the 2^-12 |x|^2 margin is far larger)
+// and misorders two centroids only if they lie within
+// 2^-17.4 (|x|^2 + max |c|^2) of each other; a key is within 2^-15 of its
+// value.  A token whose two best keys are further apart than
+//   2^-16 (|x|^2 + max |c|^2) + 2^-14 (|k1| + |k2|)
+// keeps the fp32 winner.  The others (a few in a thousand) are re-decided on
+// fp64 distances, 16 lanes per token: every bf16 x bf16 product is exact in
+// fp64 and the sums are exact for the value ranges met in practice, so the
+// decision is that of |c|^2 - 2 <x, c>, lowest index on ties.
 //
-// The fp32 ranking is exact except between centroids whose distances are
-// within the accumulation error.  v_mfma_f32_16x16x32_bf16 adds its 32 products
-// pairwise with fp32 rounding (an in-kernel probe shows partial sums rounded at
-// fp32 precision), so with the four chained instructions every accumulator is
-// within about 24 ulp of (|x|^2 + |c|^2); a token whose two best distances are
-// more than 2^-16 (|x|^2 + max |c|^2) apart (plus the 2^-15 resolution of the
-// packed keys) keeps the fp32 winner.  The few others are re-decided on fp64
-// distances, 16 lanes per token.
+// A workgroup is 8 waves x 64 tokens of one head.  The head's bf16 table
+// (swizzled 16-byte chunks, 64 KiB at 256 x 128) and its norms sit in LDS:
+// two workgroups per CU, four waves per SIMD.
+
+constexpr int ASSIGN_TB = 4;              // 16-token blocks per wave
+constexpr int TILE = 16 * ASSIGN_TB;      // tokens per wave
+constexpr int ASSIGN_WAVES = 8;           // waves per workgroup
+constexpr float PAD_HALF_NORM = -1e30f;   // padding rows: never the nearest
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float fmax_key(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, __FLT_MAX__); }
+__device__ __forceinline__ float fmin_key(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -__FLT_MAX__); }
+
+// One wave: the nearest centroid of the TILE tokens from tok0.
 template <int D, typename KVT>
 __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int tok0, const uint4 *lds,
                                             const double *lcn64, const float *lhcn, int32_t *list, int Kp,
@@ -365,79 +371,94 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
             bt[b][s] = __builtin_bit_cast(bf16x8_t, v);
         }
     }
-    // per token: hb = -(|x|^2 (1 + 2^-16) + 2^-100) / 2, so that every accumulator
-    // below, dot - (|c|^2 + B) / 2 = -(|x - c|^2 + margin) / 2, is negative (a
-    // near-zero distance that rounds positive still ranks first)
-    float xx[ASSIGN_TB], hb[ASSIGN_TB];
+    // |x|^2 of each token and its share hb of the C operand
+    float hb[ASSIGN_TB];
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
         float t = 0.f;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             const uint4 xv = __builtin_bit_cast(uint4, bt[b][s]);
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float lo = __uint_as_float(xw[i] << 16), hi = __uint_as_float(xw[i] & 0xFFFF0000u);
-                t = fmaf(lo, lo, t);
-                t = fmaf(hi, hi, t);
-            }
+            t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xv.x), __builtin_bit_cast(bf16x2_t, xv.x), t, false);
+            t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xv.y), __builtin_bit_cast(bf16x2_t, xv.y), t, false);
+            t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xv.z), __builtin_bit_cast(bf16x2_t, xv.z), t, false);
+            t = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xv.w), __builtin_bit_cast(bf16x2_t, xv.w), t, false);
         }
         t += __shfl_xor(t, 16);
         t += __shfl_xor(t, 32);
-        xx[b] = t;
-        hb[b] = -0.5f * fmaf(t, 0x1.0001p+0f, 0x1p-100f);
+        hb[b] = -0.5f * fmaf(t, 1.0f + 0x1p-12f, 0x1p-100f);
+        if (g == 0) list[16 * b + r16] = __float_as_int(t);   // |x|^2 waits in LDS (the list space)
     }
-    // The two best centroids of each (lane, token) as packed keys: the bits of
-    // a negative fp32 value grow with its magnitude, so bits(acc) with the low
-    // byte replaced by the centroid index orders like the distance (to 15
-    // mantissa bits) with ties going to the lower index.
-    uint32_t q1[ASSIGN_TB], q2[ASSIGN_TB];
+    // the two best keys of each (lane, token); the low byte holds 4 cb + r,
+    // the lane's part 4 g of the centroid number is put in before the merge
+    float q1[ASSIGN_TB], q2[ASSIGN_TB];
 #pragma unroll
-    for (int b = 0; b < ASSIGN_TB; ++b) q1[b] = q2[b] = 0xFFFFFFFFu;
+    for (int b = 0; b < ASSIGN_TB; ++b) q1[b] = q2[b] = -__FLT_MAX__;
+    const uint32_t sel = 0x07060500u;   // bytes 3..1 from the accumulator, byte 0 from the number
     const int ncb = Kp / 16;
-    for (int cb = 0; cb < ncb; ++cb) {
-        const int row = cb * 16 + r16;
+    // row cb * 16 + r16 of the table: its swizzle (row & (CH - 1)) does not depend on cb
+    const uint4 *arow[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) arow[s] = lds + r16 * CH + ((4 * s + g) ^ (r16 & (CH - 1)));
+    const float4 *cnp = reinterpret_cast<const float4 *>(lhcn + 4 * g);
+    auto block = [&](int cb, int j) {   // centroid block cb, read at offset j blocks from the pointers
         bf16x8_t a[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            a[s] = __builtin_bit_cast(bf16x8_t, lds[row * CH + ((4 * s + g) ^ (row & (CH - 1)))]);
-        const float4 cn = *reinterpret_cast<const float4 *>(lhcn + cb * 16 + 4 * g);
+        for (int s = 0; s < KS; ++s) a[s] = __builtin_bit_cast(bf16x8_t, arow[s][j * 16 * CH]);
+        const float4 cn = cnp[j * 4];
         f32x4_t acc[ASSIGN_TB];
 #pragma unroll
-        for (int b = 0; b < ASSIGN_TB; ++b) acc[b] = f32x4_t{cn.x + hb[b], cn.y + hb[b], cn.z + hb[b], cn.w + hb[b]};
+        for (int b = 0; b < ASSIGN_TB; ++b)
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a[0], bt[b][0], f32x4_t{cn.x + hb[b], cn.y + hb[b], cn.z + hb[b], cn.w + hb[b]}, 0, 0, 0);
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int s = 1; s < KS; ++s)
 #pragma unroll
             for (int b = 0; b < ASSIGN_TB; ++b)
                 acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bt[b][s], acc[b], 0, 0, 0);
-        const uint32_t kb = (uint32_t)(cb * 16 + 4 * g);
 #pragma unroll
         for (int b = 0; b < ASSIGN_TB; ++b) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const uint32_t key = (__float_as_uint(acc[b][r]) & 0xFFFFFF00u) | (kb + r);
-                q2[b] = med3_u32(q1[b], q2[b], key);
-                q1[b] = min(q1[b], key);
+                const float key =
+                    __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(acc[b][r]), (uint32_t)(4 * cb + r), sel));
+                q2[b] = __builtin_amdgcn_fmed3f(q1[b], q2[b], key);
+                q1[b] = fmax_key(q1[b], key);
             }
         }
+    };
+    int cb = 0;
+    for (; cb + 2 <= ncb; cb += 2) {   // two blocks per trip: the second at fixed LDS offsets
+        block(cb, 0);
+        __builtin_amdgcn_sched_barrier(0);   // keeps the second block's operands out of the first's registers
+        block(cb + 1, 1);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) arow[s] += 32 * CH;
+        cnp += 8;
     }
-    // merge the four lanes' top-2 keys of each token, settle the clear cases and
-    // list the near ties
+    if (cb < ncb) block(cb, 0);
+    float xx[ASSIGN_TB];
+#pragma unroll
+    for (int b = 0; b < ASSIGN_TB; ++b) xx[b] = __int_as_float(list[16 * b + r16]);
+    __builtin_amdgcn_wave_barrier();
+    // merge the four lanes of each token, settle the clear cases, list the near ties
     int n_list = 0;
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
+        uint32_t u1 = __float_as_uint(q1[b]), u2 = __float_as_uint(q2[b]);
+        u1 = (u1 & 0xFFFFFF03u) | ((u1 & 0xFCu) << 2) | (uint32_t)(4 * g);
+        u2 = (u2 & 0xFFFFFF03u) | ((u2 & 0xFCu) << 2) | (uint32_t)(4 * g);
+        float k1 = __uint_as_float(u1), k2 = __uint_as_float(u2);
 #pragma unroll
         for (int o = 16; o <= 32; o <<= 1) {
-            const uint32_t w1 = __shfl_xor(q1[b], o), w2 = __shfl_xor(q2[b], o);
-            q2[b] = min(max(q1[b], w1), min(q2[b], w2));
-            q1[b] = min(q1[b], w1);
+            const float w1 = __shfl_xor(k1, o), w2 = __shfl_xor(k2, o);
+            k2 = fmax_key(fmin_key(k1, w1), fmax_key(k2, w2));
+            k1 = fmax_key(k1, w1);
         }
-        const int c1 = (int)(q1[b] & 0xFFu), c2 = (int)(q2[b] & 0xFFu);
-        const float a1 = __uint_as_float(q1[b] & 0xFFFFFF00u), a2 = __uint_as_float(q2[b] & 0xFFFFFF00u);
-        const float cn1 = -2.0f * lhcn[c1], cn2 = -2.0f * lhcn[c2];
-        const float tol = 0x1p-16f * (xx[b] + fmaxf(cn1, cn2)) + 0x1p-14f * (fabsf(a1) + fabsf(a2));
-        const bool tie = (a1 - a2) <= tol;   // half the distance gap, from the keys
+        const int c1 = (int)(__float_as_uint(k1) & 0xFFu), c2 = (int)(__float_as_uint(k2) & 0xFFu);
+        const float cnmax = -2.0f * fminf(lhcn[c1], lhcn[c2]);
+        const float tol = 0x1p-16f * (xx[b] + cnmax) + 0x1p-14f * (fabsf(k1) + fabsf(k2));
+        const bool tie = (k1 - k2) <= tol;
         const int n = tok0 + 16 * b + r16;
         const bool mine = g == 0 && n < N;
         if (mine && !tie) {
@@ -453,14 +474,14 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
     }
     if (n_list == 0) return;
     __builtin_amdgcn_wave_barrier();
-    // near ties: 16 lanes per token, each with 8 channels, fp64 distances
+    // near ties: 16 lanes per token, 8 channels each, fp64 distances
     const int sub = lane & 15, grp = lane >> 4;
     for (int j0 = 0; j0 < n_list; j0 += 4) {
         const int j = j0 + grp;
         const int e = list[j < n_list ? j : 0];
         const int nl = e >> 16, c1 = (e >> 8) & 0xFF, c2 = e & 0xFF;
         const int n = tok0 + nl;
-        double p1 = 0.0, p2 = 0.0;
+        double p1 = 0.0, p2 = 0.0;   // <x, c1>, <x, c2>
         if (j < n_list && sub < CH) {
             const uint4 xv = src_row8_bf16<D, KVT>(src, h, n, 8 * sub);
             const uint4 a1 = lds[c1 * CH + (sub ^ (c1 & (CH - 1)))];
@@ -471,11 +492,11 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const double xl = (double)__uint_as_float(xw[i] << 16);
-                const double xh2 = (double)__uint_as_float(xw[i] & 0xFFFF0000u);
+                const double xh = (double)__uint_as_float(xw[i] & 0xFFFF0000u);
                 p1 = fma(xl, (double)__uint_as_float(aw[i] << 16), p1);
-                p1 = fma(xh2, (double)__uint_as_float(aw[i] & 0xFFFF0000u), p1);
+                p1 = fma(xh, (double)__uint_as_float(aw[i] & 0xFFFF0000u), p1);
                 p2 = fma(xl, (double)__uint_as_float(bw[i] << 16), p2);
-                p2 = fma(xh2, (double)__uint_as_float(bw[i] & 0xFFFF0000u), p2);
+                p2 = fma(xh, (double)__uint_as_float(bw[i] & 0xFFFF0000u), p2);
             }
         }
 #pragma unroll
@@ -492,15 +513,14 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
     }
 }
 
-// A block is four waves x TILE tokens of one head; the head's bf16 centroid
-// table (swizzled 16-byte chunks) and its norms (fp32 and fp64) sit in LDS,
-// fetched with all of a thread's loads in flight at once.
 template <int D, typename KVT>
-__global__ __launch_bounds__(256) void k_assign(Src src, int H, int N, const uint16_t *__restrict__ Cb,
-                                                const double *__restrict__ cnorm, int Kp, uint8_t *__restrict__ pi,
-                                                int64_t pi_hs, int32_t *__restrict__ counts) {
+__global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H, int N, const uint16_t *__restrict__ Cb,
+                                                                 const double *__restrict__ cnorm, int Kp,
+                                                                 uint8_t *__restrict__ pi, int64_t pi_hs,
+                                                                 int32_t *__restrict__ counts) {
     constexpr int CH = D / 8;
-    constexpr int STAGE = 256 * CH / 256;   // table chunks per thread at 256 centroids
+    constexpr int NT = 64 * ASSIGN_WAVES;
+    constexpr int STAGE = 256 * CH / NT;   // table chunks per thread at 256 centroids
     extern __shared__ uint4 lds[];
     double *lcn64 = reinterpret_cast<double *>(lds + Kp * CH);
     float *lhcn = reinterpret_cast<float *>(lcn64 + Kp);
@@ -511,14 +531,14 @@ __global__ __launch_bounds__(256) void k_assign(Src src, int H, int N, const uin
     uint4 st[STAGE];
 #pragma unroll
     for (int u = 0; u < STAGE; ++u) {
-        const int i = tid + 256 * u;
+        const int i = tid + NT * u;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (i < nch) v = csrc[i];
         st[u] = v;
     }
 #pragma unroll
     for (int u = 0; u < STAGE; ++u) {
-        const int i = tid + 256 * u;
+        const int i = tid + NT * u;
         if (i < nch) {
             const int row = i / CH, q = i - row * CH;
             lds[row * CH + (q ^ (row & (CH - 1)))] = st[u];
@@ -527,17 +547,18 @@ __global__ __launch_bounds__(256) void k_assign(Src src, int H, int N, const uin
     if (tid < Kp) {
         const double c = cnorm[(size_t)h * Kp + tid];
         lcn64[tid] = c;
-        lhcn[tid] = -0.5f * (float)c;
+        lhcn[tid] = c < 1e300 ? -0.5f * (float)c : PAD_HALF_NORM;
     }
     __syncthreads();
-    assign_wave<D, KVT>(src, h, N, (blockIdx.x * 4 + wave) * TILE, lds, lcn64, lhcn, lists + wave * TILE, Kp, pi,
-                        pi_hs, counts);
+    const int tok0 = (blockIdx.x * ASSIGN_WAVES + wave) * TILE;
+    if (tok0 >= N) return;
+    assign_wave<D, KVT>(src, h, N, tok0, lds, lcn64, lhcn, lists + wave * TILE, Kp, pi, pi_hs, counts);
 }
 
 hipError_t launch_assign(int D, int dtype, int H, int N, const Src &src, const uint16_t *Cb, const double *cnorm,
                          int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts, hipStream_t s) {
-    const size_t lds = (size_t)Kp * D * 2 + (size_t)Kp * 12 + 4 * TILE * sizeof(int32_t);
-    dim3 g((N + 4 * TILE - 1) / (4 * TILE), H), b(256);
+    const size_t lds = (size_t)Kp * D * 2 + (size_t)Kp * 12 + ASSIGN_WAVES * TILE * sizeof(int32_t);
+    dim3 g((N + ASSIGN_WAVES * TILE - 1) / (ASSIGN_WAVES * TILE), H), b(64 * ASSIGN_WAVES);
     QVG_DISPATCH_DT(D, dtype, {
         (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
