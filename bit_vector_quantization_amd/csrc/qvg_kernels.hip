@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 
 #include "qvg_launch.h"
 
@@ -138,18 +140,18 @@ __device__ __forceinline__ void load8<float>(const float *p, float (&v)[8]) {
 
 // Channels [c0, c0 + 8) of row n of head h of R(P): the input minus the stored
 // centroids of the P earlier stages, subtracted in stage order in fp32.
+// (The stage loop is not unrolled: its pointers are read from the kernel
+// arguments as needed instead of occupying registers for all MAX_PREV stages.)
 template <int D, typename KVT>
 __device__ __forceinline__ void src_row8(const Src &s, int h, int64_t n, int c0, float (&v)[8]) {
     load8<KVT>(static_cast<const KVT *>(s.x) + (size_t)h * s.x_hs + (size_t)n * D + c0, v);
+#pragma unroll 1
+    for (int p = 0; p < s.P; ++p) {
+        const int k = s.pi[p][(size_t)h * s.pi_hs + n];
+        float c[8];
+        load8<KVT>(static_cast<const KVT *>(s.cent[p]) + ((size_t)h * s.K + k) * D + c0, c);
 #pragma unroll
-    for (int p = 0; p < MAX_PREV; ++p) {
-        if (p < s.P) {
-            const int k = s.pi[p][(size_t)h * s.pi_hs + n];
-            float c[8];
-            load8<KVT>(static_cast<const KVT *>(s.cent[p]) + ((size_t)h * s.K + k) * D + c0, c);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = v[i] - c[i];
-        }
+        for (int i = 0; i < 8; ++i) v[i] = v[i] - c[i];
     }
 }
 
@@ -342,7 +344,7 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
 // (swizzled 16-byte chunks, 64 KiB at 256 x 128) and its norms sit in LDS:
 // two workgroups per CU, four waves per SIMD.
 
-constexpr int ASSIGN_TB = 4;              // 16-token blocks per wave
+constexpr int ASSIGN_TB = 2;              // 16-token blocks per wave
 constexpr int TILE = 16 * ASSIGN_TB;      // tokens per wave
 constexpr int ASSIGN_WAVES = 8;           // waves per workgroup
 constexpr float PAD_HALF_NORM = -1e30f;   // padding rows: never the nearest
@@ -352,25 +354,66 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float fmax_key(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, __FLT_MAX__); }
 __device__ __forceinline__ float fmin_key(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -__FLT_MAX__); }
 
-// One wave: the nearest centroid of the TILE tokens from tok0.
+// The B operands of the TILE tokens from tok0 (zero past N): channels
+// 32 s + 8 g .. +7 of R(P) for k-step s, rounded to bf16.
 template <int D, typename KVT>
-__device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int tok0, const uint4 *lds,
-                                            const double *lcn64, const float *lhcn, int32_t *list, int Kp,
-                                            uint8_t *pi, int64_t pi_hs, int32_t *counts) {
+__device__ __forceinline__ void assign_load(const Src &src, int h, int N, int tok0, bf16x8_t (&bt)[ASSIGN_TB][D / 32]) {
     constexpr int KS = D / 32;
-    constexpr int CH = D / 8;
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-    bf16x8_t bt[ASSIGN_TB][KS];
+    if (sizeof(KVT) == 2 && src.P == 0) {   // the bf16 input itself is the operand
+#pragma unroll
+        for (int b = 0; b < ASSIGN_TB; ++b) {
+            const int n = tok0 + 16 * b + r16;
+            const uint4 *row = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src.x) +
+                                                               (size_t)h * src.x_hs + (size_t)n * D + 8 * g);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) bt[b][s] = __builtin_bit_cast(bf16x8_t, n < N ? row[4 * s] : make_uint4(0, 0, 0, 0));
+        }
+        return;
+    }
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
         const int n = tok0 + 16 * b + r16;
+        float v[KS][8];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (n < N) v = src_row8_bf16<D, KVT>(src, h, n, 32 * s + 8 * g);
-            bt[b][s] = __builtin_bit_cast(bf16x8_t, v);
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[s][i] = 0.f;
+        if (n < N) {
+            const KVT *xr = static_cast<const KVT *>(src.x) + (size_t)h * src.x_hs + (size_t)n * D + 8 * g;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) load8<KVT>(xr + 32 * s, v[s]);
+#pragma unroll 1
+            for (int p = 0; p < src.P; ++p) {
+                const int k = src.pi[p][(size_t)h * src.pi_hs + n];
+                const KVT *cr = static_cast<const KVT *>(src.cent[p]) + ((size_t)h * src.K + k) * D + 8 * g;
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    float c[8];
+                    load8<KVT>(cr + 32 * s, c);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) v[s][i] = v[s][i] - c[i];
+                }
+            }
         }
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            bt[b][s] = __builtin_bit_cast(
+                bf16x8_t, make_uint4(f32_to_bf16(v[s][0]) | (f32_to_bf16(v[s][1]) << 16),
+                                     f32_to_bf16(v[s][2]) | (f32_to_bf16(v[s][3]) << 16),
+                                     f32_to_bf16(v[s][4]) | (f32_to_bf16(v[s][5]) << 16),
+                                     f32_to_bf16(v[s][6]) | (f32_to_bf16(v[s][7]) << 16)));
     }
+}
+
+// One wave: the nearest centroid of the TILE tokens from tok0, whose operands are in bt.
+template <int D, typename KVT>
+__device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int tok0, const bf16x8_t (&bt)[ASSIGN_TB][D / 32],
+                                            const uint4 *lds, const double *lcn64, const float *lhcn, int32_t *list,
+                                            int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts) {
+    constexpr int KS = D / 32;
+    constexpr int CH = D / 8;
+    const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
     // |x|^2 of each token and its share hb of the C operand
     float hb[ASSIGN_TB];
 #pragma unroll
@@ -401,12 +444,12 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
 #pragma unroll
     for (int s = 0; s < KS; ++s) arow[s] = lds + r16 * CH + ((4 * s + g) ^ (r16 & (CH - 1)));
     const float4 *cnp = reinterpret_cast<const float4 *>(lhcn + 4 * g);
-    auto block = [&](int cb, int j) {   // centroid block cb, read at offset j blocks from the pointers
+    // accumulators of the centroid block at offset j blocks from the pointers
+    auto dots = [&](int j, f32x4_t (&acc)[ASSIGN_TB]) {
         bf16x8_t a[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) a[s] = __builtin_bit_cast(bf16x8_t, arow[s][j * 16 * CH]);
         const float4 cn = cnp[j * 4];
-        f32x4_t acc[ASSIGN_TB];
 #pragma unroll
         for (int b = 0; b < ASSIGN_TB; ++b)
             acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -416,6 +459,9 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
 #pragma unroll
             for (int b = 0; b < ASSIGN_TB; ++b)
                 acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bt[b][s], acc[b], 0, 0, 0);
+    };
+    // fold the accumulators of centroid block cb into the two best keys
+    auto keys = [&](int cb, const f32x4_t (&acc)[ASSIGN_TB]) {
 #pragma unroll
         for (int b = 0; b < ASSIGN_TB; ++b) {
 #pragma unroll
@@ -427,16 +473,27 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
             }
         }
     };
+    // Two-stage pipeline: the matrix cores work on block cb + 1 while the
+    // vector ALUs fold block cb.
+    f32x4_t accA[ASSIGN_TB], accB[ASSIGN_TB];
+    dots(0, accA);
     int cb = 0;
-    for (; cb + 2 <= ncb; cb += 2) {   // two blocks per trip: the second at fixed LDS offsets
-        block(cb, 0);
-        __builtin_amdgcn_sched_barrier(0);   // keeps the second block's operands out of the first's registers
-        block(cb + 1, 1);
+    for (; cb + 2 < ncb; cb += 2) {
+        dots(1, accB);
+        keys(cb, accA);
+        dots(2, accA);
+        keys(cb + 1, accB);
 #pragma unroll
         for (int s = 0; s < KS; ++s) arow[s] += 32 * CH;
         cnp += 8;
     }
-    if (cb < ncb) block(cb, 0);
+    if (cb + 1 < ncb) {
+        dots(1, accB);
+        keys(cb, accA);
+        keys(cb + 1, accB);
+    } else {
+        keys(cb, accA);
+    }
     float xx[ASSIGN_TB];
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) xx[b] = __int_as_float(list[16 * b + r16]);
@@ -513,6 +570,10 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
     }
 }
 
+// Persistent workgroups: each owns a contiguous run of the (head, tile) units,
+// XCD by XCD so that an XCD's L2 serves the tables of a run of heads.  A
+// workgroup stages a head's table once for all of its tiles of that head, and
+// its waves take tiles from an LDS counter until the head's run is done.
 template <int D, typename KVT>
 __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H, int N, const uint16_t *__restrict__ Cb,
                                                                  const double *__restrict__ cnorm, int Kp,
@@ -525,40 +586,75 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
     double *lcn64 = reinterpret_cast<double *>(lds + Kp * CH);
     float *lhcn = reinterpret_cast<float *>(lcn64 + Kp);
     int32_t *lists = reinterpret_cast<int32_t *>(lhcn + Kp);
-    const int h = blockIdx.y, tid = threadIdx.x, wave = tid >> 6;
-    const uint4 *csrc = reinterpret_cast<const uint4 *>(Cb + (size_t)h * Kp * D);
+    int32_t *next = lists + ASSIGN_WAVES * TILE;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int T = (N + TILE - 1) / TILE;   // tiles per head
+    const int64_t U = (int64_t)H * T;
+    const int64_t r = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t u1 = U * (r + 1) / gridDim.x;
     const int nch = Kp * CH;
-    uint4 st[STAGE];
+    for (int64_t u = U * r / gridDim.x; u < u1;) {
+        const int h = (int)(u / T);
+        const int e = (int)min(u1, (int64_t)(h + 1) * T);   // end of this head's run
+        const uint4 *csrc = reinterpret_cast<const uint4 *>(Cb + (size_t)h * Kp * D);
+        uint4 st[STAGE];
 #pragma unroll
-    for (int u = 0; u < STAGE; ++u) {
-        const int i = tid + NT * u;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (i < nch) v = csrc[i];
-        st[u] = v;
-    }
-#pragma unroll
-    for (int u = 0; u < STAGE; ++u) {
-        const int i = tid + NT * u;
-        if (i < nch) {
-            const int row = i / CH, q = i - row * CH;
-            lds[row * CH + (q ^ (row & (CH - 1)))] = st[u];
+        for (int k = 0; k < STAGE; ++k) {
+            const int i = tid + NT * k;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (i < nch) v = csrc[i];
+            st[k] = v;
         }
+#pragma unroll
+        for (int k = 0; k < STAGE; ++k) {
+            const int i = tid + NT * k;
+            if (i < nch) {
+                const int row = i / CH, q = i - row * CH;
+                lds[row * CH + (q ^ (row & (CH - 1)))] = st[k];
+            }
+        }
+        if (tid < Kp) {
+            const double c = cnorm[(size_t)h * Kp + tid];
+            lcn64[tid] = c;
+            lhcn[tid] = c < 1e300 ? -0.5f * (float)c : PAD_HALF_NORM;
+        }
+        if (tid == 0) *next = (int)u;
+        __syncthreads();
+        for (;;) {
+            int m = 0;
+            if (lane == 0) m = atomicAdd(next, 1);
+            m = __builtin_amdgcn_readfirstlane(m);
+            if (m >= e) break;
+            const int tok0 = (m - h * T) * TILE;
+            bf16x8_t bt[ASSIGN_TB][D / 32];
+            assign_load<D, KVT>(src, h, N, tok0, bt);
+            assign_wave<D, KVT>(src, h, N, tok0, bt, lds, lcn64, lhcn, lists + wave * TILE, Kp, pi, pi_hs, counts);
+        }
+        __syncthreads();   // the table is replaced only once every wave is done with it
+        u = e;
     }
-    if (tid < Kp) {
-        const double c = cnorm[(size_t)h * Kp + tid];
-        lcn64[tid] = c;
-        lhcn[tid] = c < 1e300 ? -0.5f * (float)c : PAD_HALF_NORM;
+}
+
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cus[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
     }
-    __syncthreads();
-    const int tok0 = (blockIdx.x * ASSIGN_WAVES + wave) * TILE;
-    if (tok0 >= N) return;
-    assign_wave<D, KVT>(src, h, N, tok0, lds, lcn64, lhcn, lists + wave * TILE, Kp, pi, pi_hs, counts);
+    return cus[dev];
 }
 
 hipError_t launch_assign(int D, int dtype, int H, int N, const Src &src, const uint16_t *Cb, const double *cnorm,
                          int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts, hipStream_t s) {
-    const size_t lds = (size_t)Kp * D * 2 + (size_t)Kp * 12 + ASSIGN_WAVES * TILE * sizeof(int32_t);
-    dim3 g((N + ASSIGN_WAVES * TILE - 1) / (ASSIGN_WAVES * TILE), H), b(64 * ASSIGN_WAVES);
+    const size_t lds = (size_t)Kp * D * 2 + (size_t)Kp * 12 + (ASSIGN_WAVES * TILE + 4) * sizeof(int32_t);
+    // two resident workgroups per CU, at least a tile per wave
+    const int64_t units = (int64_t)H * ((N + TILE - 1) / TILE);
+    if (units >= (int64_t)1 << 31) return hipErrorInvalidValue;
+    const int64_t nb = std::min<int64_t>(2 * (int64_t)device_cus(), (units + ASSIGN_WAVES - 1) / ASSIGN_WAVES);
+    dim3 g((unsigned)std::max<int64_t>(nb, 1)), b(64 * ASSIGN_WAVES);
     QVG_DISPATCH_DT(D, dtype, {
         (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
