@@ -581,7 +581,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
                                                                  int32_t *__restrict__ counts) {
     constexpr int CH = D / 8;
     constexpr int NT = 64 * ASSIGN_WAVES;
-    constexpr int STAGE = 256 * CH / NT;   // table chunks per thread at 256 centroids
+    constexpr int STAGE = (256 * CH + NT - 1) / NT;   // table chunks per thread at 256 centroids
     extern __shared__ uint4 lds[];
     double *lcn64 = reinterpret_cast<double *>(lds + Kp * CH);
     float *lhcn = reinterpret_cast<float *>(lcn64 + Kp);
@@ -721,12 +721,19 @@ hipError_t launch_scatter(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs
 // ---------------------------------------------------------------------------
 //
 // One wave per (centroid, head), four per block.  D/8 lanes cover a row, so a
-// wave reads 512/D rows per load and keeps four such loads in flight; each
-// lane keeps its 8 channels as (sum, error) pairs grown with the error-free
-// two-sum, so every partial sum is exact for the value ranges met in practice
-// and the order the rows arrive in does not matter.  The row slots are merged
-// with lane shuffles; the exact total is rounded once to fp64, divided by the
-// count and rounded to fp32.
+// wave reads 512/D rows per load and keeps four such loads in flight.
+//
+// Fast pass: each lane sums its 8 channels in plain fp64 and their magnitudes
+// in fp32.  Any order of n additions stays within n 2^-53 sum|v| of the exact
+// sum (Higham, Accuracy and Stability of Numerical Algorithms, 2nd ed., 4.2),
+// and rounding to fp64, dividing by the count and rounding to fp32 is monotone
+// in the sum; so when both ends of the interval the bound allows give the same
+// fp32 mean, that mean is the one of the exact sum.  A centroid where some
+// channel fails the test is summed again with the error-free two-sum: each
+// lane keeps (sum, error) pairs, exact for the value ranges met in practice,
+// and the order the rows arrive in does not matter either.  The row slots are
+// merged with lane shuffles; the exact total is rounded once to fp64, divided
+// by the count and rounded to fp32.
 
 __device__ __forceinline__ void two_sum(double &s, double &e, double x) {
     const double t = s + x;
@@ -735,13 +742,73 @@ __device__ __forceinline__ void two_sum(double &s, double &e, double x) {
     s = t;
 }
 
+// Rows n[u] (where valid[u]) of R(P), channels [c0, c0 + 8), for U rows at
+// once: every load of a stage is issued for all rows before any is used.
+template <int D, typename KVT, int U>
+__device__ __forceinline__ void src_rows8(const Src &s, int h, const int (&n)[U], const bool (&valid)[U], int c0,
+                                          float (&v)[U][8]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (valid[u]) load8<KVT>(static_cast<const KVT *>(s.x) + (size_t)h * s.x_hs + (size_t)n[u] * D + c0, v[u]);
+        else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+        }
+    }
+#pragma unroll 1
+    for (int p = 0; p < s.P; ++p) {
+        int k[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) k[u] = valid[u] ? s.pi[p][(size_t)h * s.pi_hs + n[u]] : 0;
+        const KVT *cp = static_cast<const KVT *>(s.cent[p]) + (size_t)h * s.K * D + c0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (valid[u]) {
+                float c[8];
+                load8<KVT>(cp + (size_t)k[u] * D, c);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[u][i] = v[u][i] - c[i];
+            }
+        }
+    }
+}
+
+// Visits the cnt rows of R(P) listed in ord, 8 channels from c0 per lane, as
+// f(v) with v[8] in fp32 (only the lanes whose row slot holds a row call f).
+template <int D, typename KVT, typename F>
+__device__ __forceinline__ void for_rows(const Src &src, int h, const int32_t *ord, int cnt, int slot, int c0, F f) {
+    constexpr int RPI = 64 / (D / 8);   // rows per load
+    constexpr int UNROLL = 4;
+    const int lane = threadIdx.x & 63;
+    for (int i0 = 0; i0 < cnt; i0 += 64) {
+        const int m = cnt - i0 < 64 ? cnt - i0 : 64;
+        const int mine = lane < m ? ord[i0 + lane] : 0;
+        for (int j0 = 0; j0 < m; j0 += RPI * UNROLL) {
+            float v[UNROLL][8];
+            int n[UNROLL];
+            bool ok[UNROLL];
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                const int j = j0 + u * RPI + slot;
+                n[u] = __shfl(mine, j < 64 ? j : 63);
+                ok[u] = j < m;
+            }
+            src_rows8<D, KVT, UNROLL>(src, h, n, ok, c0, v);
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
+                if (ok[u]) f(v[u]);
+        }
+    }
+}
+
+// fp32(fp64(t) / n) for an fp64 t: the rounding of the mean.
+__device__ __forceinline__ float mean_of(double t, int cnt) { return (float)(t / (double)cnt); }
+
 template <int D, typename KVT>
 __global__ __launch_bounds__(256) void k_update(Src src, int N, int K, int Kp, const int32_t *counts,
                                                 const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb,
                                                 double *cnorm, int32_t *zero_cnt, int32_t *zero_fill) {
     constexpr int LPR = D / 8;        // lanes per row
-    constexpr int RPI = 64 / LPR;     // rows per load
-    constexpr int UNROLL = 4;
     const int lane = threadIdx.x & 63;
     const int k = blockIdx.x * 4 + (threadIdx.x >> 6), h = blockIdx.y;
     if (k >= K) return;
@@ -753,45 +820,63 @@ __global__ __launch_bounds__(256) void k_update(Src src, int N, int K, int Kp, c
     if (cnt == 0) return;   // empty cluster keeps its centroid
     const int32_t *ord = order + (size_t)h * N + offsets[(size_t)h * Kp + k];
     const int slot = lane / LPR, c0 = (lane % LPR) * 8;
-    double hs[8], es[8];
+    float mean[8];
+    bool ok = true;
+    {
+        double hs[8];
+        float ab[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) { hs[i] = 0.0; es[i] = 0.0; }
-    for (int i0 = 0; i0 < cnt; i0 += 64) {
-        const int m = cnt - i0 < 64 ? cnt - i0 : 64;
-        const int mine = lane < m ? ord[i0 + lane] : 0;
-        for (int j0 = 0; j0 < m; j0 += RPI * UNROLL) {
-            float v[UNROLL][8];
+        for (int i = 0; i < 8; ++i) { hs[i] = 0.0; ab[i] = 0.f; }
+        for_rows<D, KVT>(src, h, ord, cnt, slot, c0, [&](const float (&v)[8]) {
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                const int j = j0 + u * RPI + slot;
-                const int n = __shfl(mine, j < 64 ? j : 63);
-                if (j < m) src_row8<D, KVT>(src, h, n, c0, v[u]);
+            for (int i = 0; i < 8; ++i) {
+                hs[i] += (double)v[i];
+                ab[i] += fabsf(v[i]);
             }
+        });
 #pragma unroll
-            for (int u = 0; u < UNROLL; ++u) {
-                if (j0 + u * RPI + slot < m) {
+        for (int o = LPR; o < 64; o <<= 1) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) two_sum(hs[i], es[i], (double)v[u][i]);
-                }
+            for (int i = 0; i < 8; ++i) {
+                hs[i] += __shfl_xor(hs[i], o);
+                ab[i] += __shfl_xor(ab[i], o);
             }
         }
-    }
-#pragma unroll
-    for (int o = LPR; o < 64; o <<= 1) {
+        // sum|v| <= 1.07 ab (an fp32 sum of cnt <= 2^20 magnitudes); the bound
+        // takes 2^-51 for 1.1 x 2^-53 with room for both roundings
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const double oh = __shfl_xor(hs[i], o), oe = __shfl_xor(es[i], o);
-            two_sum(hs[i], es[i], oh);
-            es[i] += oe;
+            const double b = (double)ab[i] * (double)cnt * 0x1p-51 + fabs(hs[i]) * 0x1p-50;
+            const float lo = mean_of(hs[i] - b, cnt), hi = mean_of(hs[i] + b, cnt);
+            ok = ok && (lo == hi) && cnt <= (1 << 20);
+            mean[i] = lo;
         }
+    }
+    if (!__all(ok)) {   // a channel near a rounding boundary: sum the rows exactly
+        double hs[8], es[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { hs[i] = 0.0; es[i] = 0.0; }
+        for_rows<D, KVT>(src, h, ord, cnt, slot, c0, [&](const float (&v)[8]) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) two_sum(hs[i], es[i], (double)v[i]);
+        });
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const double oh = __shfl_xor(hs[i], o), oe = __shfl_xor(es[i], o);
+                two_sum(hs[i], es[i], oh);
+                es[i] += oe;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mean[i] = mean_of(hs[i] + es[i], cnt);
     }
     double sq = 0.0;
     if (slot == 0) {
-        float mean[8];
         uint32_t b[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            mean[i] = (float)((hs[i] + es[i]) / (double)cnt);
             b[i] = f32_to_bf16(mean[i]);
             const double bd = (double)bf16_to_f32(b[i]);
             sq += bd * bd;
