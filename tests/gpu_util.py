@@ -95,3 +95,80 @@ def gap_ok(Xop: np.ndarray, C: np.ndarray, got: np.ndarray, ref: np.ndarray, rel
     gap = np.abs(D[r, g] - D[r, o])
     scale = (xb * xb).sum(1) + np.maximum(cn[g], cn[o])
     return len(mis), float((gap / scale).max())
+
+
+def oracle_chunks(oc, X, chunk_tokens, heads=None):
+    heads = list(range(X.shape[0])) if heads is None else heads
+    out, cache = [], None
+    for c in range(-(-X.shape[1] // chunk_tokens)):
+        b, e = c * chunk_tokens, min((c + 1) * chunk_tokens, X.shape[1])
+        per_head = []
+        for h in heads:
+            hc = None if cache is None else cache[h]
+            per_head.append(oracle.encode_chunk(X[h:h + 1, b:e], oc, cache=hc, head_offset=h))
+        out.append(per_head)
+        cache = {h: per_head[i].cache for i, h in enumerate(heads)}
+    return out
+
+
+def check_chunk(oc, Xc, g, ora, h_local, h_global, tag):
+    """g: GPU chunk arrays (all heads); ora: oracle Encoded for one head."""
+    T = oc.n_stages
+    stats = {}
+    exact = True
+    for t in range(T):
+        mis = int((g["assign"][t, h_global] != ora.assign[t, 0]).sum())
+        stats[t + 1] = mis
+        exact &= mis == 0
+    say(f"  {tag} head {h_global}: assignment mismatches per stage {stats}")
+    N = Xc.shape[1]
+    if exact:
+        np.testing.assert_array_equal(g["centroids"][:, h_global], ora.centroids[:, 0])
+        np.testing.assert_array_equal(g["scales"][h_global], ora.scales[0])
+        np.testing.assert_array_equal(g["codes"][h_global], ora.codes[0])
+        return 0
+    # the assignment re-decides the two best candidates on exact distances, so a
+    # disagreement needs the true nearest centroid outside the fp32 top two
+    assert stats[1] <= int(1e-4 * N), stats
+    # validity of the HIP result on its own residual chain
+    R = Xc[h_global].astype(np.float64)
+    for t in range(T):
+        Ct = g["centroids"][t, h_global].astype(np.float64)
+        lab = g["assign"][t, h_global].astype(int)
+        ref = oracle.assign(R, Ct, "parity")
+        n_mis, worst = gap_ok(R, Ct, lab, ref)
+        assert worst < 1e-4, (t, n_mis, worst)
+        R = (R - Ct[lab]).astype(np.float32).astype(np.float64)
+    _, packed, s = oracle.group_quant(R.astype(np.float32), oc.group_size)
+    np.testing.assert_array_equal(g["scales"][h_global], s)
+    np.testing.assert_array_equal(g["codes"][h_global], packed)
+    return sum(stats.values())
+
+
+def check_chunk_properties(oc: oracle.CodecConfig, Xc: np.ndarray, g, h: int, tag: str) -> None:
+    """Checks that hold for any chunk without replaying the centroid chain:
+    every stage's labels are the exact nearest of the HIP path's own stored
+    centroids on the residual they define, the codes and scales are the
+    oracle's quantiser of the last residual, and the decoded rows are the
+    oracle's reconstruction of the stored encoding."""
+    R = Xc[h].astype(np.float64)
+    for t in range(oc.n_stages):
+        Ct = g["centroids"][t, h].astype(np.float64)
+        lab = g["assign"][t, h].astype(int)
+        ref = oracle.assign(R, Ct, "parity")
+        n = int((ref != lab).sum())
+        say(f"  {tag} head {h} stage {t + 1}: labels not nearest {n}")
+        assert n == 0
+        R = (R - Ct[lab]).astype(np.float32).astype(np.float64)
+    _, packed, s = oracle.group_quant(R.astype(np.float32), oc.group_size)
+    np.testing.assert_array_equal(g["scales"][h], s)
+    np.testing.assert_array_equal(g["codes"][h], packed)
+
+
+def layer_on_device(p: synthkv.Preset) -> torch.Tensor:
+    """K and V of a layer as one [2H][N][d] bf16 tensor on the device (the
+    benchmark's layout: a [2][H][N][d] buffer viewed as 2H heads)."""
+    X = torch.empty((2, p.heads, p.n_tokens, p.d), dtype=torch.bfloat16, device=DEV)
+    for i, t in enumerate(("K", "V")):
+        X[i] = torch.cat(list(synthkv.gen_torch(p, t, DEV, frames_per_call=p.chunk_frames)), dim=1)
+    return X.view(2 * p.heads, p.n_tokens, p.d)

@@ -13,57 +13,10 @@ import torch
 
 import oracle
 import synthkv
-from gpu_util import DEV, fetch, gap_ok, gcfg, gpu_encode_chunks, lib, ocfg, say, to_np
+from gpu_util import DEV, check_chunk as _check_chunk, fetch, gcfg, gpu_encode_chunks, lib, ocfg, say, to_np
+from gpu_util import oracle_chunks as _oracle_chunks
 
 pytestmark = pytest.mark.gpu
-
-
-def _oracle_chunks(oc, X, chunk_tokens, heads=None):
-    heads = list(range(X.shape[0])) if heads is None else heads
-    out, cache = [], None
-    for c in range(-(-X.shape[1] // chunk_tokens)):
-        b, e = c * chunk_tokens, min((c + 1) * chunk_tokens, X.shape[1])
-        per_head = []
-        for h in heads:
-            hc = None if cache is None else cache[h]
-            per_head.append(oracle.encode_chunk(X[h:h + 1, b:e], oc, cache=hc, head_offset=h))
-        out.append(per_head)
-        cache = {h: per_head[i].cache for i, h in enumerate(heads)}
-    return out
-
-
-def _check_chunk(oc, Xc, g, ora, h_local, h_global, tag):
-    """g: GPU chunk arrays (all heads); ora: oracle Encoded for one head."""
-    T = oc.n_stages
-    stats = {}
-    exact = True
-    for t in range(T):
-        mis = int((g["assign"][t, h_global] != ora.assign[t, 0]).sum())
-        stats[t + 1] = mis
-        exact &= mis == 0
-    say(f"  {tag} head {h_global}: assignment mismatches per stage {stats}")
-    N = Xc.shape[1]
-    if exact:
-        np.testing.assert_array_equal(g["centroids"][:, h_global], ora.centroids[:, 0])
-        np.testing.assert_array_equal(g["scales"][h_global], ora.scales[0])
-        np.testing.assert_array_equal(g["codes"][h_global], ora.codes[0])
-        return 0
-    # the assignment re-decides the two best candidates on exact distances, so a
-    # disagreement needs the true nearest centroid outside the fp32 top two
-    assert stats[1] <= int(1e-4 * N), stats
-    # validity of the HIP result on its own residual chain
-    R = Xc[h_global].astype(np.float64)
-    for t in range(T):
-        Ct = g["centroids"][t, h_global].astype(np.float64)
-        lab = g["assign"][t, h_global].astype(int)
-        ref = oracle.assign(R, Ct, "parity")
-        n_mis, worst = gap_ok(R, Ct, lab, ref)
-        assert worst < 1e-4, (t, n_mis, worst)
-        R = (R - Ct[lab]).astype(np.float32).astype(np.float64)
-    _, packed, s = oracle.group_quant(R.astype(np.float32), oc.group_size)
-    np.testing.assert_array_equal(g["scales"][h_global], s)
-    np.testing.assert_array_equal(g["codes"][h_global], packed)
-    return sum(stats.values())
 
 
 def _run(p, tensor, heads=None, n_tokens=None, oracle_heads=None, **kw):
