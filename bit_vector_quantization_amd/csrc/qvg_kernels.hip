@@ -33,11 +33,16 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
 
-// Round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values to packed bf16 (lo in bits 0-15), rounded to nearest even by
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xFFFFu; }
 
 // OCP FP8 E4M3FN of a non-negative value: round to nearest even, saturating at
 // 448 (code 0x7E).  Below 2^-6 the grid is the subnormal one, 2^-9 apart.
@@ -102,21 +107,6 @@ __device__ __forceinline__ void load16<float>(const float *p, float (&v)[16]) {
     }
 }
 
-__device__ __forceinline__ void store16_bf16(uint16_t *p, const float (&v)[16]) {
-    uint32_t w[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = f32_to_bf16(v[2 * i]) | (f32_to_bf16(v[2 * i + 1]) << 16);
-    uint4 *q = reinterpret_cast<uint4 *>(p);
-    q[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    q[1] = make_uint4(w[4], w[5], w[6], w[7]);
-}
-
-__device__ __forceinline__ void store16_f32(float *p, const float (&v)[16]) {
-    float4 *q = reinterpret_cast<float4 *>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) q[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
-}
-
 template <typename T>
 __device__ __forceinline__ void load8(const T *p, float (&v)[8]);
 
@@ -165,8 +155,8 @@ __device__ __forceinline__ uint4 src_row8_bf16(const Src &s, int h, int64_t n, i
     }
     float v[8];
     src_row8<D, KVT>(s, h, n, c0, v);
-    return make_uint4(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16),
-                      f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16), f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16));
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                      pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
 }
 
 #define QVG_DISPATCH_DT(D, dtype, ...)                          \
@@ -349,8 +339,6 @@ constexpr int TILE = 16 * ASSIGN_TB;      // tokens per wave
 constexpr int ASSIGN_WAVES = 8;           // waves per workgroup
 constexpr float PAD_HALF_NORM = -1e30f;   // padding rows: never the nearest
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
 __device__ __forceinline__ float fmax_key(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, __FLT_MAX__); }
 __device__ __forceinline__ float fmin_key(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -__FLT_MAX__); }
 
@@ -399,10 +387,10 @@ __device__ __forceinline__ void assign_load(const Src &src, int h, int N, int to
 #pragma unroll
         for (int s = 0; s < KS; ++s)
             bt[b][s] = __builtin_bit_cast(
-                bf16x8_t, make_uint4(f32_to_bf16(v[s][0]) | (f32_to_bf16(v[s][1]) << 16),
-                                     f32_to_bf16(v[s][2]) | (f32_to_bf16(v[s][3]) << 16),
-                                     f32_to_bf16(v[s][4]) | (f32_to_bf16(v[s][5]) << 16),
-                                     f32_to_bf16(v[s][6]) | (f32_to_bf16(v[s][7]) << 16)));
+                bf16x8_t, make_uint4(pack_bf16x2(v[s][0], v[s][1]),
+                                     pack_bf16x2(v[s][2], v[s][3]),
+                                     pack_bf16x2(v[s][4], v[s][5]),
+                                     pack_bf16x2(v[s][6], v[s][7])));
     }
 }
 
@@ -997,56 +985,292 @@ hipError_t launch_quant(int D, int dtype, int H, int N, const Src &src, const vo
 // fused dequantise + reconstruct
 // ---------------------------------------------------------------------------
 //
-// One thread owns 16 channels of one token: one 32-bit word of codes, one scale
-// byte, T assignment bytes, T gathered 16-channel centroid slices (the chunk's
-// tables stay in L2), and a 32- or 64-byte store.  Blocks walk (head, token)
-// tiles, XCD-contiguous.
+// Per (token, slice): two 16-bit words of codes, two scale bytes, T assignment
+// bytes, T centroid rows (two 8-channel chunks each) and two streaming stores.
 
-template <int D, typename CentT, typename OutT>
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// A decode slice: lane j of a token's D/16 lanes owns channels [8j, 8j + 8) and
+// [D/2 + 8j, D/2 + 8j + 8), so each store instruction of a token's lanes writes
+// one contiguous half row (whole cache lines).
+
+// y[i] = (q_i - 1.5) s for the 8 two-bit codes in the low 16 bits of w
+// (channel i in bits 2i, 2i+1).  With s != 0 every term is exact, so one fma
+// per channel gives the same value; s == 0 keeps the expression's signed zeros
+// (-0 below the midpoint).
+__device__ __forceinline__ void dequant8(uint32_t w, float s, float *y) {
+    if (s != 0.f) {
+        const float m = -1.5f * s;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            uint32_t b = (w >> (2 * g)) & 0x0303u;   // channels g and g + 4
+            asm volatile("" : "+v"(b));             // keeps the byte extracts as v_cvt_f32_ubyte0/1
+            y[g] = fmaf((float)(b & 0xFFu), s, m);
+            y[g + 4] = fmaf((float)((b >> 8) & 0xFFu), s, m);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = ((w >> (2 * i)) & 2u) ? 0.f : -0.f;
+    }
+}
+
+// y[i] += c_i for 8 centroid values (bf16: one 16-byte chunk; fp32: two)
+template <typename CentT>
+__device__ __forceinline__ void add8(const uint4 *c, float *y) {
+    if constexpr (sizeof(CentT) == 2) {
+        const uint32_t b[4] = {c[0].x, c[0].y, c[0].z, c[0].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[2 * i] = y[2 * i] + __uint_as_float(b[i] << 16);
+            y[2 * i + 1] = y[2 * i + 1] + __uint_as_float(b[i] & 0xFFFF0000u);
+        }
+    } else {
+        const float f[8] = {__uint_as_float(c[0].x), __uint_as_float(c[0].y), __uint_as_float(c[0].z),
+                            __uint_as_float(c[0].w), __uint_as_float(c[1].x), __uint_as_float(c[1].y),
+                            __uint_as_float(c[1].z), __uint_as_float(c[1].w)};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = y[i] + f[i];
+    }
+}
+
+// 8 outputs to p, bf16 or fp32, with streaming stores (the output is not read
+// back here; keeping it out of L2 leaves room for the centroid tables)
+template <typename OutT>
+__device__ __forceinline__ void store8_out(OutT *p, const float *v) {
+    if constexpr (sizeof(OutT) == 2) {
+        const u32x4_t q = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                           pack_bf16x2(v[6], v[7])};
+        __builtin_nontemporal_store(q, reinterpret_cast<u32x4_t *>(p));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4_t q = {__float_as_uint(v[4 * i]), __float_as_uint(v[4 * i + 1]),
+                               __float_as_uint(v[4 * i + 2]), __float_as_uint(v[4 * i + 3])};
+            __builtin_nontemporal_store(q, reinterpret_cast<u32x4_t *>(p) + i);
+        }
+    }
+}
+
+// The per-token inputs of slice j: two 16-bit code words and two scales.
+template <int D>
+__device__ __forceinline__ void slice_inputs(const uint8_t *codes, const uint8_t *scales, size_t row, int G, int j,
+                                             uint32_t &w0, uint32_t &w1, uint32_t &sc0, uint32_t &sc1) {
+    const uint16_t *c16 = reinterpret_cast<const uint16_t *>(codes + row * (D / 4));
+    w0 = c16[j];
+    w1 = c16[D / 16 + j];
+    sc0 = scales[row * (D / G) + (8 * j) / G];
+    sc1 = scales[row * (D / G) + (D / 2 + 8 * j) / G];
+}
+
+// Dequantise slice j, add the stages' centroid chunks from fetch(t, half, uint4*)
+// for t = T-1 .. 0, and store the two half rows of rb.
+template <int D, typename CentT, typename OutT, typename Fetch>
+__device__ __forceinline__ void decode_slice(int T, uint32_t w0, uint32_t w1, uint32_t sc0, uint32_t sc1, int j,
+                                             OutT *rb, Fetch fetch) {
+    float y[16];
+    dequant8(w0, e4m3_decode(sc0), y);
+    dequant8(w1, e4m3_decode(sc1), y + 8);
+    for (int t = T - 1; t >= 0; --t) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            uint4 c[sizeof(CentT) == 2 ? 1 : 2];
+            fetch(t, hf, c);
+            add8<CentT>(c, y + 8 * hf);
+        }
+    }
+    store8_out<OutT>(rb + 8 * j, y);
+    store8_out<OutT>(rb + D / 2 + 8 * j, y + 8);
+}
+
+// Tables in L2: one thread per (token, slice) for DEC_U tokens; blocks walk
+// (head, token) tiles, XCD-contiguous.  For TT >= 0 the stage count is a
+// compile-time constant and every load of the thread's tokens is in flight
+// before the first is used; TT = -1 takes T at run time.
+constexpr int DEC_U = 2;
+
+template <int D, typename CentT, typename OutT, int TT>
 __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                                 const uint8_t *__restrict__ assign, const CentT *__restrict__ cent,
-                                                int64_t cap, int chunk_tokens, int H, int K, int T, int G,
+                                                int64_t cap, int chunk_tokens, int H, int K, int T_rt, int G,
                                                 int64_t tok_begin, int64_t ntok, OutT *__restrict__ out,
                                                 int64_t out_hs, uint32_t blocks_per_head) {
     constexpr int SL = D / 16;
     constexpr int TPB = 256 / SL;
+    constexpr int TS = TT > 0 ? TT : 1;
+    const int T = TT >= 0 ? TT : T_rt;
     const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int h = tile / blocks_per_head;
-    const int64_t nl = (int64_t)(tile % blocks_per_head) * TPB + threadIdx.x / SL;
+    const int64_t nl0 = (int64_t)(tile % blocks_per_head) * (TPB * DEC_U) + threadIdx.x / SL;
     const int j = threadIdx.x % SL;
-    if (nl >= ntok) return;
-    const int64_t n = tok_begin + nl;
-    const int64_t c = n / chunk_tokens;
-    const size_t row = (size_t)h * cap + n;
-    const uint32_t w = reinterpret_cast<const uint32_t *>(codes + row * (D / 4))[j];
-    const float s = e4m3_decode(scales[row * (D / G) + (16 * j) / G]);
-    float y[16];
+    if (nl0 >= ntok) return;
+    uint32_t w0[DEC_U], w1[DEC_U], sc0[DEC_U], sc1[DEC_U];
+    int k[DEC_U][TS];
+    int64_t n[DEC_U];
+    bool ok[DEC_U];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = ((float)((w >> (2 * i)) & 3u) - 1.5f) * s;
-    for (int t = T - 1; t >= 0; --t) {
-        int k = assign[((size_t)t * H + h) * cap + n];
-        k = k < K ? k : K - 1;   // a corrupt byte cannot leave the chunk's table
-        float cv[16];
-        load16<CentT>(cent + ((((size_t)c * T + t) * H + h) * K + k) * D + 16 * j, cv);
+    for (int u = 0; u < DEC_U; ++u) {
+        ok[u] = nl0 + u * TPB < ntok;
+        n[u] = tok_begin + (ok[u] ? nl0 + u * TPB : nl0);
+        slice_inputs<D>(codes, scales, (size_t)h * cap + n[u], G, j, w0[u], w1[u], sc0[u], sc1[u]);
+        if constexpr (TT > 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) y[i] = y[i] + cv[i];
+            for (int t = 0; t < TT; ++t) {
+                const int kk = assign[((size_t)t * H + h) * cap + n[u]];
+                k[u][t] = kk < K ? kk : K - 1;   // a corrupt byte cannot leave the chunk's table
+            }
+        }
     }
-    OutT *o = out + (size_t)h * out_hs + (size_t)nl * D + 16 * j;
-    if constexpr (sizeof(OutT) == 2) store16_bf16(reinterpret_cast<uint16_t *>(o), y);
-    else store16_f32(reinterpret_cast<float *>(o), y);
+#pragma unroll
+    for (int u = 0; u < DEC_U; ++u) {
+        if (!ok[u]) continue;
+        const int64_t c = n[u] / chunk_tokens;
+        OutT *rb = out + (size_t)h * out_hs + (size_t)(n[u] - tok_begin) * D;
+        decode_slice<D, CentT, OutT>(T, w0[u], w1[u], sc0[u], sc1[u], j, rb, [&](int t, int hf, uint4 *cv) {
+            int kk;
+            if constexpr (TT > 0) {
+                kk = k[u][t];
+            } else {
+                kk = assign[((size_t)t * H + h) * cap + n[u]];
+                kk = kk < K ? kk : K - 1;
+            }
+            const uint4 *src = reinterpret_cast<const uint4 *>(
+                cent + ((((size_t)c * T + t) * H + h) * K + kk) * D + hf * (D / 2) + 8 * j);
+            cv[0] = src[0];
+            if constexpr (sizeof(CentT) == 4) cv[1] = src[1];
+        });
+    }
+}
+
+// Tables in LDS: one workgroup per (chunk, head) stages the chunk's T centroid
+// tables of that head (swizzled 16-byte chunks) and streams the chunk's tokens,
+// DEC_LDS_U (token, slice) items per thread per trip with all their global loads
+// issued together; the centroid rows then come from LDS instead of L2.
+constexpr int DEC_LDS_THREADS = 1024;
+constexpr int DEC_LDS_U = 2;
+constexpr size_t DEC_LDS_MAX = 160 * 1024 - 1024;   // table bytes that fit one workgroup
+
+template <int D, typename CentT, typename OutT, int TT>
+__global__ __launch_bounds__(DEC_LDS_THREADS) void k_decode_lds(const uint8_t *__restrict__ codes,
+                                                                const uint8_t *__restrict__ scales,
+                                                                const uint8_t *__restrict__ assign,
+                                                                const CentT *__restrict__ cent, int64_t cap,
+                                                                int chunk_tokens, int H, int K, int G,
+                                                                int64_t tok_begin, int64_t tok_end, int64_t c_first,
+                                                                OutT *__restrict__ out, int64_t out_hs) {
+    constexpr int SL = D / 16;                              // slices per token
+    constexpr int CHR = D * (int)sizeof(CentT) / 16;        // 16-byte chunks per table row
+    constexpr int CPH = CHR / 2 / SL;                       // chunks per half slice (1 bf16, 2 fp32)
+    extern __shared__ uint4 tab[];
+    const int h = (int)(blockIdx.x % H);
+    const int64_t c = c_first + blockIdx.x / H;
+    const int tid = threadIdx.x;
+    for (int t = 0; t < TT; ++t) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(cent + (((size_t)c * TT + t) * H + h) * K * D);
+        for (int i = tid; i < K * CHR; i += DEC_LDS_THREADS) {
+            const int row = i / CHR, q = i - row * CHR;
+            const int r = t * K + row;
+            tab[r * CHR + (q ^ (r & (CHR - 1)))] = src[i];
+        }
+    }
+    __syncthreads();
+    const int64_t tb = max(tok_begin, c * chunk_tokens), te = min(tok_end, (c + 1) * chunk_tokens);
+    const int items = (int)(te - tb) * SL;
+    for (int i0 = tid; i0 < items; i0 += DEC_LDS_THREADS * DEC_LDS_U) {
+        uint32_t w0[DEC_LDS_U], w1[DEC_LDS_U], sc0[DEC_LDS_U], sc1[DEC_LDS_U];
+        int k[DEC_LDS_U][TT];
+        int64_t n[DEC_LDS_U];
+        int jj[DEC_LDS_U];
+        bool ok[DEC_LDS_U];
+#pragma unroll
+        for (int u = 0; u < DEC_LDS_U; ++u) {
+            const int it0 = i0 + u * DEC_LDS_THREADS;
+            ok[u] = it0 < items;
+            const int it = ok[u] ? it0 : i0;
+            n[u] = tb + it / SL;
+            jj[u] = it % SL;
+            slice_inputs<D>(codes, scales, (size_t)h * cap + n[u], G, jj[u], w0[u], w1[u], sc0[u], sc1[u]);
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const int kk = assign[((size_t)t * H + h) * cap + n[u]];
+                k[u][t] = kk < K ? kk : K - 1;   // a corrupt byte cannot leave the chunk's table
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < DEC_LDS_U; ++u) {
+            if (!ok[u]) continue;
+            OutT *rb = out + (size_t)h * out_hs + (size_t)(n[u] - tok_begin) * D;
+            decode_slice<D, CentT, OutT>(TT, w0[u], w1[u], sc0[u], sc1[u], jj[u], rb, [&](int t, int hf, uint4 *cv) {
+                const int r = t * K + k[u][t];
+                const int q0 = CPH * (hf * SL + jj[u]);
+#pragma unroll
+                for (int q = 0; q < CPH; ++q) cv[q] = tab[r * CHR + ((q0 + q) ^ (r & (CHR - 1)))];
+            });
+        }
+    }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
-    const int TPB = 256 / (a.D / 16);
+    const size_t tab_bytes = (size_t)a.T * a.K * a.D * (a.cent_dtype == DT_BF16 ? 2 : 4);
+    if (a.T >= 1 && a.T <= 4 && tab_bytes <= DEC_LDS_MAX) {
+        const int64_t c0 = a.tok_begin / a.chunk_tokens, c1 = (a.tok_begin + a.ntok - 1) / a.chunk_tokens;
+        if ((c1 - c0 + 1) * a.H < (int64_t)UINT32_MAX) {
+            dim3 g((unsigned)((c1 - c0 + 1) * a.H)), b(DEC_LDS_THREADS);
+#define QVG_DECL(DD, CT, OT, TT)                                                                                  \
+    do {                                                                                                          \
+        (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, CT, OT, TT>,                                     \
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)tab_bytes);                    \
+        hipLaunchKernelGGL((k_decode_lds<DD, CT, OT, TT>), g, b, tab_bytes, s, a.codes, a.scales, a.assign,        \
+                           (const CT *)a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.G, a.tok_begin,                  \
+                           a.tok_begin + a.ntok, c0, (OT *)a.out, a.out_hs);                                      \
+    } while (0)
+#define QVG_DECL_T(DD, CT, OT)                             \
+    do {                                                   \
+        switch (a.T) {                                     \
+            case 1: QVG_DECL(DD, CT, OT, 1); break;        \
+            case 2: QVG_DECL(DD, CT, OT, 2); break;        \
+            case 3: QVG_DECL(DD, CT, OT, 3); break;        \
+            default: QVG_DECL(DD, CT, OT, 4); break;       \
+        }                                                  \
+    } while (0)
+#define QVG_DECL_O(DD, CT)                                 \
+    do {                                                   \
+        if (a.out_dtype == DT_BF16) QVG_DECL_T(DD, CT, uint16_t); \
+        else QVG_DECL_T(DD, CT, float);                    \
+    } while (0)
+#define QVG_DECL_C(DD)                                     \
+    do {                                                   \
+        if (a.cent_dtype == DT_BF16) QVG_DECL_O(DD, uint16_t); \
+        else QVG_DECL_O(DD, float);                        \
+    } while (0)
+            if (a.D == 128) QVG_DECL_C(128); else QVG_DECL_C(64);
+#undef QVG_DECL_C
+#undef QVG_DECL_O
+#undef QVG_DECL_T
+#undef QVG_DECL
+            return hipGetLastError();
+        }
+    }
+    const int TPB = 256 / (a.D / 16) * DEC_U;
     const uint32_t bph = (uint32_t)((a.ntok + TPB - 1) / TPB);
     dim3 g(bph * a.H), b(256);
-#define QVG_DEC(DD, CT, OT)                                                                                       \
-    hipLaunchKernelGGL((k_decode<DD, CT, OT>), g, b, 0, s, a.codes, a.scales, a.assign, (const CT *)a.cent, a.cap, \
-                       a.chunk_tokens, a.H, a.K, a.T, a.G, a.tok_begin, a.ntok, (OT *)a.out, a.out_hs, bph)
+#define QVG_DEC(DD, CT, OT, TT)                                                                                   \
+    hipLaunchKernelGGL((k_decode<DD, CT, OT, TT>), g, b, 0, s, a.codes, a.scales, a.assign, (const CT *)a.cent,    \
+                       a.cap, a.chunk_tokens, a.H, a.K, a.T, a.G, a.tok_begin, a.ntok, (OT *)a.out, a.out_hs, bph)
+#define QVG_DEC_T(DD, CT, OT)                              \
+    do {                                                   \
+        switch (a.T) {                                     \
+            case 0: QVG_DEC(DD, CT, OT, 0); break;         \
+            case 1: QVG_DEC(DD, CT, OT, 1); break;         \
+            case 2: QVG_DEC(DD, CT, OT, 2); break;         \
+            case 3: QVG_DEC(DD, CT, OT, 3); break;         \
+            case 4: QVG_DEC(DD, CT, OT, 4); break;         \
+            default: QVG_DEC(DD, CT, OT, -1); break;       \
+        }                                                  \
+    } while (0)
 #define QVG_DEC_O(DD, CT)                                  \
     do {                                                   \
-        if (a.out_dtype == DT_BF16) QVG_DEC(DD, CT, uint16_t); \
-        else QVG_DEC(DD, CT, float);                       \
+        if (a.out_dtype == DT_BF16) QVG_DEC_T(DD, CT, uint16_t); \
+        else QVG_DEC_T(DD, CT, float);                     \
     } while (0)
 #define QVG_DEC_C(DD)                                      \
     do {                                                   \
@@ -1056,6 +1280,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     if (a.D == 128) QVG_DEC_C(128); else QVG_DEC_C(64);
 #undef QVG_DEC_C
 #undef QVG_DEC_O
+#undef QVG_DEC_T
 #undef QVG_DEC
     return hipGetLastError();
 }

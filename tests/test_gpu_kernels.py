@@ -57,7 +57,8 @@ def _oracle_encoding(rng, H, N, d, K, T, G, dtype):
 
 @pytest.mark.parametrize("H,N,d,K,T,G,dtype", [(2, 700, 128, 32, 2, 64, "bf16"), (1, 333, 128, 256, 4, 16, "bf16"),
                                                (2, 200, 64, 16, 1, 16, "f32"), (1, 97, 128, 8, 0, 64, "bf16"),
-                                               (3, 129, 64, 20, 3, 32, "bf16")])
+                                               (3, 129, 64, 20, 3, 32, "bf16"), (2, 257, 128, 16, 6, 32, "bf16"),
+                                               (1, 95, 64, 12, 5, 16, "f32")])
 def test_dequant_reconstruct_bit_exact(H, N, d, K, T, G, dtype):
     say(f"dequant_reconstruct H={H} N={N} d={d} K={K} T={T} G={G} {dtype}")
     q = lib()
@@ -88,7 +89,10 @@ def _assign_case(rng, which):
         X = oracle.bf16_round(rng.standard_normal((1, 515, 64)) * 4).astype(np.float32)
         C = X[0, rng.integers(0, 515, 20)].copy()[None]
         C[0, 7] = C[0, 3]                    # duplicated centroids: the lower index wins
+        C[0, 11] = C[0, 3]                   # three copies: still the lowest
         C[0, 19] = C[0, 0]
+        X[0, 5] = C[0, 3]                    # tokens at distance zero from the copies
+        X[0, 400] = C[0, 3]
         return X, C, 64
     # fewer tokens than centroids, K not a multiple of 16
     X = oracle.bf16_round(rng.standard_normal((2, 37, 128))).astype(np.float32)
