@@ -55,9 +55,14 @@ __device__ __forceinline__ uint32_t e4m3_encode_nonneg(float v) {
     return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// Value of an E4M3FN code: its 4 exponent and 3 mantissa bits placed at fp32's
+// bits 26..20 read as fp32 with bias 127 instead of 7, so one exact scaling by
+// 2^120 gives the value; subnormal codes land on fp32 subnormals, which the
+// scaling keeps exact (fp32 denormals are not flushed).  S.1111.111 is NaN.
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
-    uint32_t e = c >> 3, m = c & 7u;
-    return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    const float v = __uint_as_float((c & 0x7Fu) << 20) * 0x1p120f;
+    const float mag = (c & 0x7Fu) == 0x7Fu ? __builtin_nanf("") : v;
+    return (c & 0x80u) ? -mag : mag;
 }
 
 // ---------------------------------------------------------------------------
@@ -996,8 +1001,8 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // y[i] = (q_i - 1.5) s for the 8 two-bit codes in the low 16 bits of w
 // (channel i in bits 2i, 2i+1).  With s != 0 every term is exact, so one fma
-// per channel gives the same value; s == 0 keeps the expression's signed zeros
-// (-0 below the midpoint).
+// per channel gives the same value; a zero scale takes the expression as
+// written, for its signed zeros.
 __device__ __forceinline__ void dequant8(uint32_t w, float s, float *y) {
     if (s != 0.f) {
         const float m = -1.5f * s;
@@ -1010,7 +1015,7 @@ __device__ __forceinline__ void dequant8(uint32_t w, float s, float *y) {
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = ((w >> (2 * i)) & 2u) ? 0.f : -0.f;
+        for (int i = 0; i < 8; ++i) y[i] = ((float)((w >> (2 * i)) & 3u) - 1.5f) * s;
     }
 }
 
@@ -1141,85 +1146,102 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ code
     }
 }
 
-// Tables in LDS: one workgroup per (chunk, head) stages the chunk's T centroid
-// tables of that head (swizzled 16-byte chunks) and streams the chunk's tokens,
-// DEC_LDS_U (token, slice) items per thread per trip with all their global loads
-// issued together; the centroid rows then come from LDS instead of L2.
+// Tables in LDS: one workgroup per (chunk, head, half row) stages that half of
+// the chunk's T centroid tables of the head (swizzled 16-byte chunks, 64 KiB at
+// T = 2, K = 256, d = 128, so two workgroups share a CU; PARTS = 1 would take
+// whole rows) and streams the chunk's tokens.  Lane jj of a token's D/16 lanes owns 8 channels, so one store
+// instruction writes 128 contiguous bytes per token; each thread keeps its lane
+// and walks tokens with a fixed stride, DEC_LDS_U tokens per trip with all their
+// global loads issued together.
 constexpr int DEC_LDS_THREADS = 1024;
-constexpr int DEC_LDS_U = 2;
+constexpr int DEC_LDS_U = 4;
+constexpr int DEC_PARTS = 2;   // workgroups per (chunk, head), each with its part of every row
 constexpr size_t DEC_LDS_MAX = 160 * 1024 - 1024;   // table bytes that fit one workgroup
 
-template <int D, typename CentT, typename OutT, int TT>
-__global__ __launch_bounds__(DEC_LDS_THREADS) void k_decode_lds(const uint8_t *__restrict__ codes,
-                                                                const uint8_t *__restrict__ scales,
-                                                                const uint8_t *__restrict__ assign,
-                                                                const CentT *__restrict__ cent, int64_t cap,
-                                                                int chunk_tokens, int H, int K, int G,
-                                                                int64_t tok_begin, int64_t tok_end, int64_t c_first,
-                                                                OutT *__restrict__ out, int64_t out_hs) {
-    constexpr int SL = D / 16;                              // slices per token
-    constexpr int CHR = D * (int)sizeof(CentT) / 16;        // 16-byte chunks per table row
-    constexpr int CPH = CHR / 2 / SL;                       // chunks per half slice (1 bf16, 2 fp32)
+template <int D, typename CentT, typename OutT, int TT, int PARTS>
+__global__ __launch_bounds__(DEC_LDS_THREADS, PARTS == 2 ? 8 : 4) void k_decode_lds(const uint8_t *__restrict__ codes,
+                                                                   const uint8_t *__restrict__ scales,
+                                                                   const uint8_t *__restrict__ assign,
+                                                                   const CentT *__restrict__ cent, int64_t cap,
+                                                                   int chunk_tokens, int H, int K, int G,
+                                                                   int64_t tok_begin, int64_t tok_end,
+                                                                   int64_t c_first, OutT *__restrict__ out,
+                                                                   int64_t out_hs) {
+    constexpr int LPT = D / 8 / PARTS;                        // lanes per token (8 channels each)
+    constexpr int CHH = D / PARTS * (int)sizeof(CentT) / 16;  // 16-byte chunks per part of a row
+    constexpr int CP8 = 8 * (int)sizeof(CentT) / 16;          // chunks per 8 channels (1 bf16, 2 fp32)
     extern __shared__ uint4 tab[];
-    const int h = (int)(blockIdx.x % H);
-    const int64_t c = c_first + blockIdx.x / H;
+    const int hf = (int)(blockIdx.x % PARTS);
+    const int h = (int)((blockIdx.x / PARTS) % H);
+    const int64_t c = c_first + (blockIdx.x / PARTS) / H;
     const int tid = threadIdx.x;
     for (int t = 0; t < TT; ++t) {
         const uint4 *src = reinterpret_cast<const uint4 *>(cent + (((size_t)c * TT + t) * H + h) * K * D);
-        for (int i = tid; i < K * CHR; i += DEC_LDS_THREADS) {
-            const int row = i / CHR, q = i - row * CHR;
+        for (int i = tid; i < K * CHH; i += DEC_LDS_THREADS) {
+            const int row = i / CHH, q = i - row * CHH;
             const int r = t * K + row;
-            tab[r * CHR + (q ^ (r & (CHR - 1)))] = src[i];
+            tab[r * CHH + (q ^ (r & (CHH - 1)))] = src[(size_t)row * PARTS * CHH + hf * CHH + q];
         }
     }
     __syncthreads();
     const int64_t tb = max(tok_begin, c * chunk_tokens), te = min(tok_end, (c + 1) * chunk_tokens);
-    const int items = (int)(te - tb) * SL;
-    for (int i0 = tid; i0 < items; i0 += DEC_LDS_THREADS * DEC_LDS_U) {
-        uint32_t w0[DEC_LDS_U], w1[DEC_LDS_U], sc0[DEC_LDS_U], sc1[DEC_LDS_U];
+    constexpr int STEP = DEC_LDS_THREADS / LPT;
+    const int jj = tid % LPT;
+    const int c0 = hf * (D / PARTS) + 8 * jj;   // first channel of the lane
+    const int64_t n0 = tb + tid / LPT;
+    const size_t row0 = (size_t)h * cap + n0;
+    const uint16_t *cp = reinterpret_cast<const uint16_t *>(codes) + row0 * (D / 8) + c0 / 8;
+    const uint8_t *sp = scales + row0 * (D / G) + c0 / G;
+    const uint8_t *ap = assign + (size_t)h * cap + n0;
+    const size_t a_stage = (size_t)H * cap;
+    OutT *op = out + (size_t)h * out_hs + (size_t)(n0 - tok_begin) * D + c0;
+    const int ntok = (int)(te - n0);   // this thread's tokens: 0, STEP, 2 STEP, ... < ntok
+    for (int i0 = 0; i0 < ntok; i0 += STEP * DEC_LDS_U) {
+        uint32_t w[DEC_LDS_U], sc[DEC_LDS_U];
         int k[DEC_LDS_U][TT];
-        int64_t n[DEC_LDS_U];
-        int jj[DEC_LDS_U];
         bool ok[DEC_LDS_U];
 #pragma unroll
         for (int u = 0; u < DEC_LDS_U; ++u) {
-            const int it0 = i0 + u * DEC_LDS_THREADS;
-            ok[u] = it0 < items;
-            const int it = ok[u] ? it0 : i0;
-            n[u] = tb + it / SL;
-            jj[u] = it % SL;
-            slice_inputs<D>(codes, scales, (size_t)h * cap + n[u], G, jj[u], w0[u], w1[u], sc0[u], sc1[u]);
+            const int i = i0 + u * STEP;
+            ok[u] = i < ntok;
+            const int ii = ok[u] ? i : i0;
+            w[u] = cp[(size_t)ii * (D / 8)];
+            sc[u] = sp[(size_t)ii * (D / G)];
 #pragma unroll
             for (int t = 0; t < TT; ++t) {
-                const int kk = assign[((size_t)t * H + h) * cap + n[u]];
+                const int kk = ap[t * a_stage + ii];
                 k[u][t] = kk < K ? kk : K - 1;   // a corrupt byte cannot leave the chunk's table
             }
         }
 #pragma unroll
         for (int u = 0; u < DEC_LDS_U; ++u) {
             if (!ok[u]) continue;
-            OutT *rb = out + (size_t)h * out_hs + (size_t)(n[u] - tok_begin) * D;
-            decode_slice<D, CentT, OutT>(TT, w0[u], w1[u], sc0[u], sc1[u], jj[u], rb, [&](int t, int hf, uint4 *cv) {
-                const int r = t * K + k[u][t];
-                const int q0 = CPH * (hf * SL + jj[u]);
+            float y[8];
+            dequant8(w[u], e4m3_decode(sc[u]), y);
 #pragma unroll
-                for (int q = 0; q < CPH; ++q) cv[q] = tab[r * CHR + ((q0 + q) ^ (r & (CHR - 1)))];
-            });
+            for (int t = TT - 1; t >= 0; --t) {
+                const int r = t * K + k[u][t];
+                uint4 cv[CP8];
+#pragma unroll
+                for (int q = 0; q < CP8; ++q) cv[q] = tab[r * CHH + ((CP8 * jj + q) ^ (r & (CHH - 1)))];
+                add8<CentT>(cv, y);
+            }
+            store8_out<OutT>(op + (size_t)(i0 + u * STEP) * D, y);
         }
     }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
-    const size_t tab_bytes = (size_t)a.T * a.K * a.D * (a.cent_dtype == DT_BF16 ? 2 : 4);
+    const size_t tab_bytes = (size_t)a.T * a.K * (a.D / DEC_PARTS) * (a.cent_dtype == DT_BF16 ? 2 : 4);
     if (a.T >= 1 && a.T <= 4 && tab_bytes <= DEC_LDS_MAX) {
         const int64_t c0 = a.tok_begin / a.chunk_tokens, c1 = (a.tok_begin + a.ntok - 1) / a.chunk_tokens;
-        if ((c1 - c0 + 1) * a.H < (int64_t)UINT32_MAX) {
-            dim3 g((unsigned)((c1 - c0 + 1) * a.H)), b(DEC_LDS_THREADS);
+        if ((c1 - c0 + 1) * a.H * DEC_PARTS < (int64_t)UINT32_MAX) {
+            dim3 g((unsigned)((c1 - c0 + 1) * a.H * DEC_PARTS)), b(DEC_LDS_THREADS);
 #define QVG_DECL(DD, CT, OT, TT)                                                                                  \
     do {                                                                                                          \
-        (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, CT, OT, TT>,                                     \
+        (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, CT, OT, TT, DEC_PARTS>,                                     \
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)tab_bytes);                    \
-        hipLaunchKernelGGL((k_decode_lds<DD, CT, OT, TT>), g, b, tab_bytes, s, a.codes, a.scales, a.assign,        \
+        hipLaunchKernelGGL((k_decode_lds<DD, CT, OT, TT, DEC_PARTS>), g, b, tab_bytes, s, a.codes, a.scales, a.assign,        \
                            (const CT *)a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.G, a.tok_begin,                  \
                            a.tok_begin + a.ntok, c0, (OT *)a.out, a.out_hs);                                      \
     } while (0)

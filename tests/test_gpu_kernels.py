@@ -76,6 +76,30 @@ def test_dequant_reconstruct_bit_exact(H, N, d, K, T, G, dtype):
         np.testing.assert_array_equal(to_np(out), ref)
 
 
+def test_decode_every_scale_code():
+    """All 256 E4M3FN scale bytes (subnormal, normal, 448, NaN and negative
+    codes) with random 2-bit codes and one stage of random centroids."""
+    say("dequant_reconstruct over every scale code")
+    q = lib()
+    rng = np.random.default_rng(11)
+    H, N, d, G, K = 1, 256, 64, 16, 8
+    codes = rng.integers(0, 256, (H, N, d // 4), dtype=np.uint8)
+    scales = ((np.arange(N)[:, None] * (d // G) + np.arange(d // G)[None, :]) % 256).astype(np.uint8)[None]
+    asg = rng.integers(0, K, (1, H, N), dtype=np.uint8)
+    cent = oracle.bf16_round(rng.standard_normal((1, H, K, d))).astype(np.float32)
+    cfg = q.config(d, K, 1, G, 2, 2, 7, "bf16")
+    dev = lambda a, dt=torch.uint8: torch.from_numpy(np.ascontiguousarray(a)).to(dt).to(DEV)
+    for out_dtype in ("f32", "bf16"):
+        ref = oracle.decode_chunk(codes, scales, asg, cent, G, out_dtype)
+        out = torch.empty((H, N, d), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16, device=DEV)
+        q.qvg_dequant_reconstruct(cfg, H, N, dev(codes), dev(scales), dev(asg), to_dev(cent, "bf16"), out,
+                                  q.QVG_F32 if out_dtype == "f32" else q.QVG_BF16)
+        torch.cuda.synchronize()
+        got = to_np(out)
+        np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+        np.testing.assert_array_equal(got.view(np.uint32)[~np.isnan(got)], ref.view(np.uint32)[~np.isnan(ref)])
+
+
 def _assign_case(rng, which):
     p = synthkv.PRESETS[2]
     if which == "kv":
