@@ -52,6 +52,26 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def hbm_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the same counter reads
+    for a copy kernel of known size), or None when the kernels' source has
+    changed since the counters were taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "hbm_traffic.json")
+    src = os.path.join(root, "bit_vector_quantization_amd", "csrc", "qvg_kernels.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if rec.get("kernels_source_sha256") != sha or not k:
+        return None
+    return round(k["fetch_bytes"] * rec["copy_scale"]["fetch"] + k["write_bytes"] * rec["copy_scale"]["write"])
+
+
 def decode_bytes(H, ntok, d, G, T, K, chunks, out_bytes=2, cent_bytes=2):
     """Algorithmic HBM bytes of one fused decode: codes, scales, assignments and
     every touched chunk's centroid tables read once, the output written once."""
@@ -164,7 +184,7 @@ def main():
     copy_gbs = 2 * src.numel() * 2 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
 
     # per-kernel breakdown with the library's event profiler
-    kernels = {}
+    kernels, raw_stats = {}, {}
     if args.profile_steps > 0:
         log(f"profiling {args.profile_steps} steps with per-launch events")
         q.qvg_profile_enable(True)
@@ -175,6 +195,7 @@ def main():
         prof_ms_step = (time.perf_counter() - t1) * 1e3 / args.profile_steps
         q.qvg_profile_enable(False)
         raw = q.qvg_profile_read()
+        raw_stats.update(raw)
         for name, r in raw.items():
             kernels[name] = dict(launches_per_step=r["launches"] / args.profile_steps,
                                  avg_us=round(r["avg_ms"] * 1e3, 3),
@@ -184,30 +205,32 @@ def main():
     else:
         prof_ms_step = None
 
-    # roofline of the dominant kernel
-    if kernels:
-        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-    else:
-        dom = "decode"
-    if dom == "decode":
-        achieved = dec_b / (dec_avg_ms * 1e-3) / 1e9
-        roof = dict(kernel="decode", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
-                    avg_launch_us=round(dec_avg_ms * 1e3, 2), algorithmic_bytes_per_launch=int(dec_b),
-                    timed="HIP events around every decode launch of the timed steps")
-    else:
-        r = raw[dom]
-        if dom == "assign":
-            achieved = r["flops"] / (r["total_ms"] * 1e-3) / 1e12
-            roof = dict(kernel=dom, bound="mfma", achieved=round(achieved, 2), peak=MFMA_BF16_PEAK_TFLOPS,
-                        unit="TFLOP/s", frac=round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None)
+    # rooflines: assign against the bf16 matrix peak, update and decode against HBM
+    roofs = {}
+    dec_roof = dict(kernel="decode", bound="hbm", achieved=round(decode_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(decode_gbs / HBM_PEAK_GBS, 4), traffic=hbm_traffic("decode"),
+                    avg_launch_us=round(dec_avg_ms * 1e3, 2), algorithmic_per_launch=int(dec_b),
+                    timed="HIP events around every decode launch of the timed steps, on its stream")
+    roofs["decode"] = dec_roof
+    for name in ("assign", "update"):
+        if name not in raw_stats:
+            continue
+        r = raw_stats[name]
+        per = (r["flops"] if name == "assign" else r["bytes"]) / r["launches"]
+        secs = r["total_ms"] * 1e-3 / r["launches"]
+        if name == "assign":
+            ach = per / secs / 1e12
+            roofs[name] = dict(kernel=name, bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFLOPS,
+                               unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4))
         else:
-            achieved = r["bytes"] / (r["total_ms"] * 1e-3) / 1e9
-            roof = dict(kernel=dom, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None)
-        roof.update(avg_launch_us=round(r["avg_ms"] * 1e3, 2),
-                    algorithmic_per_launch=(r["flops"] if dom == "assign" else r["bytes"]) / r["launches"],
-                    timed="HIP events around every launch of the profiled steps (library event profiler)")
+            ach = per / secs / 1e9
+            roofs[name] = dict(kernel=name, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                               frac=round(ach / HBM_PEAK_GBS, 4))
+        roofs[name].update(traffic=hbm_traffic(name), avg_launch_us=round(secs * 1e6, 2),
+                           algorithmic_per_launch=per,
+                           timed="HIP events around every launch of the profiled steps, on the launch stream")
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"]) if kernels else "decode"
+    roof = roofs.get(dom, dec_roof)
 
     # long-horizon decode stress: 12 heads x 128, 700 frames (1,092,000 tokens)
     stress = None
@@ -229,6 +252,7 @@ def main():
                    "heads": HK, "tokens": Ntot, "d": d, "centroids": K, "stages": T, "group_size": G,
                    "chunk_tokens": p.chunk_tokens, "iters_cold": p.iters_cold, "iters_warm": p.iters_warm},
         "roofline": roof,
+        "rooflines": roofs,
         "cpu_baseline": cpu,
         "encode": {"ms_per_step": round(enc_ms / S, 4),
                    "vectors_per_s": round(vec_step / (enc_ms / S * 1e-3), 1),
