@@ -26,6 +26,13 @@ struct qvg_centroid_cache {
     int32_t valid;   // host-side: set when an encode through this cache is enqueued
 };
 
+namespace qvg {
+LaunchEvents &launch_events() {
+    thread_local LaunchEvents ev;
+    return ev;
+}
+}  // namespace qvg
+
 namespace {
 
 using namespace qvg;
@@ -58,8 +65,9 @@ qvg_status hip_status(hipError_t e) { return e == hipSuccess ? QVG_OK : QVG_ERR_
     } while (0)
 
 // ---- per-kernel timing with HIP events (qvg_profile_*) ----------------------
-// While enabled, every launch is bracketed by two events recorded on the stream
-// it runs on, with the launch's algorithmic FLOPs and HBM bytes.
+
+// While enabled, every kernel launch records two events at its own start and
+// end (see LaunchEvents), kept with the launch's algorithmic FLOPs and HBM bytes.
 struct ProfRecord {
     const char *name;
     hipEvent_t a, b;
@@ -81,11 +89,12 @@ hipEvent_t prof_event() {
     return e;
 }
 
+// The launcher call inside a scope hands the pair of events to its kernel
+// launch, which records them at the kernel's own start and end.
 struct ProfScope {
     ProfRecord rec{};
-    hipStream_t s;
     bool on = false;
-    ProfScope(const char *name, hipStream_t st, double flops, double bytes) : s(st) {
+    ProfScope(const char *name, double flops, double bytes) {
         std::lock_guard<std::mutex> lk(g_prof_mu);
         if (!g_prof_on) return;
         rec.name = name;
@@ -94,18 +103,27 @@ struct ProfScope {
         rec.flops = flops;
         rec.bytes = bytes;
         if (!rec.a || !rec.b) return;
-        on = hipEventRecord(rec.a, s) == hipSuccess;
+        launch_events() = LaunchEvents{rec.a, rec.b};
+        on = true;
     }
     ~ProfScope() {
         if (!on) return;
+        LaunchEvents &le = launch_events();
+        const bool launched = le.start == nullptr;   // the launch took the events
+        le = LaunchEvents{};
         std::lock_guard<std::mutex> lk(g_prof_mu);
-        if (hipEventRecord(rec.b, s) == hipSuccess) g_prof.push_back(rec);
+        if (launched) {
+            g_prof.push_back(rec);
+        } else {
+            g_prof_pool.push_back(rec.a);
+            g_prof_pool.push_back(rec.b);
+        }
     }
 };
 
 #define QVG_LAUNCH(name, flops, bytes, expr)                   \
     do {                                                       \
-        ProfScope prof_(name, s, (double)(flops), (double)(bytes)); \
+        ProfScope prof_(name, (double)(flops), (double)(bytes));    \
         QVG_TRY(expr);                                         \
     } while (0)
 

@@ -14,6 +14,7 @@
 // (bf16 x bf16 squares/products, 2 * x, (q - 1.5) * s), so FMA contraction
 // cannot change a result; divisions are IEEE (correctly rounded).
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -23,6 +24,19 @@
 #include "qvg_launch.h"
 
 namespace qvg {
+
+// Every kernel launch: with the profiler's events set, the launch records them
+// at the kernel's own start and end.
+#define QVG_KERNEL(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                                    \
+    do {                                                                                                      \
+        LaunchEvents &le_ = launch_events();                                                                  \
+        if (le_.start) {                                                                                      \
+            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, le_.start, le_.stop, 0, __VA_ARGS__);   \
+            le_.start = le_.stop = nullptr;                                                                   \
+        } else {                                                                                              \
+            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                              \
+        }                                                                                                     \
+    } while (0)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -237,7 +251,7 @@ __global__ __launch_bounds__(64) void k_forgy(int H, int N, int K, uint64_t seed
 }
 
 hipError_t launch_forgy(int T, int H, int N, int K, uint64_t seed, int32_t *idx, hipStream_t s) {
-    hipLaunchKernelGGL(k_forgy, dim3(H, T), dim3(64), 0, s, H, N, K, seed, idx);
+    QVG_KERNEL(k_forgy, dim3(H, T), dim3(64), 0, s, H, N, K, seed, idx);
     return hipGetLastError();
 }
 
@@ -295,7 +309,7 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
                                  int32_t *fill0, hipStream_t s) {
     const int Kp = padded_k(K);
     QVG_DISPATCH_DT(D, dtype,
-                    hipLaunchKernelGGL((k_init_centroids<DD, KVT>), dim3(Kp, H), dim3(64), 0, s, K, Kp, src, idx,
+                    QVG_KERNEL((k_init_centroids<DD, KVT>), dim3(Kp, H), dim3(64), 0, s, K, Kp, src, idx,
                                        warm, C, Cb, cnorm, cnt0, fill0));
     return hipGetLastError();
 }
@@ -651,7 +665,7 @@ hipError_t launch_assign(int D, int dtype, int H, int N, const Src &src, const u
     QVG_DISPATCH_DT(D, dtype, {
         (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
-        hipLaunchKernelGGL((k_assign<DD, KVT>), g, b, lds, s, src, H, N, Cb, cnorm, Kp, pi, pi_hs, counts);
+        QVG_KERNEL((k_assign<DD, KVT>), g, b, lds, s, src, H, N, Cb, cnorm, Kp, pi, pi_hs, counts);
     });
     return hipGetLastError();
 }
@@ -667,7 +681,7 @@ __global__ __launch_bounds__(256) void k_count(int N, int Kp, const uint8_t *pi,
 }
 
 hipError_t launch_count(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, int32_t *counts, hipStream_t s) {
-    hipLaunchKernelGGL(k_count, dim3((N + 255) / 256, H), dim3(256), 0, s, N, Kp, pi, pi_hs, counts);
+    QVG_KERNEL(k_count, dim3((N + 255) / 256, H), dim3(256), 0, s, N, Kp, pi, pi_hs, counts);
     return hipGetLastError();
 }
 
@@ -704,7 +718,7 @@ __global__ __launch_bounds__(256) void k_scatter(int N, int Kp, const uint8_t *p
 
 hipError_t launch_scatter(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, const int32_t *counts,
                           int32_t *fill, int32_t *offsets, int32_t *order, hipStream_t s) {
-    hipLaunchKernelGGL(k_scatter, dim3((N + 255) / 256, H), dim3(256), 0, s, N, Kp, pi, pi_hs, counts, fill,
+    QVG_KERNEL(k_scatter, dim3((N + 255) / 256, H), dim3(256), 0, s, N, Kp, pi, pi_hs, counts, fill,
                        offsets, order);
     return hipGetLastError();
 }
@@ -890,7 +904,7 @@ hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, 
                          int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s) {
     const int Kp = padded_k(K);
     QVG_DISPATCH_DT(D, dtype,
-                    hipLaunchKernelGGL((k_update<DD, KVT>), dim3((K + 3) / 4, H), dim3(256), 0, s, src, N, K, Kp,
+                    QVG_KERNEL((k_update<DD, KVT>), dim3((K + 3) / 4, H), dim3(256), 0, s, src, N, K, Kp,
                                        counts, offsets, order, C, Cb, cnorm, zero_cnt, zero_fill));
     return hipGetLastError();
 }
@@ -916,8 +930,8 @@ __global__ __launch_bounds__(64) void k_store_centroids(int K, const float *C, i
 hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype, void *dst, float *cache,
                                   hipStream_t s) {
     dim3 g(K, H), b(64);
-    if (D == 128) hipLaunchKernelGGL(k_store_centroids<128>, g, b, 0, s, K, C, dtype, dst, cache);
-    else hipLaunchKernelGGL(k_store_centroids<64>, g, b, 0, s, K, C, dtype, dst, cache);
+    if (D == 128) QVG_KERNEL(k_store_centroids<128>, g, b, 0, s, K, C, dtype, dst, cache);
+    else QVG_KERNEL(k_store_centroids<64>, g, b, 0, s, K, C, dtype, dst, cache);
     return hipGetLastError();
 }
 
@@ -977,10 +991,10 @@ hipError_t launch_quant(int D, int dtype, int H, int N, const Src &src, const vo
     dim3 g((N + TPB - 1) / TPB, H), b(256);
     QVG_DISPATCH_DT(D, dtype, {
         if (cent)
-            hipLaunchKernelGGL((k_quant<DD, KVT, true>), g, b, 0, s, src, N, (const KVT *)cent, cent_rows, pi, pi_hs,
+            QVG_KERNEL((k_quant<DD, KVT, true>), g, b, 0, s, src, N, (const KVT *)cent, cent_rows, pi, pi_hs,
                                codes, scales, q_cap, G);
         else
-            hipLaunchKernelGGL((k_quant<DD, KVT, false>), g, b, 0, s, src, N, (const KVT *)nullptr, 0, pi, pi_hs,
+            QVG_KERNEL((k_quant<DD, KVT, false>), g, b, 0, s, src, N, (const KVT *)nullptr, 0, pi, pi_hs,
                                codes, scales, q_cap, G);
     });
     return hipGetLastError();
@@ -1241,7 +1255,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     do {                                                                                                          \
         (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, CT, OT, TT, DEC_PARTS>,                                     \
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)tab_bytes);                    \
-        hipLaunchKernelGGL((k_decode_lds<DD, CT, OT, TT, DEC_PARTS>), g, b, tab_bytes, s, a.codes, a.scales, a.assign,        \
+        QVG_KERNEL((k_decode_lds<DD, CT, OT, TT, DEC_PARTS>), g, b, tab_bytes, s, a.codes, a.scales, a.assign,        \
                            (const CT *)a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.G, a.tok_begin,                  \
                            a.tok_begin + a.ntok, c0, (OT *)a.out, a.out_hs);                                      \
     } while (0)
@@ -1276,7 +1290,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const uint32_t bph = (uint32_t)((a.ntok + TPB - 1) / TPB);
     dim3 g(bph * a.H), b(256);
 #define QVG_DEC(DD, CT, OT, TT)                                                                                   \
-    hipLaunchKernelGGL((k_decode<DD, CT, OT, TT>), g, b, 0, s, a.codes, a.scales, a.assign, (const CT *)a.cent,    \
+    QVG_KERNEL((k_decode<DD, CT, OT, TT>), g, b, 0, s, a.codes, a.scales, a.assign, (const CT *)a.cent,    \
                        a.cap, a.chunk_tokens, a.H, a.K, a.T, a.G, a.tok_begin, a.ntok, (OT *)a.out, a.out_hs, bph)
 #define QVG_DEC_T(DD, CT, OT)                              \
     do {                                                   \
@@ -1317,7 +1331,7 @@ __global__ __launch_bounds__(256) void k_zero(int32_t *p, int64_t n) {
 }
 
 hipError_t launch_zero(int32_t *p, int64_t n, hipStream_t s) {
-    hipLaunchKernelGGL(k_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
+    QVG_KERNEL(k_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
     return hipGetLastError();
 }
 

@@ -91,6 +91,14 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 
+// Events the next kernel launch records at its own start and end
+// (hipExtLaunchKernelGGL); the library's profiler sets them around one launcher
+// call, and the launch clears them.  Thread-local; null when profiling is off.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents &launch_events();
+
 // Fills n int32 with zero.
 hipError_t launch_zero(int32_t *p, int64_t n, hipStream_t s);
 

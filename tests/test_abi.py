@@ -31,7 +31,8 @@ def q():
 def test_every_declared_function_is_exported(q):
     names = _declared()
     assert len(names) >= 20
-    lib = ctypes.CDLL(q._lib.LIB_PATH)
+    # RTLD_NOW: every symbol the library needs must resolve at load time
+    lib = ctypes.CDLL(q._lib.LIB_PATH, mode=os.RTLD_NOW)
     for n in names:
         assert hasattr(lib, n), n
     # and the binding wraps every one of them under the same name
