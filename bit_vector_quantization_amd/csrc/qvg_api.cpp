@@ -131,7 +131,7 @@ struct ProfScope {
 // residuals R(t) are never stored: each kernel rebuilds them from the input
 // and the earlier stages' stored centroids and assignments.
 struct EncodeWorkspace {
-    size_t C = 0, Cb = 0, cn = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, total = 0;
+    size_t C = 0, Cb = 0, cn = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, vstats = 0, total = 0;
 
     EncodeWorkspace(const qvg_config &c, int H, int N) {
         const size_t D = c.d, K = c.n_centroids, Kp = padded_k(c.n_centroids);
@@ -147,13 +147,14 @@ struct EncodeWorkspace {
         offsets = take((size_t)H * Kp * 4);
         order = take((size_t)H * N * 4);
         idx = take((size_t)T * H * K * 4);
+        vstats = take(value_stats_words(H) * 4);
         total = off;
     }
 };
 
 // Workspace of the stage-level k-means entry points.
 struct StageWorkspace {
-    size_t C = 0, Cb = 0, cn = 0, cnt = 0, fill = 0, offsets = 0, order = 0, total = 0;
+    size_t C = 0, Cb = 0, cn = 0, cnt = 0, fill = 0, offsets = 0, order = 0, vstats = 0, total = 0;
     StageWorkspace(int H, int N, int D, int K) {
         const size_t Kp = padded_k(K);
         size_t off = 0;
@@ -165,6 +166,7 @@ struct StageWorkspace {
         fill = take((size_t)H * Kp * 4);
         offsets = take((size_t)H * Kp * 4);
         order = take((size_t)H * N * 4);
+        vstats = take(value_stats_words(H) * 4);
         total = off;
     }
 };
@@ -352,9 +354,14 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
     int32_t *offsets = at<int32_t>(workspace, ws.offsets);
     int32_t *order = at<int32_t>(workspace, ws.order);
     int32_t *idx = at<int32_t>(workspace, ws.idx);
+    uint32_t *vstats = at<uint32_t>(workspace, ws.vstats);
     const bool warm_cache = cache && cache->valid;
     const bool need_draw = !init_centroids && !warm_cache;
     if (need_draw) QVG_LAUNCH("forgy", 0, (double)T * H * K * 4, launch_forgy(T, H, N, K, cfg->seed, idx, s));
+
+    if (update_seg_fits(N))
+        QVG_LAUNCH("value_stats", 0, HND * esz, launch_value_stats(cfg->dtype, H, x, x_head_stride, (int64_t)N * D,
+                                                                   vstats, s));
 
     // R(t-1) is rebuilt from x and the stored centroids / assignments of stages 1..t-1
     Src src = src0;
@@ -376,11 +383,17 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
             const int c = it & 1;
             QVG_LAUNCH("assign", assign_flops, row_bytes + H * N + table,
                        launch_assign(D, cfg->dtype, H, N, src, Cb, cn, Kp, pi, cap, cnt[c], s));
-            QVG_LAUNCH("scatter", 0, H * N * 5.0 + H * Kp * 8.0,
-                       launch_scatter(H, N, Kp, pi, cap, cnt[c], fill[c], offsets, order, s));
-            QVG_LAUNCH("update", HND, row_bytes + H * N * 4.0 + (double)H * K * D * 4 + table,
-                       launch_update(D, cfg->dtype, H, N, K, src, cnt[c], offsets, order, C, Cb, cn, cnt[c ^ 1],
-                                     fill[c ^ 1], s));
+            if (update_seg_fits(N)) {
+                QVG_LAUNCH("update", HND, row_bytes + H * N + (double)H * K * D * 4 + table,
+                           launch_update_seg(D, cfg->dtype, H, N, K, src, pi, cap, cnt[c], vstats, C, Cb, cn,
+                                             cnt[c ^ 1], fill[c ^ 1], s));
+            } else {
+                QVG_LAUNCH("scatter", 0, H * N * 5.0 + H * Kp * 8.0,
+                           launch_scatter(H, N, Kp, pi, cap, cnt[c], fill[c], offsets, order, s));
+                QVG_LAUNCH("update", HND, row_bytes + H * N * 4.0 + (double)H * K * D * 4 + table,
+                           launch_update(D, cfg->dtype, H, N, K, src, cnt[c], offsets, order, C, Cb, cn, cnt[c ^ 1],
+                                         fill[c ^ 1], s));
+            }
         }
         QVG_LAUNCH("assign", assign_flops, row_bytes + H * N + table,
                    launch_assign(D, cfg->dtype, H, N, src, Cb, cn, Kp, pi, cap, nullptr, s));
@@ -499,17 +512,26 @@ qvg_status qvg_centroid_update(const void *x, int32_t x_dtype, int64_t x_head_st
     int32_t *order = at<int32_t>(workspace, ws.order);
     const double HND = (double)heads * n_tokens * d;
     QVG_LAUNCH("zero", 0, heads * Kp * 8.0, launch_zero(cnt, (int64_t)heads * Kp, s));
-    QVG_LAUNCH("zero", 0, heads * Kp * 8.0, launch_zero(fill, (int64_t)heads * Kp, s));
     QVG_LAUNCH("count", 0, (double)heads * n_tokens + heads * Kp * 4.0,
                launch_count(heads, n_tokens, Kp, assign, assign_head_stride, cnt, s));
-    QVG_LAUNCH("scatter", 0, heads * n_tokens * 5.0 + heads * Kp * 8.0,
-               launch_scatter(heads, n_tokens, Kp, assign, assign_head_stride, cnt, fill, offsets, order, s));
-    QVG_LAUNCH("update", HND,
-               HND * dtype_size(x_dtype) + heads * n_tokens * 4.0 + (double)heads * n_centroids * d * 4 +
-                   (double)heads * Kp * (d * 2 + 8),
-               launch_update(d, x_dtype, heads, n_tokens, n_centroids, plain_src(x, x_head_stride), cnt, offsets,
-                             order, centroids, at<uint16_t>(workspace, ws.Cb), at<double>(workspace, ws.cn), nullptr,
-                             nullptr, s));
+    const double tables = (double)heads * n_centroids * d * 4 + (double)heads * Kp * (d * 2 + 8);
+    if (update_seg_fits(n_tokens)) {
+        uint32_t *vstats = at<uint32_t>(workspace, ws.vstats);
+        QVG_LAUNCH("value_stats", 0, HND * dtype_size(x_dtype),
+                   launch_value_stats(x_dtype, heads, x, x_head_stride, (int64_t)n_tokens * d, vstats, s));
+        QVG_LAUNCH("update", HND, HND * dtype_size(x_dtype) + (double)heads * n_tokens + tables,
+                   launch_update_seg(d, x_dtype, heads, n_tokens, n_centroids, plain_src(x, x_head_stride), assign,
+                                     assign_head_stride, cnt, vstats, centroids, at<uint16_t>(workspace, ws.Cb),
+                                     at<double>(workspace, ws.cn), nullptr, nullptr, s));
+    } else {
+        QVG_LAUNCH("zero", 0, heads * Kp * 8.0, launch_zero(fill, (int64_t)heads * Kp, s));
+        QVG_LAUNCH("scatter", 0, heads * n_tokens * 5.0 + heads * Kp * 8.0,
+                   launch_scatter(heads, n_tokens, Kp, assign, assign_head_stride, cnt, fill, offsets, order, s));
+        QVG_LAUNCH("update", HND, HND * dtype_size(x_dtype) + heads * n_tokens * 4.0 + tables,
+                   launch_update(d, x_dtype, heads, n_tokens, n_centroids, plain_src(x, x_head_stride), cnt, offsets,
+                                 order, centroids, at<uint16_t>(workspace, ws.Cb), at<double>(workspace, ws.cn),
+                                 nullptr, nullptr, s));
+    }
     if (counts_out)
         QVG_TRY(hipMemcpy2DAsync(counts_out, (size_t)n_centroids * 4, cnt, (size_t)Kp * 4, (size_t)n_centroids * 4,
                                  heads, hipMemcpyDeviceToDevice, s));

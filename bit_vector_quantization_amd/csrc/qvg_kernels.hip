@@ -749,35 +749,32 @@ __device__ __forceinline__ void two_sum(double &s, double &e, double x) {
     s = t;
 }
 
-// Rows n[u] (where valid[u]) of R(P), channels [c0, c0 + 8), for U rows at
-// once: every load of a stage is issued for all rows before any is used.
+// Rows n[u] of R(P), channels [c0, c0 + 8), for U rows at once (every n[u] a
+// valid row; slots with !valid[u] come out zero).  Every load of a stage is
+// issued for all rows, unconditionally, before any is used.
 template <int D, typename KVT, int U>
 __device__ __forceinline__ void src_rows8(const Src &s, int h, const int (&n)[U], const bool (&valid)[U], int c0,
                                           float (&v)[U][8]) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        if (valid[u]) load8<KVT>(static_cast<const KVT *>(s.x) + (size_t)h * s.x_hs + (size_t)n[u] * D + c0, v[u]);
-        else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
-        }
-    }
+    for (int u = 0; u < U; ++u) load8<KVT>(static_cast<const KVT *>(s.x) + (size_t)h * s.x_hs + (size_t)n[u] * D + c0, v[u]);
 #pragma unroll 1
     for (int p = 0; p < s.P; ++p) {
         int k[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) k[u] = valid[u] ? s.pi[p][(size_t)h * s.pi_hs + n[u]] : 0;
+        for (int u = 0; u < U; ++u) k[u] = s.pi[p][(size_t)h * s.pi_hs + n[u]];
         const KVT *cp = static_cast<const KVT *>(s.cent[p]) + (size_t)h * s.K * D + c0;
+        float c[U][8];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (valid[u]) {
-                float c[8];
-                load8<KVT>(cp + (size_t)k[u] * D, c);
+        for (int u = 0; u < U; ++u) load8<KVT>(cp + (size_t)k[u] * D, c[u]);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v[u][i] = v[u][i] - c[i];
-            }
-        }
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[u][i] = v[u][i] - c[u][i];
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[u][i] = valid[u] ? v[u][i] : 0.f;
 }
 
 // Visits the cnt rows of R(P) listed in ord, 8 channels from c0 per lane, as
@@ -789,7 +786,7 @@ __device__ __forceinline__ void for_rows(const Src &src, int h, const int32_t *o
     const int lane = threadIdx.x & 63;
     for (int i0 = 0; i0 < cnt; i0 += 64) {
         const int m = cnt - i0 < 64 ? cnt - i0 : 64;
-        const int mine = lane < m ? ord[i0 + lane] : 0;
+        const int mine = ord[i0 + (lane < m ? lane : m - 1)];
         for (int j0 = 0; j0 < m; j0 += RPI * UNROLL) {
             float v[UNROLL][8];
             int n[UNROLL];
@@ -906,6 +903,527 @@ hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, 
     QVG_DISPATCH_DT(D, dtype,
                     QVG_KERNEL((k_update<DD, KVT>), dim3((K + 3) / 4, H), dim3(256), 0, s, src, N, K, Kp,
                                        counts, offsets, order, C, Cb, cnorm, zero_cnt, zero_fill));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// update, segmented: exact means from a per-workgroup token list in LDS
+// ---------------------------------------------------------------------------
+//
+// One workgroup per (head, run of SEG_KR centroids); the runs of a head are
+// neighbours in xcd_tile order, so they share one XCD's L2 (the head's
+// assignments and centroid tables).
+//  1. The run's histogram (from the assign) gives each centroid its place in a
+//     token list in LDS; one pass over the head's assignments puts every token
+//     of the run there, with its labels of the first two earlier stages packed
+//     beside it.  No global sort.
+//  2. The waves split the run's list evenly.  A wave reads one row per load
+//     instruction (64 lanes x D/64 channels, row addresses in scalar
+//     registers), rebuilds R(t-1), and sums in fp64 registers while the rows
+//     belong to one centroid; when the centroid changes, the partial sums go
+//     into that centroid's LDS accumulator.
+//  3. Exactness.  If every value of a channel is a multiple of 2^e and every
+//     partial sum stays below 2^(53+e) in magnitude, each partial sum is an
+//     fp64 number, so each addition (in registers or LDS atomics, in any
+//     order) is exact and the accumulator holds the exact sum; fp32(sum / n)
+//     is then the exactly rounded mean.
+//     Run certificate (no per-value work): fp32(a - b) of two multiples of
+//     2^e is again one (when it rounds, its ulp exceeds 2^e) and is at most
+//     (|a| + |b|)(1 + 2^-24) in magnitude.  So every value of R(t-1) of a head
+//     is a multiple of the smallest ulp among the head's input values and
+//     stored centroid tables, and at most the sum of their largest magnitudes
+//     (times 1 + 2^-20).  k_value_stats provides the input's part; each
+//     workgroup scans the tables.  When (largest count of the run) x (that
+//     magnitude) < 2^(53+e), every centroid of the run is certified.
+//     Otherwise each centroid collects max|v| and the lowest set bit of its
+//     values during the sums and is certified on its own; a centroid without
+//     a certificate is summed again by one wave with the interval test and the
+//     two-sum pass of k_update.
+
+constexpr int SEG_KR = 32;          // centroids per workgroup
+constexpr int SEG_WAVES = 8;
+constexpr int SEG_U = 8;            // rows in flight per wave
+constexpr int SEG_EMPTY_E = 4096;   // lowest-bit exponent of a centroid with only zeros so far
+constexpr int VSTAT_BLOCKS = 8;     // partial statistics per head from k_value_stats
+
+// Smallest nonzero and largest magnitude bits (bf16: 15 bits, fp32: 31 bits) of
+// each head's count values, as VSTAT_BLOCKS partial pairs per head:
+// stats[h][b] = {smallest nonzero magnitude - 1 (0xFFFFFFFF: all zero), largest}.
+template <typename KVT>
+__global__ __launch_bounds__(256) void k_value_stats(const KVT *x, int64_t x_hs, int64_t count, uint32_t *stats) {
+    constexpr int PER = 16 / sizeof(KVT);
+    constexpr int STRIDE = 256 * VSTAT_BLOCKS;
+    const int h = blockIdx.y;
+    const uint4 *p = reinterpret_cast<const uint4 *>(x + (size_t)h * x_hs);
+    const int64_t nv = count / PER;   // count is a multiple of PER
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    // four loads in flight; indices past the end read the last chunk again,
+    // which leaves a minimum and a maximum unchanged
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nv; i += 4 * STRIDE) {
+        uint4 q[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[k] = p[std::min<int64_t>(i + k * STRIDE, nv - 1)];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t w[4] = {q[k].x, q[k].y, q[k].z, q[k].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (sizeof(KVT) == 2) {
+                    const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+                    mx = max(mx, max(lo, hi));
+                    mn = min(mn, min(lo - 1u, hi - 1u));   // zero wraps to the largest value
+                } else {
+                    const uint32_t a = w[j] & 0x7FFFFFFFu;
+                    mx = max(mx, a);
+                    mn = min(mn, a - 1u);
+                }
+            }
+        }
+    }
+    __shared__ uint32_t red[2][4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        red[0][threadIdx.x >> 6] = mn;
+        red[1][threadIdx.x >> 6] = mx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t *o = stats + ((size_t)h * VSTAT_BLOCKS + blockIdx.x) * 2;
+        o[0] = min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3]));
+        o[1] = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
+    }
+}
+
+hipError_t launch_value_stats(int dtype, int H, const void *x, int64_t x_hs, int64_t count, uint32_t *stats,
+                              hipStream_t s) {
+    const int esz = dtype == DT_BF16 ? 2 : 4;
+    if ((count * esz) % 16 != 0 || (x_hs * esz) % 16 != 0) return hipErrorInvalidValue;
+    if (dtype == DT_BF16)
+        QVG_KERNEL(k_value_stats<uint16_t>, dim3(VSTAT_BLOCKS, H), dim3(256), 0, s,
+                   static_cast<const uint16_t *>(x), x_hs, count, stats);
+    else
+        QVG_KERNEL(k_value_stats<float>, dim3(VSTAT_BLOCKS, H), dim3(256), 0, s, static_cast<const float *>(x),
+                   x_hs, count, stats);
+    return hipGetLastError();
+}
+
+// Exponent of the smallest ulp of the values whose smallest nonzero magnitude
+// has bits mbits (bf16: 2^(E-134) at exponent field E, subnormals below that;
+// fp32: 2^(E-150)).
+template <typename KVT>
+__device__ __forceinline__ int ulp_exp_of(uint32_t mbits) {
+    if constexpr (sizeof(KVT) == 2) return (int)(mbits >> 7) - 134;
+    else return (int)(mbits >> 23) - 150;
+}
+
+template <typename KVT>
+__device__ __forceinline__ float magnitude_of(uint32_t mbits) {
+    if constexpr (sizeof(KVT) == 2) return __uint_as_float(mbits << 16);
+    else return __uint_as_float(mbits);
+}
+
+// D/64 consecutive channels of a row, as fp32.
+template <typename KVT, int CPL>
+__device__ __forceinline__ void load_part(const KVT *p, float (&v)[CPL]) {
+    if constexpr (sizeof(KVT) == 2) {
+        if constexpr (CPL == 2) {
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(p);
+            v[0] = __uint_as_float(w << 16);
+            v[1] = __uint_as_float(w & 0xFFFF0000u);
+        } else {
+            v[0] = __uint_as_float((uint32_t)*reinterpret_cast<const uint16_t *>(p) << 16);
+        }
+    } else {
+        if constexpr (CPL == 2) {
+            const float2 f = *reinterpret_cast<const float2 *>(p);
+            v[0] = f.x;
+            v[1] = f.y;
+        } else {
+            v[0] = *reinterpret_cast<const float *>(p);
+        }
+    }
+}
+
+// Exponent of the lowest set bit of a nonzero fp32 value (a lower bound for
+// subnormals), SEG_EMPTY_E for zeros.
+__device__ __forceinline__ int lowest_bit_exp(float v) {
+    const uint32_t b = __float_as_uint(v) & 0x7FFFFFFFu;
+    const int e = (int)(b >> 23) + (int)__builtin_ctz(b | 0x800000u) - 150;
+    return b ? e : SEG_EMPTY_E;
+}
+
+// Rows list[j .. j + m) (1 <= m <= U) of R(P), this lane's channels; slots
+// u >= m read row list[j] again and come out zero.  A list entry is
+// token | label(stage 1) << 16 | label(stage 2) << 24; entries are the same
+// in every lane, so row addresses are formed in scalar registers.  Every load
+// is issued unconditionally (a load under a branch is waited for inside it).
+template <int D, typename KVT, int U>
+__device__ __forceinline__ void seg_rows(const Src &s, int h, int N, const uint32_t *list, int j, int m,
+                                         float (&v)[U][D / 64]) {
+    constexpr int CPL = D / 64;
+    const int c0 = (threadIdx.x & 63) * CPL;
+    uint32_t e[U];
+    int n[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        e[u] = __builtin_amdgcn_readfirstlane(list[j + (u < m ? u : 0)]);
+        // a token index is below N by construction; the clamp keeps every row read in bounds
+        n[u] = min((int)(e[u] & 0xFFFFu), N - 1);
+    }
+    const KVT *x = static_cast<const KVT *>(s.x) + (size_t)h * s.x_hs + c0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_part<KVT, CPL>(x + (size_t)n[u] * D, v[u]);
+#pragma unroll 1
+    for (int p = 0; p < s.P; ++p) {
+        const KVT *cp = static_cast<const KVT *>(s.cent[p]) + (size_t)h * s.K * D + c0;
+        int k[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            k[u] = p < 2 ? (int)((e[u] >> (16 + 8 * p)) & 0xFFu)
+                         : __builtin_amdgcn_readfirstlane((int)s.pi[p][(size_t)h * s.pi_hs + n[u]]);
+        float c[U][CPL];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_part<KVT, CPL>(cp + (size_t)k[u] * D, c[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) v[u][i] = v[u][i] - c[u][i];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) v[u][i] = u < m ? v[u][i] : 0.f;
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+    return v;
+}
+
+template <int D>
+constexpr size_t seg_lds_bytes(int N) {
+    return (size_t)SEG_KR * D * 8 + (size_t)(5 * SEG_KR + 1 + 4) * 4 + (size_t)N * 4;
+}
+
+// Phase 2 of k_update_seg for one wave: list entries [beg, end).  CERT: also
+// collect each centroid's max|v| and lowest set bit.
+template <int D, typename KVT, bool CERT>
+__device__ __forceinline__ void seg_sums(const Src &src, int h, int N, const uint32_t *list, const int32_t *s_off,
+                                         double *acc, int32_t *s_emin, uint32_t *s_amax, int beg, int end) {
+    constexpr int CPL = D / 64;
+    const int lane = threadIdx.x & 63;
+    int ci = 0;   // the offsets are monotone, so the guards below never bind
+    while (ci < SEG_KR - 1 && s_off[ci + 1] <= beg) ++ci;
+    ci = __builtin_amdgcn_readfirstlane(ci);
+    int bound = __builtin_amdgcn_readfirstlane(s_off[ci + 1]);
+    double sum[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) sum[c] = 0.0;
+    int emin = SEG_EMPTY_E;
+    uint32_t amax = 0u;
+    auto flush = [&]() {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            atomicAdd(&acc[ci * D + lane * CPL + c], sum[c]);
+            sum[c] = 0.0;
+        }
+        if constexpr (CERT) {
+            const int e = wave_min_i(emin);
+            const uint32_t a = wave_max_u(amax);
+            if (lane == 0) {
+                atomicMin(&s_emin[ci], e);
+                atomicMax(&s_amax[ci], a);
+            }
+            emin = SEG_EMPTY_E;
+            amax = 0u;
+        }
+    };
+    for (int j = beg; j < end; j += SEG_U) {
+        const int m = min(SEG_U, end - j);
+        float v[SEG_U][CPL];
+        seg_rows<D, KVT, SEG_U>(src, h, N, list, j, m, v);
+#pragma unroll
+        for (int u = 0; u < SEG_U; ++u) {
+            if (u < m) {
+                if (j + u >= bound) {
+                    flush();
+                    do {
+                        ++ci;
+                        bound = __builtin_amdgcn_readfirstlane(s_off[ci + 1]);
+                    } while (j + u >= bound && ci < SEG_KR - 1);
+                }
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    sum[c] += (double)v[u][c];
+                    if constexpr (CERT) {
+                        emin = min(emin, lowest_bit_exp(v[u][c]));
+                        amax = max(amax, __float_as_uint(v[u][c]) & 0x7FFFFFFFu);
+                    }
+                }
+            }
+        }
+    }
+    flush();
+}
+
+template <int D, typename KVT>
+__global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, int N, int K, int Kp,
+                                                               const uint8_t *__restrict__ pi, int64_t pi_hs,
+                                                               const int32_t *__restrict__ counts,
+                                                               const uint32_t *__restrict__ xstats, float *C,
+                                                               uint16_t *Cb, double *cnorm, int32_t *zero_cnt,
+                                                               int32_t *zero_fill) {
+    constexpr int CPL = D / 64;
+    constexpr int NT = 64 * SEG_WAVES;
+    extern __shared__ double seg_lds[];
+    double *acc = seg_lds;                                              // [SEG_KR][D]
+    int32_t *s_cnt = reinterpret_cast<int32_t *>(acc + SEG_KR * D);   // [SEG_KR]
+    int32_t *s_fill = s_cnt + SEG_KR;                                   // [SEG_KR]
+    int32_t *s_emin = s_fill + SEG_KR;                                  // [SEG_KR]
+    uint32_t *s_amax = reinterpret_cast<uint32_t *>(s_emin + SEG_KR);  // [SEG_KR] bits of max|v|
+    int32_t *s_off = reinterpret_cast<int32_t *>(s_amax + SEG_KR);     // [SEG_KR + 1]
+    uint32_t *s_misc = reinterpret_cast<uint32_t *>(s_off + SEG_KR + 1);  // table min, table max, max count, run certified
+    uint32_t *list = s_misc + 4;                                        // [N]
+
+    const int groups = (K + SEG_KR - 1) / SEG_KR;
+    const uint32_t r = xcd_tile(blockIdx.x, gridDim.x);
+    const int h = (int)(r / groups), k0 = (int)(r % groups) * SEG_KR;
+    if (h >= H) return;
+    const int nk = min(SEG_KR, K - k0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int i = tid; i < SEG_KR * D; i += NT) acc[i] = 0.0;
+    if (tid < SEG_KR) {
+        const bool in = tid < nk;
+        s_cnt[tid] = in ? counts[(size_t)h * Kp + k0 + tid] : 0;
+        s_fill[tid] = 0;
+        s_emin[tid] = SEG_EMPTY_E;
+        s_amax[tid] = 0u;
+        if (in && zero_cnt) zero_cnt[(size_t)h * Kp + k0 + tid] = 0;
+        if (in && zero_fill) zero_fill[(size_t)h * Kp + k0 + tid] = 0;
+    }
+    if (tid == 0) {
+        s_misc[0] = 0xFFFFFFFFu;
+        s_misc[1] = 0u;
+    }
+    __syncthreads();
+    if (wave == 0) {   // exclusive prefix of the run's counts, and their maximum
+        const int c = lane < SEG_KR ? s_cnt[lane] : 0;
+        int x = c;
+#pragma unroll
+        for (int o = 1; o < SEG_KR; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (lane < SEG_KR) s_off[lane] = x - c;
+        if (lane == SEG_KR - 1) s_off[SEG_KR] = x;
+        const uint32_t cm = wave_max_u((uint32_t)c);
+        if (lane == 0) s_misc[2] = cm;
+    }
+    if (xstats) {   // magnitudes of the earlier stages' stored tables of this head
+        constexpr int PER = 16 / sizeof(KVT);
+        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+        const int nv = K * D / PER;
+#pragma unroll 1
+        for (int p = 0; p < src.P; ++p) {
+            const uint4 *tp = reinterpret_cast<const uint4 *>(static_cast<const KVT *>(src.cent[p]) + (size_t)h * K * D);
+            for (int i = tid; i < nv; i += NT) {
+                const uint4 q = tp[i];
+                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    if constexpr (sizeof(KVT) == 2) {
+                        const uint32_t lo = w[jj] & 0x7FFFu, hi = (w[jj] >> 16) & 0x7FFFu;
+                        mx = max(mx, max(lo, hi));
+                        mn = min(mn, min(lo - 1u, hi - 1u));
+                    } else {
+                        const uint32_t a = w[jj] & 0x7FFFFFFFu;
+                        mx = max(mx, a);
+                        mn = min(mn, a - 1u);
+                    }
+                }
+            }
+        }
+        mn = (uint32_t)wave_min_i((int)(mn ^ 0x80000000u)) ^ 0x80000000u;   // unsigned minimum
+        mx = wave_max_u(mx);
+        if (lane == 0 && src.P > 0) {
+            atomicMin(&s_misc[0], mn);
+            atomicMax(&s_misc[1], mx);
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {   // the run certificate
+        bool ok = xstats != nullptr;
+        if (ok) {
+            uint32_t mn = s_misc[0], mx = s_misc[1];
+            double mag = (double)magnitude_of<KVT>(mx);   // the tables' largest magnitudes, summed over stages
+            if (src.P > 1) mag *= (double)src.P;          // (a bound: each table's maximum is at most mx)
+            uint32_t xmn = 0xFFFFFFFFu, xmx = 0u;
+            for (int b = 0; b < VSTAT_BLOCKS; ++b) {
+                xmn = min(xmn, xstats[((size_t)h * VSTAT_BLOCKS + b) * 2]);
+                xmx = max(xmx, xstats[((size_t)h * VSTAT_BLOCKS + b) * 2 + 1]);
+            }
+            mag += (double)magnitude_of<KVT>(xmx);
+            mn = min(mn, xmn);
+            const int e = mn == 0xFFFFFFFFu ? 1000 : ulp_exp_of<KVT>(mn + 1u);
+            const double reach = (double)s_misc[2] * mag * (1.0 + 0x1p-20);
+            ok = reach < ldexp(1.0, min(53 + e, 1023));
+        }
+        s_misc[3] = ok ? 1u : 0u;
+    }
+
+    // 1. the run's tokens, grouped by centroid
+    {
+        // labels of the earlier stages ride along in the list entries; missing
+        // stages read the current labels again and drop them
+        const uint8_t *lab = pi + (size_t)h * pi_hs;
+        const uint8_t *l1 = src.P >= 1 ? src.pi[0] + (size_t)h * src.pi_hs : lab;
+        const uint8_t *l2 = src.P >= 2 ? src.pi[1] + (size_t)h * src.pi_hs : lab;
+        const uint32_t m1 = src.P >= 1 ? 0xFFu : 0u, m2 = src.P >= 2 ? 0xFFu : 0u;
+        constexpr int B = 8;
+        for (int n0 = 0; n0 < N; n0 += NT * B) {
+            uint32_t k[B], a[B], b[B];
+#pragma unroll
+            for (int i = 0; i < B; ++i) {   // unconditional loads, all in flight together
+                const int n = min(n0 + i * NT + tid, N - 1);
+                k[i] = lab[n];
+                a[i] = l1[n];
+                b[i] = l2[n];
+            }
+#pragma unroll
+            for (int i = 0; i < B; ++i) {
+                k[i] = n0 + i * NT + tid < N ? k[i] - (uint32_t)k0 : 0xFFFFFFFFu;
+                a[i] &= m1;
+                b[i] &= m2;
+            }
+#pragma unroll
+            for (int i = 0; i < B; ++i) {
+                if (k[i] < (uint32_t)nk) {
+                    const int pos = atomicAdd(&s_fill[k[i]], 1);
+                    if (pos < s_cnt[k[i]])   // always, with counts taken from these labels
+                        list[s_off[k[i]] + pos] = (uint32_t)(n0 + i * NT + tid) | (a[i] << 16) | (b[i] << 24);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // 2. segmented sums: wave w takes list entries [w per, (w + 1) per)
+    const bool run_exact = s_misc[3] != 0u;
+    {
+        const int S = s_off[SEG_KR];
+        const int per = (S + SEG_WAVES - 1) / SEG_WAVES;
+        const int beg = min(S, wave * per), end = min(S, beg + per);
+        if (beg < end) {
+            if (run_exact) seg_sums<D, KVT, false>(src, h, N, list, s_off, acc, s_emin, s_amax, beg, end);
+            else seg_sums<D, KVT, true>(src, h, N, list, s_off, acc, s_emin, s_amax, beg, end);
+        }
+    }
+    __syncthreads();
+
+    // 3. means: one wave per centroid
+    for (int i = wave; i < nk; i += SEG_WAVES) {
+        const int cnt = s_cnt[i];
+        if (cnt == 0) continue;   // an empty cluster keeps its centroid
+        const int k = k0 + i;
+        const double reach = (double)cnt * (double)__uint_as_float(s_amax[i]);
+        const bool exact = run_exact || reach < ldexp(1.0, min(53 + s_emin[i], 1023));
+        float mean[CPL];
+        if (exact) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) mean[c] = mean_of(acc[i * D + lane * CPL + c], cnt);
+        } else {
+            const int a = s_off[i], b = s_off[i + 1];
+            double hs[CPL];
+            float ab[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) { hs[c] = 0.0; ab[c] = 0.f; }
+            for (int j = a; j < b; j += 4) {
+                float v[4][CPL];
+                seg_rows<D, KVT, 4>(src, h, N, list, j, min(4, b - j), v);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        hs[c] += (double)v[u][c];
+                        ab[c] += fabsf(v[u][c]);
+                    }
+            }
+            bool ok = cnt <= (1 << 20);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const double bd = (double)ab[c] * (double)cnt * 0x1p-51 + fabs(hs[c]) * 0x1p-50;
+                const float lo = mean_of(hs[c] - bd, cnt), hi = mean_of(hs[c] + bd, cnt);
+                ok = ok && lo == hi;
+                mean[c] = lo;
+            }
+            if (!__all(ok)) {
+                double es[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) { hs[c] = 0.0; es[c] = 0.0; }
+                for (int j = a; j < b; j += 4) {
+                    float v[4][CPL];
+                    seg_rows<D, KVT, 4>(src, h, N, list, j, min(4, b - j), v);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+#pragma unroll
+                        for (int c = 0; c < CPL; ++c) two_sum(hs[c], es[c], (double)v[u][c]);
+                }
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) mean[c] = mean_of(hs[c] + es[c], cnt);
+            }
+        }
+        double sq = 0.0;
+        uint32_t bb[CPL];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            bb[c] = f32_to_bf16(mean[c]);
+            const double bd = (double)bf16_to_f32(bb[c]);
+            sq += bd * bd;
+        }
+        float *cr = C + ((size_t)h * K + k) * D + lane * CPL;
+        uint16_t *br = Cb + ((size_t)h * Kp + k) * D + lane * CPL;
+        if constexpr (CPL == 2) {
+            *reinterpret_cast<float2 *>(cr) = make_float2(mean[0], mean[1]);
+            *reinterpret_cast<uint32_t *>(br) = bb[0] | (bb[1] << 16);
+        } else {
+            cr[0] = mean[0];
+            br[0] = (uint16_t)bb[0];
+        }
+        sq = wave_sum(sq);
+        if (lane == 0) cnorm[(size_t)h * Kp + k] = sq;
+    }
+}
+
+bool update_seg_fits(int N) { return N >= 1 && N <= SEG_MAX_N; }
+
+size_t value_stats_words(int H) { return (size_t)H * VSTAT_BLOCKS * 2; }
+
+hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &src, const uint8_t *pi,
+                             int64_t pi_hs, const int32_t *counts, const uint32_t *xstats, float *C, uint16_t *Cb,
+                             double *cnorm, int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s) {
+    if (!update_seg_fits(N)) return hipErrorInvalidValue;
+    const int Kp = padded_k(K);
+    const int64_t nb = (int64_t)H * ((K + SEG_KR - 1) / SEG_KR);
+    if (nb >= (int64_t)1 << 31) return hipErrorInvalidValue;
+    QVG_DISPATCH_DT(D, dtype, {
+        const size_t lds = seg_lds_bytes<DD>(N);
+        (void)hipFuncSetAttribute((const void *)k_update_seg<DD, KVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)lds);
+        QVG_KERNEL((k_update_seg<DD, KVT>), dim3((unsigned)nb), dim3(64 * SEG_WAVES), lds, s, src, H, N, K, Kp, pi,
+                   pi_hs, counts, xstats, C, Cb, cnorm, zero_cnt, zero_fill);
+    });
     return hipGetLastError();
 }
 

@@ -66,6 +66,20 @@ hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, 
                          const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb, double *cnorm,
                          int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s);
 
+// The same update without a global sort (k_update_seg): each workgroup lists the
+// tokens of a run of centroids in LDS from pi (uint8, head stride pi_hs, the
+// assignment the counts were taken from).  For N <= SEG_MAX_N.  xstats
+// (value_stats_words(H) words from launch_value_stats over the chunk's input,
+// or null) lets whole runs of centroids skip the per-value exactness checks.
+constexpr int SEG_MAX_N = 16384;
+bool update_seg_fits(int N);
+size_t value_stats_words(int H);
+hipError_t launch_value_stats(int dtype, int H, const void *x, int64_t x_hs, int64_t count, uint32_t *stats,
+                              hipStream_t s);
+hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &src, const uint8_t *pi,
+                             int64_t pi_hs, const int32_t *counts, const uint32_t *xstats, float *C, uint16_t *Cb,
+                             double *cnorm, int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s);
+
 // dst_slice [H][K][D] = C rounded to dtype; cache_slice [H][K][D] = C (if non-null).
 hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype, void *dst_slice,
                                   float *cache_slice, hipStream_t s);

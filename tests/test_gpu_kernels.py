@@ -162,8 +162,36 @@ def test_assign_from_fp32_input_rounds_operands():
     np.testing.assert_array_equal(to_np(out)[0], oracle.assign(X[0], C[0], "parity"))
 
 
+def _run_update(X, lab, C0, dtype):
+    """qvg_centroid_update on the device; returns (centroids, counts) as numpy."""
+    q = lib()
+    H, N, d = X.shape
+    K = C0.shape[1]
+    cd = torch.from_numpy(C0).to(DEV)
+    counts = torch.empty((H, K), dtype=torch.int32, device=DEV)
+    ws_bytes = q.qvg_stage_workspace_bytes(H, N, d, K)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    labd = torch.from_numpy(lab.astype(np.uint8)).to(DEV)
+    q.qvg_centroid_update(to_dev(X, dtype), q.QVG_BF16 if dtype == "bf16" else q.QVG_F32, N * d, labd, N, H, N,
+                          d, K, cd, counts, ws, ws_bytes)
+    torch.cuda.synchronize()
+    return to_np(cd), to_np(counts)
+
+
+def _check_update(X, lab, C0, dtype):
+    got, cnt_got = _run_update(X, lab, C0, dtype)
+    for h in range(X.shape[0]):
+        ref, cnt = oracle.update(X[h].astype(np.float64), lab[h], C0[h].astype(np.float64), "parity")
+        np.testing.assert_array_equal(cnt_got[h], cnt)
+        np.testing.assert_array_equal(got[h], ref.astype(np.float32))
+    return got
+
+
+# N up to 16384 runs the LDS token-list kernel, longer chunks the global sort
 @pytest.mark.parametrize("dtype,d,K,N,H", [("bf16", 128, 256, 4680, 1), ("f32", 128, 256, 2000, 2),
-                                           ("f32", 64, 16, 128, 1), ("bf16", 64, 40, 1001, 3)])
+                                           ("f32", 64, 16, 128, 1), ("bf16", 64, 40, 1001, 3),
+                                           ("bf16", 128, 256, 16384, 1), ("bf16", 128, 256, 20000, 1),
+                                           ("f32", 64, 200, 17000, 2)])
 def test_update_bit_exact(dtype, d, K, N, H):
     say(f"centroid_update {dtype} d={d} K={K} N={N} H={H}")
     q = lib()
@@ -189,6 +217,43 @@ def test_update_bit_exact(dtype, d, K, N, H):
         np.testing.assert_array_equal(to_np(counts[h]), cnt)
         np.testing.assert_array_equal(to_np(cd[h]), ref.astype(np.float32))
         np.testing.assert_array_equal(to_np(cd[h])[K - 1], C0[h, K - 1])
+
+
+@pytest.mark.parametrize("N", [300, 16384])
+def test_update_one_cluster_holds_every_token(N):
+    """The whole chunk in one centroid: the token list of one workgroup is full."""
+    say(f"centroid_update, all {N} tokens in centroid 37")
+    rng = np.random.default_rng(N)
+    X = oracle.bf16_round(rng.standard_normal((1, N, 128)) * 3).astype(np.float32)
+    lab = np.full((1, N), 37)
+    C0 = rng.standard_normal((1, 256, 128)).astype(np.float32)
+    got = _check_update(X, lab, C0, "bf16")
+    np.testing.assert_array_equal(np.delete(got[0], 37, axis=0), np.delete(C0[0], 37, axis=0))
+
+
+@pytest.mark.parametrize("N", [1000, 17000])
+def test_update_cancellation_needs_exact_sums(N):
+    """Rows that cancel at 2^24 around tiny values: the plain fp64 sum loses the
+    tiny part, so neither the lowest-bit certificate nor the interval test holds
+    and the exact two-sum pass decides (its result is the oracle's exactly rounded
+    mean).  Other centroids hold values 2^40 apart in magnitude, which fail the
+    certificate but pass the interval test."""
+    say(f"centroid_update cancellation, N={N}")
+    rng = np.random.default_rng(7)
+    d, K = 64, 20
+    X = rng.standard_normal((1, N, d)).astype(np.float32)
+    lab = rng.integers(2, K, (1, N))
+    big = np.float32(2.0 ** 24)
+    tiny = (rng.integers(1, 1 << 20, d) * 2.0 ** -52).astype(np.float32)
+    X[0, 0], X[0, 1], X[0, 2] = big, -big, tiny          # centroid 0: exact mean tiny / 5
+    X[0, 3], X[0, 4] = big * 0.5, -big * 0.5
+    lab[0, :5] = 0
+    X[0, 5:9] = rng.standard_normal((4, d)) * 2.0 ** 20   # centroid 1: magnitudes 2^40 apart
+    X[0, 9:13] = rng.standard_normal((4, d)) * 2.0 ** -20
+    lab[0, 5:13] = 1
+    C0 = rng.standard_normal((1, K, d)).astype(np.float32)
+    got = _check_update(X, lab, C0, "f32")
+    np.testing.assert_array_equal(got[0, 0], (tiny.astype(np.float64) / 5).astype(np.float32))
 
 
 @pytest.mark.parametrize("N,K,dtype", [(4680, 256, "bf16"), (128, 16, "f32"), (100, 256, "bf16"), (257, 256, "f32")])
