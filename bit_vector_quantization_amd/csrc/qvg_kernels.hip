@@ -361,55 +361,93 @@ constexpr float PAD_HALF_NORM = -1e30f;   // padding rows: never the nearest
 __device__ __forceinline__ float fmax_key(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, __FLT_MAX__); }
 __device__ __forceinline__ float fmin_key(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -__FLT_MAX__); }
 
+// fp32(x - c) of eight bf16 pairs, rounded back to bf16.
+__device__ __forceinline__ uint4 sub_bf16x8(uint4 x, uint4 c) {
+    const uint32_t xw[4] = {x.x, x.y, x.z, x.w}, cw[4] = {c.x, c.y, c.z, c.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = pack_bf16x2(__uint_as_float(xw[i] << 16) - __uint_as_float(cw[i] << 16),
+                           __uint_as_float(xw[i] & 0xFFFF0000u) - __uint_as_float(cw[i] & 0xFFFF0000u));
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // The B operands of the TILE tokens from tok0 (zero past N): channels
-// 32 s + 8 g .. +7 of R(P) for k-step s, rounded to bf16.
-template <int D, typename KVT>
+// 32 s + 8 g .. +7 of R(P) for k-step s, rounded to bf16.  Rows past N read
+// row N - 1 and are zeroed afterwards, so every load is issued unconditionally
+// and the loads of a stage are in flight together.  ANYP: any number of
+// earlier stages (else a bf16 tensor with at most one).
+template <int D, typename KVT, bool ANYP>
 __device__ __forceinline__ void assign_load(const Src &src, int h, int N, int tok0, bf16x8_t (&bt)[ASSIGN_TB][D / 32]) {
     constexpr int KS = D / 32;
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-    if (sizeof(KVT) == 2 && src.P == 0) {   // the bf16 input itself is the operand
+    int n[ASSIGN_TB];
+    bool ok[ASSIGN_TB];
 #pragma unroll
-        for (int b = 0; b < ASSIGN_TB; ++b) {
-            const int n = tok0 + 16 * b + r16;
-            const uint4 *row = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src.x) +
-                                                               (size_t)h * src.x_hs + (size_t)n * D + 8 * g);
+    for (int b = 0; b < ASSIGN_TB; ++b) {
+        const int t = tok0 + 16 * b + r16;
+        ok[b] = t < N;
+        n[b] = ok[b] ? t : N - 1;
+    }
+    if constexpr (sizeof(KVT) == 2 && !ANYP) {
+        {   // the input, or the input less one stored bf16 table
+            uint4 xr[ASSIGN_TB][KS];
 #pragma unroll
-            for (int s = 0; s < KS; ++s) bt[b][s] = __builtin_bit_cast(bf16x8_t, n < N ? row[4 * s] : make_uint4(0, 0, 0, 0));
+            for (int b = 0; b < ASSIGN_TB; ++b) {
+                const uint4 *row = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src.x) +
+                                                                   (size_t)h * src.x_hs + (size_t)n[b] * D + 8 * g);
+#pragma unroll
+                for (int s = 0; s < KS; ++s) xr[b][s] = row[4 * s];
+            }
+            if (src.P == 1) {
+                int k[ASSIGN_TB];
+#pragma unroll
+                for (int b = 0; b < ASSIGN_TB; ++b) k[b] = src.pi[0][(size_t)h * src.pi_hs + n[b]];
+                // one token block at a time: the table rows come from L2, and
+                // holding both blocks' rows at once would exceed the register budget
+#pragma unroll
+                for (int b = 0; b < ASSIGN_TB; ++b) {
+                    const uint4 *row = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(src.cent[0]) +
+                                                                       ((size_t)h * src.K + k[b]) * D + 8 * g);
+                    uint4 cr[KS];
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) cr[s] = row[4 * s];
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) xr[b][s] = sub_bf16x8(xr[b][s], cr[s]);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < ASSIGN_TB; ++b)
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    bt[b][s] = __builtin_bit_cast(bf16x8_t, ok[b] ? xr[b][s] : make_uint4(0, 0, 0, 0));
         }
         return;
     }
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
-        const int n = tok0 + 16 * b + r16;
         float v[KS][8];
+        const KVT *xr = static_cast<const KVT *>(src.x) + (size_t)h * src.x_hs + (size_t)n[b] * D + 8 * g;
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[s][i] = 0.f;
-        if (n < N) {
-            const KVT *xr = static_cast<const KVT *>(src.x) + (size_t)h * src.x_hs + (size_t)n * D + 8 * g;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) load8<KVT>(xr + 32 * s, v[s]);
+        for (int s = 0; s < KS; ++s) load8<KVT>(xr + 32 * s, v[s]);
 #pragma unroll 1
-            for (int p = 0; p < src.P; ++p) {
-                const int k = src.pi[p][(size_t)h * src.pi_hs + n];
-                const KVT *cr = static_cast<const KVT *>(src.cent[p]) + ((size_t)h * src.K + k) * D + 8 * g;
+        for (int p = 0; p < src.P; ++p) {
+            const int k = src.pi[p][(size_t)h * src.pi_hs + n[b]];
+            const KVT *cr = static_cast<const KVT *>(src.cent[p]) + ((size_t)h * src.K + k) * D + 8 * g;
+            float c[KS][8];
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    float c[8];
-                    load8<KVT>(cr + 32 * s, c);
+            for (int s = 0; s < KS; ++s) load8<KVT>(cr + 32 * s, c[s]);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) v[s][i] = v[s][i] - c[i];
-                }
-            }
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v[s][i] = v[s][i] - c[s][i];
         }
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-            bt[b][s] = __builtin_bit_cast(
-                bf16x8_t, make_uint4(pack_bf16x2(v[s][0], v[s][1]),
-                                     pack_bf16x2(v[s][2], v[s][3]),
-                                     pack_bf16x2(v[s][4], v[s][5]),
-                                     pack_bf16x2(v[s][6], v[s][7])));
+        for (int s = 0; s < KS; ++s) {
+            const uint4 w = make_uint4(pack_bf16x2(v[s][0], v[s][1]), pack_bf16x2(v[s][2], v[s][3]),
+                                       pack_bf16x2(v[s][4], v[s][5]), pack_bf16x2(v[s][6], v[s][7]));
+            bt[b][s] = __builtin_bit_cast(bf16x8_t, ok[b] ? w : make_uint4(0, 0, 0, 0));
+        }
     }
 }
 
@@ -581,7 +619,7 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
 // XCD by XCD so that an XCD's L2 serves the tables of a run of heads.  A
 // workgroup stages a head's table once for all of its tiles of that head, and
 // its waves take tiles from an LDS counter until the head's run is done.
-template <int D, typename KVT>
+template <int D, typename KVT, bool ANYP>
 __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H, int N, const uint16_t *__restrict__ Cb,
                                                                  const double *__restrict__ cnorm, int Kp,
                                                                  uint8_t *__restrict__ pi, int64_t pi_hs,
@@ -634,7 +672,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
             if (m >= e) break;
             const int tok0 = (m - h * T) * TILE;
             bf16x8_t bt[ASSIGN_TB][D / 32];
-            assign_load<D, KVT>(src, h, N, tok0, bt);
+            assign_load<D, KVT, ANYP>(src, h, N, tok0, bt);
             assign_wave<D, KVT>(src, h, N, tok0, bt, lds, lcn64, lhcn, lists + wave * TILE, Kp, pi, pi_hs, counts);
         }
         __syncthreads();   // the table is replaced only once every wave is done with it
@@ -662,10 +700,20 @@ hipError_t launch_assign(int D, int dtype, int H, int N, const Src &src, const u
     if (units >= (int64_t)1 << 31) return hipErrorInvalidValue;
     const int64_t nb = std::min<int64_t>(2 * (int64_t)device_cus(), (units + ASSIGN_WAVES - 1) / ASSIGN_WAVES);
     dim3 g((unsigned)std::max<int64_t>(nb, 1)), b(64 * ASSIGN_WAVES);
+    // bf16 tensors with at most one earlier stage (every stage at T <= 2) take the
+    // specialised operand load
+    const bool anyp = !(dtype == DT_BF16 && src.P <= 1);
     QVG_DISPATCH_DT(D, dtype, {
-        (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)lds);
-        QVG_KERNEL((k_assign<DD, KVT>), g, b, lds, s, src, H, N, Cb, cnorm, Kp, pi, pi_hs, counts);
+        if (anyp || sizeof(KVT) != 2) {
+            (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT, true>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            QVG_KERNEL((k_assign<DD, KVT, true>), g, b, lds, s, src, H, N, Cb, cnorm, Kp, pi, pi_hs, counts);
+        } else {
+            using KB = uint16_t;   // (this branch is only taken for bf16)
+            (void)hipFuncSetAttribute((const void *)k_assign<DD, KB, false>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            QVG_KERNEL((k_assign<DD, KB, false>), g, b, lds, s, src, H, N, Cb, cnorm, Kp, pi, pi_hs, counts);
+        }
     });
     return hipGetLastError();
 }
