@@ -349,13 +349,13 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
 // fp64 and the sums are exact for the value ranges met in practice, so the
 // decision is that of |c|^2 - 2 <x, c>, lowest index on ties.
 //
-// A workgroup is 8 waves x 64 tokens of one head.  The head's bf16 table
-// (swizzled 16-byte chunks, 64 KiB at 256 x 128) and its norms sit in LDS:
-// two workgroups per CU, four waves per SIMD.
+// A workgroup is 16 waves, each taking 32-token tiles; the bf16 tables of up
+// to two heads (swizzled 16-byte chunks, 64 KiB each at 256 x 128) and their
+// norms sit in LDS: one workgroup per CU, four waves per SIMD.
 
 constexpr int ASSIGN_TB = 2;              // 16-token blocks per wave
 constexpr int TILE = 16 * ASSIGN_TB;      // tokens per wave
-constexpr int ASSIGN_WAVES = 8;           // waves per workgroup
+constexpr int ASSIGN_WAVES = 16;          // waves per workgroup
 constexpr float PAD_HALF_NORM = -1e30f;   // padding rows: never the nearest
 
 __device__ __forceinline__ float fmax_key(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, __FLT_MAX__); }
@@ -615,10 +615,11 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
     }
 }
 
-// Persistent workgroups: each owns a contiguous run of the (head, tile) units,
-// XCD by XCD so that an XCD's L2 serves the tables of a run of heads.  A
-// workgroup stages a head's table once for all of its tiles of that head, and
-// its waves take tiles from an LDS counter until the head's run is done.
+// Persistent workgroups, one per CU: each owns a contiguous run of the
+// (head, tile) units, XCD by XCD so that an XCD's L2 serves the tables of a run
+// of heads.  The run is taken in windows of at most two heads whose tables are
+// staged together in LDS (a run shorter than a head's tiles is one window), and
+// the waves take the window's tiles from an LDS counter.
 template <int D, typename KVT, bool ANYP>
 __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H, int N, const uint16_t *__restrict__ Cb,
                                                                  const double *__restrict__ cnorm, int Kp,
@@ -627,10 +628,10 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
     constexpr int CH = D / 8;
     constexpr int NT = 64 * ASSIGN_WAVES;
     constexpr int STAGE = (256 * CH + NT - 1) / NT;   // table chunks per thread at 256 centroids
-    extern __shared__ uint4 lds[];
-    double *lcn64 = reinterpret_cast<double *>(lds + Kp * CH);
-    float *lhcn = reinterpret_cast<float *>(lcn64 + Kp);
-    int32_t *lists = reinterpret_cast<int32_t *>(lhcn + Kp);
+    extern __shared__ uint4 lds[];                      // two table slots
+    double *lcn64 = reinterpret_cast<double *>(lds + 2 * Kp * CH);
+    float *lhcn = reinterpret_cast<float *>(lcn64 + 2 * Kp);
+    int32_t *lists = reinterpret_cast<int32_t *>(lhcn + 2 * Kp);
     int32_t *next = lists + ASSIGN_WAVES * TILE;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int T = (N + TILE - 1) / TILE;   // tiles per head
@@ -639,29 +640,35 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
     const int64_t u1 = U * (r + 1) / gridDim.x;
     const int nch = Kp * CH;
     for (int64_t u = U * r / gridDim.x; u < u1;) {
-        const int h = (int)(u / T);
-        const int e = (int)min(u1, (int64_t)(h + 1) * T);   // end of this head's run
-        const uint4 *csrc = reinterpret_cast<const uint4 *>(Cb + (size_t)h * Kp * D);
-        uint4 st[STAGE];
+        const int h0 = (int)(u / T);
+        const int nh = (int)min((int64_t)2, (u1 - 1) / T - h0 + 1);   // heads in this window
+        const int e = (int)min(u1, (int64_t)(h0 + nh) * T);
+        // the thread index is re-read here so that the staging addresses are
+        // formed per window instead of being held in registers across windows
+        int t0 = tid;
+        asm volatile("" : "+v"(t0));
+        for (int sl = 0; sl < nh; ++sl) {
+            const uint4 *csrc = reinterpret_cast<const uint4 *>(Cb + (size_t)(h0 + sl) * Kp * D);
+            uint4 st[STAGE];
 #pragma unroll
-        for (int k = 0; k < STAGE; ++k) {
-            const int i = tid + NT * k;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (i < nch) v = csrc[i];
-            st[k] = v;
-        }
-#pragma unroll
-        for (int k = 0; k < STAGE; ++k) {
-            const int i = tid + NT * k;
-            if (i < nch) {
-                const int row = i / CH, q = i - row * CH;
-                lds[row * CH + (q ^ (row & (CH - 1)))] = st[k];
+            for (int k = 0; k < STAGE; ++k) {   // unconditional loads: rows past the table read its last chunk
+                const int i = t0 + NT * k;
+                st[k] = csrc[i < nch ? i : nch - 1];
             }
-        }
-        if (tid < Kp) {
-            const double c = cnorm[(size_t)h * Kp + tid];
-            lcn64[tid] = c;
-            lhcn[tid] = c < 1e300 ? -0.5f * (float)c : PAD_HALF_NORM;
+            uint4 *slot = lds + sl * nch;
+#pragma unroll
+            for (int k = 0; k < STAGE; ++k) {
+                const int i = t0 + NT * k;
+                if (i < nch) {
+                    const int row = i / CH, q = i - row * CH;
+                    slot[row * CH + (q ^ (row & (CH - 1)))] = st[k];
+                }
+            }
+            if (t0 < Kp) {
+                const double c = cnorm[(size_t)(h0 + sl) * Kp + t0];
+                lcn64[sl * Kp + t0] = c;
+                lhcn[sl * Kp + t0] = c < 1e300 ? -0.5f * (float)c : PAD_HALF_NORM;
+            }
         }
         if (tid == 0) *next = (int)u;
         __syncthreads();
@@ -670,12 +677,14 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
             if (lane == 0) m = atomicAdd(next, 1);
             m = __builtin_amdgcn_readfirstlane(m);
             if (m >= e) break;
+            const int h = m / T, sl = h - h0;
             const int tok0 = (m - h * T) * TILE;
             bf16x8_t bt[ASSIGN_TB][D / 32];
             assign_load<D, KVT, ANYP>(src, h, N, tok0, bt);
-            assign_wave<D, KVT>(src, h, N, tok0, bt, lds, lcn64, lhcn, lists + wave * TILE, Kp, pi, pi_hs, counts);
+            assign_wave<D, KVT>(src, h, N, tok0, bt, lds + sl * nch, lcn64 + sl * Kp, lhcn + sl * Kp,
+                                lists + wave * TILE, Kp, pi, pi_hs, counts);
         }
-        __syncthreads();   // the table is replaced only once every wave is done with it
+        __syncthreads();   // the tables are replaced only once every wave is done with them
         u = e;
     }
 }
@@ -694,11 +703,11 @@ static int device_cus() {
 
 hipError_t launch_assign(int D, int dtype, int H, int N, const Src &src, const uint16_t *Cb, const double *cnorm,
                          int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts, hipStream_t s) {
-    const size_t lds = (size_t)Kp * D * 2 + (size_t)Kp * 12 + (ASSIGN_WAVES * TILE + 4) * sizeof(int32_t);
-    // two resident workgroups per CU, at least a tile per wave
+    const size_t lds = 2 * ((size_t)Kp * D * 2 + (size_t)Kp * 12) + (ASSIGN_WAVES * TILE + 4) * sizeof(int32_t);
+    // one resident workgroup per CU, at least a tile per wave
     const int64_t units = (int64_t)H * ((N + TILE - 1) / TILE);
     if (units >= (int64_t)1 << 31) return hipErrorInvalidValue;
-    const int64_t nb = std::min<int64_t>(2 * (int64_t)device_cus(), (units + ASSIGN_WAVES - 1) / ASSIGN_WAVES);
+    const int64_t nb = std::min<int64_t>((int64_t)device_cus(), (units + ASSIGN_WAVES - 1) / ASSIGN_WAVES);
     dim3 g((unsigned)std::max<int64_t>(nb, 1)), b(64 * ASSIGN_WAVES);
     // bf16 tensors with at most one earlier stage (every stage at T <= 2) take the
     // specialised operand load
