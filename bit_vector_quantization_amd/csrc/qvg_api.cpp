@@ -131,7 +131,7 @@ struct ProfScope {
 // residuals R(t) are never stored: each kernel rebuilds them from the input
 // and the earlier stages' stored centroids and assignments.
 struct EncodeWorkspace {
-    size_t C = 0, Cb = 0, cn = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, vstats = 0, total = 0;
+    size_t C = 0, Cb = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, vstats = 0, total = 0;
 
     EncodeWorkspace(const qvg_config &c, int H, int N) {
         const size_t D = c.d, K = c.n_centroids, Kp = padded_k(c.n_centroids);
@@ -141,7 +141,6 @@ struct EncodeWorkspace {
         auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
         C = take((size_t)H * K * D * 4);
         Cb = take((size_t)H * Kp * D * 2);
-        cn = take((size_t)H * Kp * 8);
         cnt = take((size_t)2 * H * Kp * 4);
         fill = take((size_t)2 * H * Kp * 4);
         offsets = take((size_t)H * Kp * 4);
@@ -154,14 +153,13 @@ struct EncodeWorkspace {
 
 // Workspace of the stage-level k-means entry points.
 struct StageWorkspace {
-    size_t C = 0, Cb = 0, cn = 0, cnt = 0, fill = 0, offsets = 0, order = 0, vstats = 0, total = 0;
+    size_t C = 0, Cb = 0, cnt = 0, fill = 0, offsets = 0, order = 0, vstats = 0, total = 0;
     StageWorkspace(int H, int N, int D, int K) {
         const size_t Kp = padded_k(K);
         size_t off = 0;
         auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
         C = take((size_t)H * K * D * 4);
         Cb = take((size_t)H * Kp * D * 2);
-        cn = take((size_t)H * Kp * 8);
         cnt = take((size_t)H * Kp * 4);
         fill = take((size_t)H * Kp * 4);
         offsets = take((size_t)H * Kp * 4);
@@ -348,7 +346,6 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
 
     float *C = at<float>(workspace, ws.C);
     uint16_t *Cb = at<uint16_t>(workspace, ws.Cb);
-    double *cn = at<double>(workspace, ws.cn);
     int32_t *cnt[2] = {at<int32_t>(workspace, ws.cnt), at<int32_t>(workspace, ws.cnt) + (size_t)H * Kp};
     int32_t *fill[2] = {at<int32_t>(workspace, ws.fill), at<int32_t>(workspace, ws.fill) + (size_t)H * Kp};
     int32_t *offsets = at<int32_t>(workspace, ws.offsets);
@@ -367,7 +364,7 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
     Src src = src0;
     src.pi_hs = cap;
     src.K = K;
-    const double table = (double)H * Kp * (D * 2 + 8);
+    const double table = (double)H * Kp * D * 2;
     for (int t = 1; t <= T; ++t) {
         uint8_t *pi = dst->assign + (size_t)(t - 1) * H * cap + tok0;
         const size_t slice = (size_t)(t - 1) * H * K * D;
@@ -377,26 +374,26 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
         const double row_bytes = HND * esz + (double)H * N * (t - 1);
         const double assign_flops = 2.0 * H * N * K * D;
         QVG_LAUNCH("init_centroids", 0, (double)H * K * D * (esz + 4) + table,
-                   launch_init_centroids(D, cfg->dtype, H, K, src, idx + (size_t)(t - 1) * H * K, warm, C, Cb, cn,
+                   launch_init_centroids(D, cfg->dtype, H, K, src, idx + (size_t)(t - 1) * H * K, warm, C, Cb,
                                          cnt[0], fill[0], s));
         for (int it = 0; it < iters; ++it) {
             const int c = it & 1;
             QVG_LAUNCH("assign", assign_flops, row_bytes + H * N + table,
-                       launch_assign(D, cfg->dtype, H, N, src, Cb, cn, Kp, pi, cap, cnt[c], s));
+                       launch_assign(D, cfg->dtype, H, N, K, src, Cb, pi, cap, cnt[c], s));
             if (update_seg_fits(N)) {
                 QVG_LAUNCH("update", HND, row_bytes + H * N + (double)H * K * D * 4 + table,
-                           launch_update_seg(D, cfg->dtype, H, N, K, src, pi, cap, cnt[c], vstats, C, Cb, cn,
+                           launch_update_seg(D, cfg->dtype, H, N, K, src, pi, cap, cnt[c], vstats, C, Cb,
                                              cnt[c ^ 1], fill[c ^ 1], s));
             } else {
                 QVG_LAUNCH("scatter", 0, H * N * 5.0 + H * Kp * 8.0,
                            launch_scatter(H, N, Kp, pi, cap, cnt[c], fill[c], offsets, order, s));
                 QVG_LAUNCH("update", HND, row_bytes + H * N * 4.0 + (double)H * K * D * 4 + table,
-                           launch_update(D, cfg->dtype, H, N, K, src, cnt[c], offsets, order, C, Cb, cn, cnt[c ^ 1],
+                           launch_update(D, cfg->dtype, H, N, K, src, cnt[c], offsets, order, C, Cb, cnt[c ^ 1],
                                          fill[c ^ 1], s));
             }
         }
         QVG_LAUNCH("assign", assign_flops, row_bytes + H * N + table,
-                   launch_assign(D, cfg->dtype, H, N, src, Cb, cn, Kp, pi, cap, nullptr, s));
+                   launch_assign(D, cfg->dtype, H, N, K, src, Cb, pi, cap, nullptr, s));
         void *cslot = static_cast<char *>(dst->centroids) +
                       (((size_t)chunk_index * T + (t - 1)) * H * K * D) * esz;
         QVG_LAUNCH("store_centroids", 0, (double)H * K * D * (4 + esz + (cache ? 4 : 0)),
@@ -477,15 +474,14 @@ qvg_status qvg_kmeans_assign(const void *x, int32_t x_dtype, int64_t x_head_stri
     const Src src = plain_src(x, x_head_stride);
     float *C = at<float>(workspace, ws.C);
     uint16_t *Cb = at<uint16_t>(workspace, ws.Cb);
-    double *cn = at<double>(workspace, ws.cn);
     const int Kp = padded_k(n_centroids);
-    const double table = (double)heads * Kp * (d * 2 + 8);
+    const double table = (double)heads * Kp * d * 2;
     QVG_LAUNCH("init_centroids", 0, (double)heads * n_centroids * d * 8 + table,
-               launch_init_centroids(d, x_dtype, heads, n_centroids, src, nullptr, centroids, C, Cb, cn, nullptr,
+               launch_init_centroids(d, x_dtype, heads, n_centroids, src, nullptr, centroids, C, Cb, nullptr,
                                      nullptr, s));
     QVG_LAUNCH("assign", 2.0 * heads * n_tokens * n_centroids * d,
                (double)heads * n_tokens * (d * dtype_size(x_dtype) + 1) + table,
-               launch_assign(d, x_dtype, heads, n_tokens, src, Cb, cn, Kp, assign_out, assign_head_stride, nullptr,
+               launch_assign(d, x_dtype, heads, n_tokens, n_centroids, src, Cb, assign_out, assign_head_stride, nullptr,
                              s));
     return QVG_OK;
 }
@@ -514,7 +510,7 @@ qvg_status qvg_centroid_update(const void *x, int32_t x_dtype, int64_t x_head_st
     QVG_LAUNCH("zero", 0, heads * Kp * 8.0, launch_zero(cnt, (int64_t)heads * Kp, s));
     QVG_LAUNCH("count", 0, (double)heads * n_tokens + heads * Kp * 4.0,
                launch_count(heads, n_tokens, Kp, assign, assign_head_stride, cnt, s));
-    const double tables = (double)heads * n_centroids * d * 4 + (double)heads * Kp * (d * 2 + 8);
+    const double tables = (double)heads * n_centroids * d * 4 + (double)heads * Kp * d * 2;
     if (update_seg_fits(n_tokens)) {
         uint32_t *vstats = at<uint32_t>(workspace, ws.vstats);
         QVG_LAUNCH("value_stats", 0, HND * dtype_size(x_dtype),
@@ -522,14 +518,14 @@ qvg_status qvg_centroid_update(const void *x, int32_t x_dtype, int64_t x_head_st
         QVG_LAUNCH("update", HND, HND * dtype_size(x_dtype) + (double)heads * n_tokens + tables,
                    launch_update_seg(d, x_dtype, heads, n_tokens, n_centroids, plain_src(x, x_head_stride), assign,
                                      assign_head_stride, cnt, vstats, centroids, at<uint16_t>(workspace, ws.Cb),
-                                     at<double>(workspace, ws.cn), nullptr, nullptr, s));
+                                     nullptr, nullptr, s));
     } else {
         QVG_LAUNCH("zero", 0, heads * Kp * 8.0, launch_zero(fill, (int64_t)heads * Kp, s));
         QVG_LAUNCH("scatter", 0, heads * n_tokens * 5.0 + heads * Kp * 8.0,
                    launch_scatter(heads, n_tokens, Kp, assign, assign_head_stride, cnt, fill, offsets, order, s));
         QVG_LAUNCH("update", HND, HND * dtype_size(x_dtype) + heads * n_tokens * 4.0 + tables,
                    launch_update(d, x_dtype, heads, n_tokens, n_centroids, plain_src(x, x_head_stride), cnt, offsets,
-                                 order, centroids, at<uint16_t>(workspace, ws.Cb), at<double>(workspace, ws.cn),
+                                 order, centroids, at<uint16_t>(workspace, ws.Cb),
                                  nullptr, nullptr, s));
     }
     if (counts_out)

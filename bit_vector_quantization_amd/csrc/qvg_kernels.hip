@@ -256,44 +256,35 @@ hipError_t launch_forgy(int T, int H, int N, int K, uint64_t seed, int32_t *idx,
 }
 
 // ---------------------------------------------------------------------------
-// centroid rows: C (fp32), Cb (bf16 operand), cnorm = |Cb|^2 (fp64)
+// centroid rows: C (fp32) and Cb (bf16 operand)
 // ---------------------------------------------------------------------------
 
 // Lanes 0 .. D/8-1 of a wave own 8 channels each of centroid k of head h.
 template <int D>
 __device__ __forceinline__ void write_centroid8(int h, int k, int K, int Kp, int lane, const float (&v)[8],
-                                                float *C, uint16_t *Cb, double *cnorm) {
-    double sq = 0.0;
+                                                float *C, uint16_t *Cb) {
     if (lane < D / 8) {
         uint32_t b[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            b[i] = f32_to_bf16(v[i]);
-            const double bd = (double)bf16_to_f32(b[i]);
-            sq += bd * bd;
-        }
+        for (int i = 0; i < 8; ++i) b[i] = f32_to_bf16(v[i]);
         float4 *c = reinterpret_cast<float4 *>(C + ((size_t)h * K + k) * D + lane * 8);
         c[0] = make_float4(v[0], v[1], v[2], v[3]);
         c[1] = make_float4(v[4], v[5], v[6], v[7]);
         *reinterpret_cast<uint4 *>(Cb + ((size_t)h * Kp + k) * D + lane * 8) =
             make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
     }
-    sq = wave_sum(sq);
-    if (lane == 0) cnorm[(size_t)h * Kp + k] = sq;
 }
 
 template <int D, typename KVT>
 __global__ __launch_bounds__(64) void k_init_centroids(int K, int Kp, Src src, const int32_t *idx, const float *warm,
-                                                       float *C, uint16_t *Cb, double *cnorm, int32_t *cnt0,
-                                                       int32_t *fill0) {
+                                                       float *C, uint16_t *Cb, int32_t *cnt0, int32_t *fill0) {
     const int k = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
     if (lane == 0 && cnt0) {
         cnt0[(size_t)h * Kp + k] = 0;
         fill0[(size_t)h * Kp + k] = 0;
     }
-    if (k >= K) {  // padding rows: never chosen
+    if (k >= K) {  // padding rows (the assign never chooses them)
         if (lane < D / 8) *reinterpret_cast<uint4 *>(Cb + ((size_t)h * Kp + k) * D + lane * 8) = make_uint4(0, 0, 0, 0);
-        if (lane == 0) cnorm[(size_t)h * Kp + k] = __builtin_inf();
         return;
     }
     float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -301,16 +292,16 @@ __global__ __launch_bounds__(64) void k_init_centroids(int K, int Kp, Src src, c
         if (warm) load8<float>(warm + ((size_t)h * K + k) * D + lane * 8, v);
         else src_row8<D, KVT>(src, h, idx[(size_t)h * K + k], lane * 8, v);
     }
-    write_centroid8<D>(h, k, K, Kp, lane, v, C, Cb, cnorm);
+    write_centroid8<D>(h, k, K, Kp, lane, v, C, Cb);
 }
 
 hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src, const int32_t *idx,
-                                 const float *warm, float *C, uint16_t *Cb, double *cnorm, int32_t *cnt0,
-                                 int32_t *fill0, hipStream_t s) {
+                                 const float *warm, float *C, uint16_t *Cb, int32_t *cnt0, int32_t *fill0,
+                                 hipStream_t s) {
     const int Kp = padded_k(K);
     QVG_DISPATCH_DT(D, dtype,
                     QVG_KERNEL((k_init_centroids<DD, KVT>), dim3(Kp, H), dim3(64), 0, s, K, Kp, src, idx,
-                                       warm, C, Cb, cnorm, cnt0, fill0));
+                                       warm, C, Cb, cnt0, fill0));
     return hipGetLastError();
 }
 
@@ -622,9 +613,8 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
 // the waves take the window's tiles from an LDS counter.
 template <int D, typename KVT, bool ANYP>
 __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H, int N, const uint16_t *__restrict__ Cb,
-                                                                 const double *__restrict__ cnorm, int Kp,
-                                                                 uint8_t *__restrict__ pi, int64_t pi_hs,
-                                                                 int32_t *__restrict__ counts) {
+                                                                 int K, int Kp, uint8_t *__restrict__ pi,
+                                                                 int64_t pi_hs, int32_t *__restrict__ counts) {
     constexpr int CH = D / 8;
     constexpr int NT = 64 * ASSIGN_WAVES;
     constexpr int STAGE = (256 * CH + NT - 1) / NT;   // table chunks per thread at 256 centroids
@@ -659,15 +649,25 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
 #pragma unroll
             for (int k = 0; k < STAGE; ++k) {
                 const int i = t0 + NT * k;
-                if (i < nch) {
-                    const int row = i / CH, q = i - row * CH;
-                    slot[row * CH + (q ^ (row & (CH - 1)))] = st[k];
+                const int row = i / CH, q = i - row * CH;
+                if (i < nch) slot[row * CH + (q ^ (row & (CH - 1)))] = st[k];
+                // |c|^2 of the row: the CH lanes holding its chunks are neighbours;
+                // every bf16 square is exact in fp64
+                const uint32_t w[4] = {st[k].x, st[k].y, st[k].z, st[k].w};
+                double sq = 0.0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const double lo = (double)__uint_as_float(w[j] << 16), hi = (double)__uint_as_float(w[j] & 0xFFFF0000u);
+                    sq = fma(lo, lo, sq);
+                    sq = fma(hi, hi, sq);
                 }
-            }
-            if (t0 < Kp) {
-                const double c = cnorm[(size_t)(h0 + sl) * Kp + t0];
-                lcn64[sl * Kp + t0] = c;
-                lhcn[sl * Kp + t0] = c < 1e300 ? -0.5f * (float)c : PAD_HALF_NORM;
+#pragma unroll
+                for (int o = 1; o < CH; o <<= 1) sq += __shfl_xor(sq, o);
+                if (q == 0 && i < nch) {
+                    const bool real = row < K;   // padding rows are never chosen
+                    lcn64[sl * Kp + row] = real ? sq : __builtin_inf();
+                    lhcn[sl * Kp + row] = real ? -0.5f * (float)sq : PAD_HALF_NORM;
+                }
             }
         }
         if (tid == 0) *next = (int)u;
@@ -701,8 +701,9 @@ static int device_cus() {
     return cus[dev];
 }
 
-hipError_t launch_assign(int D, int dtype, int H, int N, const Src &src, const uint16_t *Cb, const double *cnorm,
-                         int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts, hipStream_t s) {
+hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, const uint16_t *Cb, uint8_t *pi,
+                         int64_t pi_hs, int32_t *counts, hipStream_t s) {
+    const int Kp = padded_k(K);
     const size_t lds = 2 * ((size_t)Kp * D * 2 + (size_t)Kp * 12) + (ASSIGN_WAVES * TILE + 4) * sizeof(int32_t);
     // one resident workgroup per CU, at least a tile per wave
     const int64_t units = (int64_t)H * ((N + TILE - 1) / TILE);
@@ -716,12 +717,12 @@ hipError_t launch_assign(int D, int dtype, int H, int N, const Src &src, const u
         if (anyp || sizeof(KVT) != 2) {
             (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT, true>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            QVG_KERNEL((k_assign<DD, KVT, true>), g, b, lds, s, src, H, N, Cb, cnorm, Kp, pi, pi_hs, counts);
+            QVG_KERNEL((k_assign<DD, KVT, true>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts);
         } else {
             using KB = uint16_t;   // (this branch is only taken for bf16)
             (void)hipFuncSetAttribute((const void *)k_assign<DD, KB, false>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            QVG_KERNEL((k_assign<DD, KB, false>), g, b, lds, s, src, H, N, Cb, cnorm, Kp, pi, pi_hs, counts);
+            QVG_KERNEL((k_assign<DD, KB, false>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts);
         }
     });
     return hipGetLastError();
@@ -868,7 +869,7 @@ __device__ __forceinline__ float mean_of(double t, int cnt) { return (float)(t /
 template <int D, typename KVT>
 __global__ __launch_bounds__(256) void k_update(Src src, int N, int K, int Kp, const int32_t *counts,
                                                 const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb,
-                                                double *cnorm, int32_t *zero_cnt, int32_t *zero_fill) {
+                                                int32_t *zero_cnt, int32_t *zero_fill) {
     constexpr int LPR = D / 8;        // lanes per row
     const int lane = threadIdx.x & 63;
     const int k = blockIdx.x * 4 + (threadIdx.x >> 6), h = blockIdx.y;
@@ -933,33 +934,25 @@ __global__ __launch_bounds__(256) void k_update(Src src, int N, int K, int Kp, c
 #pragma unroll
         for (int i = 0; i < 8; ++i) mean[i] = mean_of(hs[i] + es[i], cnt);
     }
-    double sq = 0.0;
     if (slot == 0) {
         uint32_t b[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            b[i] = f32_to_bf16(mean[i]);
-            const double bd = (double)bf16_to_f32(b[i]);
-            sq += bd * bd;
-        }
+        for (int i = 0; i < 8; ++i) b[i] = f32_to_bf16(mean[i]);
         float4 *c = reinterpret_cast<float4 *>(C + ((size_t)h * K + k) * D + c0);
         c[0] = make_float4(mean[0], mean[1], mean[2], mean[3]);
         c[1] = make_float4(mean[4], mean[5], mean[6], mean[7]);
         *reinterpret_cast<uint4 *>(Cb + ((size_t)h * Kp + k) * D + c0) =
             make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
     }
-#pragma unroll
-    for (int o = 1; o < LPR; o <<= 1) sq += __shfl_xor(sq, o);
-    if (lane == 0) cnorm[(size_t)h * Kp + k] = sq;
 }
 
 hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, const int32_t *counts,
-                         const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb, double *cnorm,
-                         int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s) {
+                         const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb, int32_t *zero_cnt,
+                         int32_t *zero_fill, hipStream_t s) {
     const int Kp = padded_k(K);
     QVG_DISPATCH_DT(D, dtype,
                     QVG_KERNEL((k_update<DD, KVT>), dim3((K + 3) / 4, H), dim3(256), 0, s, src, N, K, Kp,
-                                       counts, offsets, order, C, Cb, cnorm, zero_cnt, zero_fill));
+                                       counts, offsets, order, C, Cb, zero_cnt, zero_fill));
     return hipGetLastError();
 }
 
@@ -1239,7 +1232,7 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
                                                                const uint8_t *__restrict__ pi, int64_t pi_hs,
                                                                const int32_t *__restrict__ counts,
                                                                const uint32_t *__restrict__ xstats, float *C,
-                                                               uint16_t *Cb, double *cnorm, int32_t *zero_cnt,
+                                                               uint16_t *Cb, int32_t *zero_cnt,
                                                                int32_t *zero_fill) {
     constexpr int CPL = D / 64;
     constexpr int NT = 64 * SEG_WAVES;
@@ -1260,6 +1253,52 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
     const int nk = min(SEG_KR, K - k0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+    // The reads that do not depend on the counts are issued first, so that the
+    // label batch, the tables and the counts are in flight together.
+    // Labels of the earlier stages ride along in the list entries; missing
+    // stages read the current labels again and drop them.
+    const uint8_t *lab = pi + (size_t)h * pi_hs;
+    const uint8_t *l1 = src.P >= 1 ? src.pi[0] + (size_t)h * src.pi_hs : lab;
+    const uint8_t *l2 = src.P >= 2 ? src.pi[1] + (size_t)h * src.pi_hs : lab;
+    const uint32_t m1 = src.P >= 1 ? 0xFFu : 0u, m2 = src.P >= 2 ? 0xFFu : 0u;
+    constexpr int B = 8;
+    uint32_t lk[B], la[B], lb[B];
+    auto label_batch = [&](int n0) {   // unconditional loads, all in flight together
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const int n = min(n0 + i * NT + tid, N - 1);
+            lk[i] = lab[n];
+            la[i] = l1[n];
+            lb[i] = l2[n];
+        }
+    };
+    label_batch(0);
+    uint32_t tmn = 0xFFFFFFFFu, tmx = 0u;   // magnitudes of the earlier stages' stored tables
+    if (xstats) {
+        constexpr int PER = 16 / sizeof(KVT);
+        const int nv = K * D / PER;
+#pragma unroll 1
+        for (int p = 0; p < src.P; ++p) {
+            const uint4 *tp = reinterpret_cast<const uint4 *>(static_cast<const KVT *>(src.cent[p]) + (size_t)h * K * D);
+            for (int i = tid; i < nv; i += NT) {
+                const uint4 q = tp[i];
+                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    if constexpr (sizeof(KVT) == 2) {
+                        const uint32_t lo = w[jj] & 0x7FFFu, hi = (w[jj] >> 16) & 0x7FFFu;
+                        tmx = max(tmx, max(lo, hi));
+                        tmn = min(tmn, min(lo - 1u, hi - 1u));
+                    } else {
+                        const uint32_t a = w[jj] & 0x7FFFFFFFu;
+                        tmx = max(tmx, a);
+                        tmn = min(tmn, a - 1u);
+                    }
+                }
+            }
+        }
+    }
+
     for (int i = tid; i < SEG_KR * D; i += NT) acc[i] = 0.0;
     if (tid < SEG_KR) {
         const bool in = tid < nk;
@@ -1274,6 +1313,8 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
         s_misc[0] = 0xFFFFFFFFu;
         s_misc[1] = 0u;
     }
+    tmn = (uint32_t)wave_min_i((int)(tmn ^ 0x80000000u)) ^ 0x80000000u;   // unsigned minimum
+    tmx = wave_max_u(tmx);
     __syncthreads();
     if (wave == 0) {   // exclusive prefix of the run's counts, and their maximum
         const int c = lane < SEG_KR ? s_cnt[lane] : 0;
@@ -1288,36 +1329,9 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
         const uint32_t cm = wave_max_u((uint32_t)c);
         if (lane == 0) s_misc[2] = cm;
     }
-    if (xstats) {   // magnitudes of the earlier stages' stored tables of this head
-        constexpr int PER = 16 / sizeof(KVT);
-        uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-        const int nv = K * D / PER;
-#pragma unroll 1
-        for (int p = 0; p < src.P; ++p) {
-            const uint4 *tp = reinterpret_cast<const uint4 *>(static_cast<const KVT *>(src.cent[p]) + (size_t)h * K * D);
-            for (int i = tid; i < nv; i += NT) {
-                const uint4 q = tp[i];
-                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    if constexpr (sizeof(KVT) == 2) {
-                        const uint32_t lo = w[jj] & 0x7FFFu, hi = (w[jj] >> 16) & 0x7FFFu;
-                        mx = max(mx, max(lo, hi));
-                        mn = min(mn, min(lo - 1u, hi - 1u));
-                    } else {
-                        const uint32_t a = w[jj] & 0x7FFFFFFFu;
-                        mx = max(mx, a);
-                        mn = min(mn, a - 1u);
-                    }
-                }
-            }
-        }
-        mn = (uint32_t)wave_min_i((int)(mn ^ 0x80000000u)) ^ 0x80000000u;   // unsigned minimum
-        mx = wave_max_u(mx);
-        if (lane == 0 && src.P > 0) {
-            atomicMin(&s_misc[0], mn);
-            atomicMax(&s_misc[1], mx);
-        }
+    if (xstats && lane == 0 && src.P > 0) {
+        atomicMin(&s_misc[0], tmn);
+        atomicMax(&s_misc[1], tmx);
     }
     __syncthreads();
     if (tid == 0) {   // the run certificate
@@ -1341,36 +1355,15 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
     }
 
     // 1. the run's tokens, grouped by centroid
-    {
-        // labels of the earlier stages ride along in the list entries; missing
-        // stages read the current labels again and drop them
-        const uint8_t *lab = pi + (size_t)h * pi_hs;
-        const uint8_t *l1 = src.P >= 1 ? src.pi[0] + (size_t)h * src.pi_hs : lab;
-        const uint8_t *l2 = src.P >= 2 ? src.pi[1] + (size_t)h * src.pi_hs : lab;
-        const uint32_t m1 = src.P >= 1 ? 0xFFu : 0u, m2 = src.P >= 2 ? 0xFFu : 0u;
-        constexpr int B = 8;
-        for (int n0 = 0; n0 < N; n0 += NT * B) {
-            uint32_t k[B], a[B], b[B];
+    for (int n0 = 0; n0 < N; n0 += NT * B) {
+        if (n0 > 0) label_batch(n0);
 #pragma unroll
-            for (int i = 0; i < B; ++i) {   // unconditional loads, all in flight together
-                const int n = min(n0 + i * NT + tid, N - 1);
-                k[i] = lab[n];
-                a[i] = l1[n];
-                b[i] = l2[n];
-            }
-#pragma unroll
-            for (int i = 0; i < B; ++i) {
-                k[i] = n0 + i * NT + tid < N ? k[i] - (uint32_t)k0 : 0xFFFFFFFFu;
-                a[i] &= m1;
-                b[i] &= m2;
-            }
-#pragma unroll
-            for (int i = 0; i < B; ++i) {
-                if (k[i] < (uint32_t)nk) {
-                    const int pos = atomicAdd(&s_fill[k[i]], 1);
-                    if (pos < s_cnt[k[i]])   // always, with counts taken from these labels
-                        list[s_off[k[i]] + pos] = (uint32_t)(n0 + i * NT + tid) | (a[i] << 16) | (b[i] << 24);
-                }
+        for (int i = 0; i < B; ++i) {
+            const uint32_t k = n0 + i * NT + tid < N ? lk[i] - (uint32_t)k0 : 0xFFFFFFFFu;
+            if (k < (uint32_t)nk) {
+                const int pos = atomicAdd(&s_fill[k], 1);
+                if (pos < s_cnt[k])   // always, with counts taken from these labels
+                    list[s_off[k] + pos] = (uint32_t)(n0 + i * NT + tid) | ((la[i] & m1) << 16) | ((lb[i] & m2) << 24);
             }
         }
     }
@@ -1441,14 +1434,9 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
                 for (int c = 0; c < CPL; ++c) mean[c] = mean_of(hs[c] + es[c], cnt);
             }
         }
-        double sq = 0.0;
         uint32_t bb[CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            bb[c] = f32_to_bf16(mean[c]);
-            const double bd = (double)bf16_to_f32(bb[c]);
-            sq += bd * bd;
-        }
+        for (int c = 0; c < CPL; ++c) bb[c] = f32_to_bf16(mean[c]);
         float *cr = C + ((size_t)h * K + k) * D + lane * CPL;
         uint16_t *br = Cb + ((size_t)h * Kp + k) * D + lane * CPL;
         if constexpr (CPL == 2) {
@@ -1458,8 +1446,6 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
             cr[0] = mean[0];
             br[0] = (uint16_t)bb[0];
         }
-        sq = wave_sum(sq);
-        if (lane == 0) cnorm[(size_t)h * Kp + k] = sq;
     }
 }
 
@@ -1469,7 +1455,7 @@ size_t value_stats_words(int H) { return (size_t)H * VSTAT_BLOCKS * 2; }
 
 hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &src, const uint8_t *pi,
                              int64_t pi_hs, const int32_t *counts, const uint32_t *xstats, float *C, uint16_t *Cb,
-                             double *cnorm, int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s) {
+                             int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s) {
     if (!update_seg_fits(N)) return hipErrorInvalidValue;
     const int Kp = padded_k(K);
     const int64_t nb = (int64_t)H * ((K + SEG_KR - 1) / SEG_KR);
@@ -1479,7 +1465,7 @@ hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &s
         (void)hipFuncSetAttribute((const void *)k_update_seg<DD, KVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
         QVG_KERNEL((k_update_seg<DD, KVT>), dim3((unsigned)nb), dim3(64 * SEG_WAVES), lds, s, src, H, N, K, Kp, pi,
-                   pi_hs, counts, xstats, C, Cb, cnorm, zero_cnt, zero_fill);
+                   pi_hs, counts, xstats, C, Cb, zero_cnt, zero_fill);
     });
     return hipGetLastError();
 }

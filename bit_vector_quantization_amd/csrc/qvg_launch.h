@@ -34,19 +34,18 @@ struct Src {
 hipError_t launch_forgy(int T, int H, int N, int K, uint64_t seed, int32_t *idx, hipStream_t s);
 
 // Starting centroids from fp32 `warm` [H][K][D] (when non-null) or from the rows
-// idx[h][k] of R(t-1).  Writes C fp32 [H][K][D], Cb bf16 [H][Kp][D] (padding
-// rows zero), cnorm = |Cb|^2 fp64 [H][Kp] (padding +inf) and zeroes cnt0 and
-// fill0 [H][Kp] (non-null) for the first histogram.
+// idx[h][k] of R(t-1).  Writes C fp32 [H][K][D] and Cb bf16 [H][Kp][D] (padding
+// rows zero), and zeroes cnt0 and fill0 [H][Kp] (non-null) for the first
+// histogram.
 hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src, const int32_t *idx,
-                                 const float *warm, float *C, uint16_t *Cb, double *cnorm, int32_t *cnt0,
-                                 int32_t *fill0, hipStream_t s);
+                                 const float *warm, float *C, uint16_t *Cb, int32_t *cnt0, int32_t *fill0,
+                                 hipStream_t s);
 
-// pi[h][n] = argmin_k cnorm[k] - 2 <bf16(R(t-1)[h][n]), Cb[h][k]>: bf16 MFMA with
-// fp32 accumulation ranks the centroids, the best two are re-decided exactly
-// in fp64.  counts (non-null) [H][Kp] += tokens per centroid.
-hipError_t launch_assign(int D, int dtype, int H, int N, const Src &src, const uint16_t *Cb,
-                         const double *cnorm, int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts,
-                         hipStream_t s);
+// pi[h][n] = argmin_{k < K} |Cb[h][k]|^2 - 2 <bf16(R(t-1)[h][n]), Cb[h][k]>: bf16
+// MFMA with fp32 accumulation ranks the centroids, the best two are re-decided
+// exactly in fp64.  counts (non-null) [H][Kp] += tokens per centroid.
+hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, const uint16_t *Cb, uint8_t *pi,
+                         int64_t pi_hs, int32_t *counts, hipStream_t s);
 
 // Histogram of an assignment (counts must be zero on entry).
 hipError_t launch_count(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, int32_t *counts,
@@ -59,12 +58,12 @@ hipError_t launch_scatter(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs
                           int32_t *fill, int32_t *offsets, int32_t *order, hipStream_t s);
 
 // Every centroid with tokens becomes the exactly summed mean of their rows of
-// R(t-1) (rounded once to fp64, divided by the count, rounded to fp32); C, Cb
-// and cnorm are refreshed for those centroids.  zero_cnt / zero_fill
-// (non-null) [H][Kp] are cleared for the next round.
+// R(t-1) (rounded once to fp64, divided by the count, rounded to fp32); C and
+// Cb are refreshed for those centroids.  zero_cnt / zero_fill (non-null)
+// [H][Kp] are cleared for the next round.
 hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, const int32_t *counts,
-                         const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb, double *cnorm,
-                         int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s);
+                         const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb, int32_t *zero_cnt,
+                         int32_t *zero_fill, hipStream_t s);
 
 // The same update without a global sort (k_update_seg): each workgroup lists the
 // tokens of a run of centroids in LDS from pi (uint8, head stride pi_hs, the
@@ -78,7 +77,7 @@ hipError_t launch_value_stats(int dtype, int H, const void *x, int64_t x_hs, int
                               hipStream_t s);
 hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &src, const uint8_t *pi,
                              int64_t pi_hs, const int32_t *counts, const uint32_t *xstats, float *C, uint16_t *Cb,
-                             double *cnorm, int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s);
+                             int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s);
 
 // dst_slice [H][K][D] = C rounded to dtype; cache_slice [H][K][D] = C (if non-null).
 hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype, void *dst_slice,
