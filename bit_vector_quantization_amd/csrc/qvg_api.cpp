@@ -356,7 +356,11 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
     const bool need_draw = !init_centroids && !warm_cache;
     if (need_draw) QVG_LAUNCH("forgy", 0, (double)T * H * K * 4, launch_forgy(T, H, N, K, cfg->seed, idx, s));
 
-    if (update_seg_fits(N))
+    // the exactness certificate of the update needs the input's value statistics:
+    // the first assign gathers them for bf16 tensors, a pass of their own otherwise
+    const bool seg = update_seg_fits(N);
+    const bool stats_in_assign = seg && cfg->dtype == QVG_BF16;
+    if (seg && !stats_in_assign)
         QVG_LAUNCH("value_stats", 0, HND * esz, launch_value_stats(cfg->dtype, H, x, x_head_stride, (int64_t)N * D,
                                                                    vstats, s));
 
@@ -375,12 +379,13 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
         const double assign_flops = 2.0 * H * N * K * D;
         QVG_LAUNCH("init_centroids", 0, (double)H * K * D * (esz + 4) + table,
                    launch_init_centroids(D, cfg->dtype, H, K, src, idx + (size_t)(t - 1) * H * K, warm, C, Cb,
-                                         cnt[0], fill[0], s));
+                                         cnt[0], fill[0], t == 1 && stats_in_assign ? vstats : nullptr, s));
         for (int it = 0; it < iters; ++it) {
             const int c = it & 1;
             QVG_LAUNCH("assign", assign_flops, row_bytes + H * N + table,
-                       launch_assign(D, cfg->dtype, H, N, K, src, Cb, pi, cap, cnt[c], s));
-            if (update_seg_fits(N)) {
+                       launch_assign(D, cfg->dtype, H, N, K, src, Cb, pi, cap, cnt[c],
+                                     t == 1 && it == 0 && stats_in_assign ? vstats : nullptr, s));
+            if (seg) {
                 QVG_LAUNCH("update", HND, row_bytes + H * N + (double)H * K * D * 4 + table,
                            launch_update_seg(D, cfg->dtype, H, N, K, src, pi, cap, cnt[c], vstats, C, Cb,
                                              cnt[c ^ 1], fill[c ^ 1], s));
@@ -393,7 +398,7 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
             }
         }
         QVG_LAUNCH("assign", assign_flops, row_bytes + H * N + table,
-                   launch_assign(D, cfg->dtype, H, N, K, src, Cb, pi, cap, nullptr, s));
+                   launch_assign(D, cfg->dtype, H, N, K, src, Cb, pi, cap, nullptr, nullptr, s));
         void *cslot = static_cast<char *>(dst->centroids) +
                       (((size_t)chunk_index * T + (t - 1)) * H * K * D) * esz;
         QVG_LAUNCH("store_centroids", 0, (double)H * K * D * (4 + esz + (cache ? 4 : 0)),
@@ -478,11 +483,11 @@ qvg_status qvg_kmeans_assign(const void *x, int32_t x_dtype, int64_t x_head_stri
     const double table = (double)heads * Kp * d * 2;
     QVG_LAUNCH("init_centroids", 0, (double)heads * n_centroids * d * 8 + table,
                launch_init_centroids(d, x_dtype, heads, n_centroids, src, nullptr, centroids, C, Cb, nullptr,
-                                     nullptr, s));
+                                     nullptr, nullptr, s));
     QVG_LAUNCH("assign", 2.0 * heads * n_tokens * n_centroids * d,
                (double)heads * n_tokens * (d * dtype_size(x_dtype) + 1) + table,
                launch_assign(d, x_dtype, heads, n_tokens, n_centroids, src, Cb, assign_out, assign_head_stride, nullptr,
-                             s));
+                             nullptr, s));
     return QVG_OK;
 }
 

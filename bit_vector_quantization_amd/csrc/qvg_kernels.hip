@@ -89,6 +89,39 @@ __device__ __forceinline__ double wave_sum(double v) {
     return v;
 }
 
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+    return v;
+}
+
+// v plus its value in the lane that the DPP control CTRL selects (all lanes valid).
+template <int CTRL>
+__device__ __forceinline__ double dpp_add(double v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+    return v + __hiloint2double(hi, lo);
+}
+
+// Sum over aligned groups of L = 8 or 16 lanes, in every lane of the group, by
+// DPP moves: lane swaps within quads (xor 1, xor 2), then the mirror within
+// each half row (8 lanes) and, for 16, within the row.
+template <int L>
+__device__ __forceinline__ double group_sum(double v) {
+    static_assert(L == 8 || L == 16, "groups of 8 or 16 lanes");
+    v = dpp_add<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+    v = dpp_add<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+    v = dpp_add<0x141>(v);   // row_half_mirror
+    if constexpr (L == 16) v = dpp_add<0x140>(v);   // row_mirror
+    return v;
+}
+
 // Blocks are dispatched round-robin over the 8 XCDs; give each XCD one
 // contiguous range of logical tiles so that neighbouring tiles share its L2.
 __device__ __forceinline__ uint32_t xcd_tile(uint32_t bid, uint32_t nblocks) {
@@ -206,52 +239,39 @@ __device__ __forceinline__ uint64_t splitmix64_at(uint64_t key, uint64_t i) {
     return z ^ (z >> 31);
 }
 
-constexpr int FORGY_TABLE = 256;   // K <= 256 steps, at most one new displaced position each
+constexpr int FORGY_TABLE = 256;   // K <= 256 steps
 
-// One wave per (head, stage).  Step i of the shuffle swaps a[i] with a[j_i],
-// j_i = i + r_i mod (N - i).  The draws are independent of the shuffle, so the
-// wave computes all j_i at once; the swaps then run in order, keeping only the
-// displaced positions in a small LDS table searched by the whole wave.
-__global__ __launch_bounds__(64) void k_forgy(int H, int N, int K, uint64_t seed, int32_t *idx) {
-    __shared__ int32_t keys[FORGY_TABLE];
-    __shared__ int32_t vals[FORGY_TABLE];
-    __shared__ int32_t sel[FORGY_TABLE];
+// One workgroup per (head, stage).  Step i of the shuffle swaps a[i] with
+// a[j_i], j_i = i + r_i mod (N - i), and position i is final after step i, so
+// entry i is the value at position j_i once steps 0 .. i-1 are done.  The draws
+// do not depend on the shuffle: all j_i are computed at once, and thread i
+// finds its entry by undoing steps i-1 .. 0 on the position j_i (a swap of m
+// and j_m maps m to j_m and j_m to m); the position it ends at is the value,
+// since the shuffle starts from the identity.
+__global__ __launch_bounds__(FORGY_TABLE) void k_forgy(int H, int N, int K, uint64_t seed, int32_t *idx) {
     __shared__ int32_t jv[FORGY_TABLE];
-    const int h = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+    __shared__ int32_t sel[FORGY_TABLE];
+    const int h = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
     const uint64_t key = (seed * 65536ull + (uint64_t)h) * 64ull + (uint64_t)(t + 1);
     const int steps = K < N ? K : N;
-    for (int i = lane; i < steps; i += 64) jv[i] = i + (int)(splitmix64_at(key, (uint64_t)i) % (uint64_t)(N - i));
+    if (tid < steps) jv[tid] = tid + (int)(splitmix64_at(key, (uint64_t)tid) % (uint64_t)(N - tid));
     __syncthreads();
-    int n_ent = 0;
-    for (int i = 0; i < steps; ++i) {
-        const int j = jv[i];
-        int vi_l = i, vj_l = j, ej_l = -1;
-        bool fi = false, fj = false;
-        for (int e = lane; e < n_ent; e += 64) {
-            const int kk = keys[e];
-            if (kk == i) { vi_l = vals[e]; fi = true; }
-            if (kk == j) { vj_l = vals[e]; ej_l = e; fj = true; }
+    if (tid < steps) {
+        int p = jv[tid];
+        for (int m = tid - 1; m >= 0; --m) {
+            const int jm = jv[m];
+            p = p == m ? jm : (p == jm ? m : p);
         }
-        const uint64_t mi = __ballot(fi), mj = __ballot(fj);
-        const int vi = mi ? __shfl(vi_l, __ffsll((long long)mi) - 1) : i;
-        const int vj = mj ? __shfl(vj_l, __ffsll((long long)mj) - 1) : j;
-        const int ej = mj ? __shfl(ej_l, __ffsll((long long)mj) - 1) : -1;
-        __syncthreads();
-        if (lane == 0) {
-            sel[i] = vj;                      // position i is final after step i
-            if (ej >= 0) vals[ej] = vi;       // a[j] = old a[i]
-            else { keys[n_ent] = j; vals[n_ent] = vi; }
-        }
-        if (ej < 0) ++n_ent;
-        __syncthreads();
+        sel[tid] = p;
     }
+    __syncthreads();
     // fewer tokens than centroids: entry k repeats entry k mod N
     int32_t *out = idx + ((size_t)t * H + h) * K;
-    for (int k = lane; k < K; k += 64) out[k] = sel[k < steps ? k : k % N];
+    if (tid < K) out[tid] = sel[tid < steps ? tid : tid % N];
 }
 
 hipError_t launch_forgy(int T, int H, int N, int K, uint64_t seed, int32_t *idx, hipStream_t s) {
-    QVG_KERNEL(k_forgy, dim3(H, T), dim3(64), 0, s, H, N, K, seed, idx);
+    QVG_KERNEL(k_forgy, dim3(H, T), dim3(FORGY_TABLE), 0, s, H, N, K, seed, idx);
     return hipGetLastError();
 }
 
@@ -277,8 +297,11 @@ __device__ __forceinline__ void write_centroid8(int h, int k, int K, int Kp, int
 
 template <int D, typename KVT>
 __global__ __launch_bounds__(64) void k_init_centroids(int K, int Kp, Src src, const int32_t *idx, const float *warm,
-                                                       float *C, uint16_t *Cb, int32_t *cnt0, int32_t *fill0) {
+                                                       float *C, uint16_t *Cb, int32_t *cnt0, int32_t *fill0,
+                                                       uint32_t *vstats_clear) {
     const int k = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+    if (vstats_clear && k == 0 && lane < 2 * VSTAT_BLOCKS)   // neutral value statistics
+        vstats_clear[(size_t)h * 2 * VSTAT_BLOCKS + lane] = (lane & 1) ? 0u : 0xFFFFFFFFu;
     if (lane == 0 && cnt0) {
         cnt0[(size_t)h * Kp + k] = 0;
         fill0[(size_t)h * Kp + k] = 0;
@@ -297,11 +320,11 @@ __global__ __launch_bounds__(64) void k_init_centroids(int K, int Kp, Src src, c
 
 hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src, const int32_t *idx,
                                  const float *warm, float *C, uint16_t *Cb, int32_t *cnt0, int32_t *fill0,
-                                 hipStream_t s) {
+                                 uint32_t *vstats_clear, hipStream_t s) {
     const int Kp = padded_k(K);
     QVG_DISPATCH_DT(D, dtype,
                     QVG_KERNEL((k_init_centroids<DD, KVT>), dim3(Kp, H), dim3(64), 0, s, K, Kp, src, idx,
-                                       warm, C, Cb, cnt0, fill0));
+                                       warm, C, Cb, cnt0, fill0, vstats_clear));
     return hipGetLastError();
 }
 
@@ -614,7 +637,8 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
 template <int D, typename KVT, bool ANYP>
 __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H, int N, const uint16_t *__restrict__ Cb,
                                                                  int K, int Kp, uint8_t *__restrict__ pi,
-                                                                 int64_t pi_hs, int32_t *__restrict__ counts) {
+                                                                 int64_t pi_hs, int32_t *__restrict__ counts,
+                                                                 uint32_t *__restrict__ vstats) {
     constexpr int CH = D / 8;
     constexpr int NT = 64 * ASSIGN_WAVES;
     constexpr int STAGE = (256 * CH + NT - 1) / NT;   // table chunks per thread at 256 centroids
@@ -661,8 +685,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
                     sq = fma(lo, lo, sq);
                     sq = fma(hi, hi, sq);
                 }
-#pragma unroll
-                for (int o = 1; o < CH; o <<= 1) sq += __shfl_xor(sq, o);
+                sq = group_sum<CH>(sq);
                 if (q == 0 && i < nch) {
                     const bool real = row < K;   // padding rows are never chosen
                     lcn64[sl * Kp + row] = real ? sq : __builtin_inf();
@@ -681,6 +704,30 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
             const int tok0 = (m - h * T) * TILE;
             bf16x8_t bt[ASSIGN_TB][D / 32];
             assign_load<D, KVT, ANYP>(src, h, N, tok0, bt);
+            if constexpr (!ANYP) {
+                if (vstats) {   // the input's value statistics, from the operands (bf16 input, first stage)
+                    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+                    for (int b = 0; b < ASSIGN_TB; ++b)
+#pragma unroll
+                        for (int ks = 0; ks < D / 32; ++ks) {
+                            const uint4 q = __builtin_bit_cast(uint4, bt[b][ks]);
+                            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj) {
+                                const uint32_t lo = w[jj] & 0x7FFFu, hi = (w[jj] >> 16) & 0x7FFFu;
+                                mx = max(mx, max(lo, hi));
+                                mn = min(mn, min(lo - 1u, hi - 1u));   // zero wraps to the largest value
+                            }
+                        }
+                    mn = (uint32_t)wave_min_i((int)(mn ^ 0x80000000u)) ^ 0x80000000u;   // unsigned minimum
+                    mx = wave_max_u(mx);
+                    if (lane == 0) {
+                        atomicMin(&vstats[(size_t)h * 2 * VSTAT_BLOCKS], mn);
+                        atomicMax(&vstats[(size_t)h * 2 * VSTAT_BLOCKS + 1], mx);
+                    }
+                }
+            }
             assign_wave<D, KVT>(src, h, N, tok0, bt, lds + sl * nch, lcn64 + sl * Kp, lhcn + sl * Kp,
                                 lists + wave * TILE, Kp, pi, pi_hs, counts);
         }
@@ -702,7 +749,7 @@ static int device_cus() {
 }
 
 hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, const uint16_t *Cb, uint8_t *pi,
-                         int64_t pi_hs, int32_t *counts, hipStream_t s) {
+                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, hipStream_t s) {
     const int Kp = padded_k(K);
     const size_t lds = 2 * ((size_t)Kp * D * 2 + (size_t)Kp * 12) + (ASSIGN_WAVES * TILE + 4) * sizeof(int32_t);
     // one resident workgroup per CU, at least a tile per wave
@@ -717,12 +764,13 @@ hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, 
         if (anyp || sizeof(KVT) != 2) {
             (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT, true>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            QVG_KERNEL((k_assign<DD, KVT, true>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts);
+            QVG_KERNEL((k_assign<DD, KVT, true>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts,
+                       (uint32_t *)nullptr);
         } else {
             using KB = uint16_t;   // (this branch is only taken for bf16)
             (void)hipFuncSetAttribute((const void *)k_assign<DD, KB, false>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            QVG_KERNEL((k_assign<DD, KB, false>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts);
+            QVG_KERNEL((k_assign<DD, KB, false>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts, vstats);
         }
     });
     return hipGetLastError();
@@ -994,7 +1042,6 @@ constexpr int SEG_KR = 32;          // centroids per workgroup
 constexpr int SEG_WAVES = 8;
 constexpr int SEG_U = 8;            // rows in flight per wave
 constexpr int SEG_EMPTY_E = 4096;   // lowest-bit exponent of a centroid with only zeros so far
-constexpr int VSTAT_BLOCKS = 8;     // partial statistics per head from k_value_stats
 
 // Smallest nonzero and largest magnitude bits (bf16: 15 bits, fp32: 31 bits) of
 // each head's count values, as VSTAT_BLOCKS partial pairs per head:
@@ -1147,18 +1194,6 @@ __device__ __forceinline__ void seg_rows(const Src &s, int h, int N, const uint3
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int i = 0; i < CPL; ++i) v[u][i] = u < m ? v[u][i] : 0.f;
-}
-
-__device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ __forceinline__ uint32_t wave_max_u(uint32_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-    return v;
 }
 
 template <int D>
@@ -1503,7 +1538,8 @@ hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype
 // One thread owns 16 consecutive channels of one token; the G/16 threads of a
 // group are adjacent lanes and combine their maxima with lane shuffles.
 
-template <int D, typename KVT, bool CENT>
+// PM: the number of earlier stages when it is 0 or 1, else 2 (any number).
+template <int D, typename KVT, bool CENT, int PM>
 __global__ __launch_bounds__(256) void k_quant(Src src, int N, const KVT *cent, int cent_rows, const uint8_t *pi,
                                                int64_t pi_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap, int G) {
     constexpr int SL = D / 16;
@@ -1513,19 +1549,36 @@ __global__ __launch_bounds__(256) void k_quant(Src src, int N, const KVT *cent, 
     const int n = blockIdx.x * TPB + threadIdx.x / SL;
     if (n >= N) return;   // whole groups leave together (SL divides 64)
     float r[16];
-    {
+    if constexpr (PM <= 1) {
+        // every label first, then every row: two dependent reads in all
+        const KVT *xr = static_cast<const KVT *>(src.x) + (size_t)h * src.x_hs + (size_t)n * D + 16 * j;
+        const int k1 = PM == 1 ? (int)src.pi[0][(size_t)h * src.pi_hs + n] : 0;
+        const int kt = CENT ? (int)pi[(size_t)h * pi_hs + n] : 0;
+        load16<KVT>(xr, r);
+        float c1[16], ct[16];
+        if constexpr (PM == 1) load16<KVT>(static_cast<const KVT *>(src.cent[0]) + ((size_t)h * src.K + k1) * D + 16 * j, c1);
+        if constexpr (CENT) load16<KVT>(cent + ((size_t)h * cent_rows + kt) * D + 16 * j, ct);
+        if constexpr (PM == 1) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) r[i] = r[i] - c1[i];
+        }
+        if constexpr (CENT) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) r[i] = r[i] - ct[i];
+        }
+    } else {
         float a[8], b[8];
         src_row8<D, KVT>(src, h, n, 16 * j, a);
         src_row8<D, KVT>(src, h, n, 16 * j + 8, b);
 #pragma unroll
         for (int i = 0; i < 8; ++i) { r[i] = a[i]; r[8 + i] = b[i]; }
-    }
-    if constexpr (CENT) {
-        const int k = pi[(size_t)h * pi_hs + n];
-        float c[16];
-        load16<KVT>(cent + ((size_t)h * cent_rows + k) * D + 16 * j, c);
+        if constexpr (CENT) {
+            const int k = pi[(size_t)h * pi_hs + n];
+            float c[16];
+            load16<KVT>(cent + ((size_t)h * cent_rows + k) * D + 16 * j, c);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) r[i] = r[i] - c[i];
+            for (int i = 0; i < 16; ++i) r[i] = r[i] - c[i];
+        }
     }
     float a = 0.f;
 #pragma unroll
@@ -1550,14 +1603,20 @@ hipError_t launch_quant(int D, int dtype, int H, int N, const Src &src, const vo
                         hipStream_t s) {
     const int TPB = 256 / (D / 16);
     dim3 g((N + TPB - 1) / TPB, H), b(256);
+#define QVG_QUANT_LAUNCH(CE, PMV)                                                                            \
+    QVG_KERNEL((k_quant<DD, KVT, CE, PMV>), g, b, 0, s, src, N, (const KVT *)cent, cent_rows, pi, pi_hs, codes, \
+               scales, q_cap, G)
     QVG_DISPATCH_DT(D, dtype, {
-        if (cent)
-            QVG_KERNEL((k_quant<DD, KVT, true>), g, b, 0, s, src, N, (const KVT *)cent, cent_rows, pi, pi_hs,
-                               codes, scales, q_cap, G);
-        else
-            QVG_KERNEL((k_quant<DD, KVT, false>), g, b, 0, s, src, N, (const KVT *)nullptr, 0, pi, pi_hs,
-                               codes, scales, q_cap, G);
+        if (cent) {
+            if (src.P == 0) QVG_QUANT_LAUNCH(true, 0);
+            else if (src.P == 1) QVG_QUANT_LAUNCH(true, 1);
+            else QVG_QUANT_LAUNCH(true, 2);
+        } else {
+            if (src.P == 0) QVG_QUANT_LAUNCH(false, 0);
+            else QVG_QUANT_LAUNCH(false, 2);
+        }
     });
+#undef QVG_QUANT_LAUNCH
     return hipGetLastError();
 }
 

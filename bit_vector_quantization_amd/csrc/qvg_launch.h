@@ -33,19 +33,25 @@ struct Src {
 // Cold start: indices [T][H][K] of the Forgy rows of every (stage, head).
 hipError_t launch_forgy(int T, int H, int N, int K, uint64_t seed, int32_t *idx, hipStream_t s);
 
+// Per-head value statistics (see launch_value_stats): VSTAT_BLOCKS partial
+// pairs {smallest nonzero magnitude - 1, largest magnitude} per head.
+constexpr int VSTAT_BLOCKS = 8;
+
 // Starting centroids from fp32 `warm` [H][K][D] (when non-null) or from the rows
 // idx[h][k] of R(t-1).  Writes C fp32 [H][K][D] and Cb bf16 [H][Kp][D] (padding
-// rows zero), and zeroes cnt0 and fill0 [H][Kp] (non-null) for the first
-// histogram.
+// rows zero), zeroes cnt0 and fill0 [H][Kp] (non-null) for the first
+// histogram, and sets vstats_clear (non-null) to neutral value statistics.
 hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src, const int32_t *idx,
                                  const float *warm, float *C, uint16_t *Cb, int32_t *cnt0, int32_t *fill0,
-                                 hipStream_t s);
+                                 uint32_t *vstats_clear, hipStream_t s);
 
 // pi[h][n] = argmin_{k < K} |Cb[h][k]|^2 - 2 <bf16(R(t-1)[h][n]), Cb[h][k]>: bf16
 // MFMA with fp32 accumulation ranks the centroids, the best two are re-decided
-// exactly in fp64.  counts (non-null) [H][Kp] += tokens per centroid.
+// exactly in fp64.  counts (non-null) [H][Kp] += tokens per centroid.  vstats
+// (non-null; a bf16 tensor without earlier stages only): the input's value
+// statistics are folded into partial 0 of each head (cleared beforehand).
 hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, const uint16_t *Cb, uint8_t *pi,
-                         int64_t pi_hs, int32_t *counts, hipStream_t s);
+                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, hipStream_t s);
 
 // Histogram of an assignment (counts must be zero on entry).
 hipError_t launch_count(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, int32_t *counts,
