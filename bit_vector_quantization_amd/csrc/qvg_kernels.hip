@@ -279,52 +279,50 @@ hipError_t launch_forgy(int T, int H, int N, int K, uint64_t seed, int32_t *idx,
 // centroid rows: C (fp32) and Cb (bf16 operand)
 // ---------------------------------------------------------------------------
 
-// Lanes 0 .. D/8-1 of a wave own 8 channels each of centroid k of head h.
-template <int D>
-__device__ __forceinline__ void write_centroid8(int h, int k, int K, int Kp, int lane, const float (&v)[8],
-                                                float *C, uint16_t *Cb) {
-    if (lane < D / 8) {
-        uint32_t b[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) b[i] = f32_to_bf16(v[i]);
-        float4 *c = reinterpret_cast<float4 *>(C + ((size_t)h * K + k) * D + lane * 8);
-        c[0] = make_float4(v[0], v[1], v[2], v[3]);
-        c[1] = make_float4(v[4], v[5], v[6], v[7]);
-        *reinterpret_cast<uint4 *>(Cb + ((size_t)h * Kp + k) * D + lane * 8) =
-            make_uint4(b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16));
-    }
-}
-
+// Starting centroids: D/8 threads per row (8 channels each), 256 threads per
+// block, rows in (head, row) order over the padded tables.
 template <int D, typename KVT>
-__global__ __launch_bounds__(64) void k_init_centroids(int K, int Kp, Src src, const int32_t *idx, const float *warm,
-                                                       float *C, uint16_t *Cb, int32_t *cnt0, int32_t *fill0,
-                                                       uint32_t *vstats_clear) {
-    const int k = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-    if (vstats_clear && k == 0 && lane < 2 * VSTAT_BLOCKS)   // neutral value statistics
-        vstats_clear[(size_t)h * 2 * VSTAT_BLOCKS + lane] = (lane & 1) ? 0u : 0xFFFFFFFFu;
-    if (lane == 0 && cnt0) {
+__global__ __launch_bounds__(256) void k_init_centroids(int H, int K, int Kp, Src src, const int32_t *idx,
+                                                        const float *warm, float *C, uint16_t *Cb, int32_t *cnt0,
+                                                        int32_t *fill0, uint32_t *vstats_clear) {
+    constexpr int TPR = D / 8;
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t rowg = g / TPR;
+    if (rowg >= (int64_t)H * Kp) return;
+    const int j = (int)(g - rowg * TPR);
+    const int h = (int)(rowg / Kp), k = (int)(rowg - (int64_t)h * Kp);
+    if (vstats_clear && k == 0 && j < 2 * VSTAT_BLOCKS)   // neutral value statistics
+        vstats_clear[(size_t)h * 2 * VSTAT_BLOCKS + j] = (j & 1) ? 0u : 0xFFFFFFFFu;
+    if (j == 0 && cnt0) {
         cnt0[(size_t)h * Kp + k] = 0;
         fill0[(size_t)h * Kp + k] = 0;
     }
+    uint4 *cb = reinterpret_cast<uint4 *>(Cb + ((size_t)h * Kp + k) * D + j * 8);
     if (k >= K) {  // padding rows (the assign never chooses them)
-        if (lane < D / 8) *reinterpret_cast<uint4 *>(Cb + ((size_t)h * Kp + k) * D + lane * 8) = make_uint4(0, 0, 0, 0);
+        *cb = make_uint4(0, 0, 0, 0);
         return;
     }
-    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (lane < D / 8) {
-        if (warm) load8<float>(warm + ((size_t)h * K + k) * D + lane * 8, v);
-        else src_row8<D, KVT>(src, h, idx[(size_t)h * K + k], lane * 8, v);
-    }
-    write_centroid8<D>(h, k, K, Kp, lane, v, C, Cb);
+    float v[8];
+    if (warm) load8<float>(warm + ((size_t)h * K + k) * D + j * 8, v);
+    else src_row8<D, KVT>(src, h, idx[(size_t)h * K + k], j * 8, v);
+    uint32_t bb[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bb[i] = f32_to_bf16(v[i]);
+    float4 *c = reinterpret_cast<float4 *>(C + ((size_t)h * K + k) * D + j * 8);
+    c[0] = make_float4(v[0], v[1], v[2], v[3]);
+    c[1] = make_float4(v[4], v[5], v[6], v[7]);
+    *cb = make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16), bb[6] | (bb[7] << 16));
 }
 
 hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src, const int32_t *idx,
                                  const float *warm, float *C, uint16_t *Cb, int32_t *cnt0, int32_t *fill0,
                                  uint32_t *vstats_clear, hipStream_t s) {
     const int Kp = padded_k(K);
+    const int64_t threads = (int64_t)H * Kp * (D / 8);
+    if ((threads + 255) / 256 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     QVG_DISPATCH_DT(D, dtype,
-                    QVG_KERNEL((k_init_centroids<DD, KVT>), dim3(Kp, H), dim3(64), 0, s, K, Kp, src, idx,
-                                       warm, C, Cb, cnt0, fill0, vstats_clear));
+                    QVG_KERNEL((k_init_centroids<DD, KVT>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                               H, K, Kp, src, idx, warm, C, Cb, cnt0, fill0, vstats_clear));
     return hipGetLastError();
 }
 
@@ -1509,25 +1507,30 @@ hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &s
 // stored centroids and the streaming cache
 // ---------------------------------------------------------------------------
 
-template <int D>
-__global__ __launch_bounds__(64) void k_store_centroids(int K, const float *C, int dtype, void *dst, float *cache) {
-    constexpr int P = D / 64;
-    const int k = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-    const size_t off = ((size_t)h * K + k) * D + lane * P;
-#pragma unroll
-    for (int i = 0; i < P; ++i) {
-        const float v = C[off + i];
-        if (dtype == DT_BF16) reinterpret_cast<uint16_t *>(dst)[off + i] = (uint16_t)f32_to_bf16(v);
-        else reinterpret_cast<float *>(dst)[off + i] = v;
-        if (cache) cache[off + i] = v;
+// Eight consecutive values per thread over the H K D values.
+__global__ __launch_bounds__(256) void k_store_centroids(int64_t n8, const float *C, int dtype, void *dst,
+                                                         float *cache) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= n8) return;
+    const float4 a = reinterpret_cast<const float4 *>(C)[2 * g], b = reinterpret_cast<const float4 *>(C)[2 * g + 1];
+    if (dtype == DT_BF16) {
+        reinterpret_cast<uint4 *>(dst)[g] = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
+                                                       pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
+    } else {
+        reinterpret_cast<float4 *>(dst)[2 * g] = a;
+        reinterpret_cast<float4 *>(dst)[2 * g + 1] = b;
+    }
+    if (cache) {
+        reinterpret_cast<float4 *>(cache)[2 * g] = a;
+        reinterpret_cast<float4 *>(cache)[2 * g + 1] = b;
     }
 }
 
 hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype, void *dst, float *cache,
                                   hipStream_t s) {
-    dim3 g(K, H), b(64);
-    if (D == 128) QVG_KERNEL(k_store_centroids<128>, g, b, 0, s, K, C, dtype, dst, cache);
-    else QVG_KERNEL(k_store_centroids<64>, g, b, 0, s, K, C, dtype, dst, cache);
+    const int64_t n8 = (int64_t)H * K * D / 8;   // D is a multiple of 8
+    if ((n8 + 255) / 256 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    QVG_KERNEL(k_store_centroids, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, n8, C, dtype, dst, cache);
     return hipGetLastError();
 }
 

@@ -120,3 +120,37 @@ def test_run_twice_is_deterministic():
     a, b = fetch(d1, 0, oc), fetch(d2, 0, oc)
     for k in a:
         np.testing.assert_array_equal(a[k], b[k])
+
+
+def test_tiny_values_need_exact_sums():
+    """bf16 input where channel 5 of one well-separated cluster holds 1, 2^-80
+    and -1 in three tokens and zero in the rest: the exact column sum is 2^-80,
+    while an fp64 sum that adds 1 + 2^-80 first returns 0.  The input's value
+    statistics (gathered by the first assign) must rule out the run-level
+    exactness certificate, so the update sums that cluster exactly; centroids,
+    codes and the decode must equal the oracle's."""
+    say("e2e bf16 input with values 2^80 apart inside one cluster")
+    rng = np.random.default_rng(11)
+    K, N, d = 16, 480, 128
+    centers = oracle.bf16_round(rng.standard_normal((K, d)) * 50).astype(np.float32)
+    lab = np.arange(N) % K
+    X = oracle.bf16_round(centers[lab] + rng.standard_normal((N, d)) * 0.5).astype(np.float32)
+    members = np.nonzero(lab == 3)[0]
+    X[members, 5] = 0.0
+    X[members[:3], 5] = [1.0, 2.0 ** -80, -1.0]
+    X = X.reshape(1, N, d).copy()   # (a fresh head axis: numpy's X[None] has stride 0 there)
+    oc = oracle.CodecConfig(d=d, n_centroids=K, n_stages=1, group_size=64, iters_cold=3, iters_warm=3, seed=5,
+                            dtype="bf16")
+    init = centers.reshape(1, 1, K, d).copy()        # [T][H][K][d]
+    dst, _ = gpu_encode_chunks(oc, X, N, use_cache=False, init=init)
+    ora = oracle.encode_chunk(X, oc, init=init.astype(np.float64))
+    assert abs(float(ora.cache[0, 0, 3, 5])) > 0     # the exact mean is 2^-80 / 30, not 0
+    g = fetch(dst, 0, oc)
+    assert check_chunk_exact(oc, X, g, ora) == 0
+    q = lib()
+    y = to_np(q.decode(gcfg(oc), dst, 0, N, out_dtype="bf16"))
+    np.testing.assert_array_equal(y, oracle.decode(ora, oc.group_size, "bf16"))
+
+
+def check_chunk_exact(oc, X, g, ora):
+    return _check_chunk(oc, X, g, ora, 0, 0, "chunk 0")
