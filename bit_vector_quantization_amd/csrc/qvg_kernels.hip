@@ -1802,15 +1802,21 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, PARTS == 2 ? 8 : 4) void k_decode_
                                                                    const CentT *__restrict__ cent, int64_t cap,
                                                                    int chunk_tokens, int H, int K, int G,
                                                                    int64_t tok_begin, int64_t tok_end,
-                                                                   int64_t c_first, OutT *__restrict__ out,
-                                                                   int64_t out_hs) {
+                                                                   int64_t c_first, int64_t n_units,
+                                                                   OutT *__restrict__ out, int64_t out_hs) {
     constexpr int LPT = D / 8 / PARTS;                        // lanes per token (8 channels each)
     constexpr int CHH = D / PARTS * (int)sizeof(CentT) / 16;  // 16-byte chunks per part of a row
     constexpr int CP8 = 8 * (int)sizeof(CentT) / 16;          // chunks per 8 channels (1 bf16, 2 fp32)
     extern __shared__ uint4 tab[];
-    const int hf = (int)(blockIdx.x % PARTS);
-    const int h = (int)((blockIdx.x / PARTS) % H);
-    const int64_t c = c_first + (blockIdx.x / PARTS) / H;
+    // The PARTS workgroups of one (chunk, head) are 8 apart in dispatch order:
+    // the same XCD, running together, so a code line fetched by one is still in
+    // that XCD's L2 for the other.  Workgroups past the last (chunk, head) of a
+    // grid padded to a multiple of 8 x PARTS have nothing to do.
+    const int hf = (int)((blockIdx.x / 8) % PARTS);
+    const int64_t uu = (int64_t)(blockIdx.x / 8 / PARTS) * 8 + blockIdx.x % 8;
+    if (uu >= n_units) return;
+    const int h = (int)(uu % H);
+    const int64_t c = c_first + uu / H;
     const int tid = threadIdx.x;
     for (int t = 0; t < TT; ++t) {
         const uint4 *src = reinterpret_cast<const uint4 *>(cent + (((size_t)c * TT + t) * H + h) * K * D);
@@ -1872,15 +1878,17 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const size_t tab_bytes = (size_t)a.T * a.K * (a.D / DEC_PARTS) * (a.cent_dtype == DT_BF16 ? 2 : 4);
     if (a.T >= 1 && a.T <= 4 && tab_bytes <= DEC_LDS_MAX) {
         const int64_t c0 = a.tok_begin / a.chunk_tokens, c1 = (a.tok_begin + a.ntok - 1) / a.chunk_tokens;
-        if ((c1 - c0 + 1) * a.H * DEC_PARTS < (int64_t)UINT32_MAX) {
-            dim3 g((unsigned)((c1 - c0 + 1) * a.H * DEC_PARTS)), b(DEC_LDS_THREADS);
+        const int64_t units = (c1 - c0 + 1) * a.H;   // (chunk, head) pairs
+        const int64_t nb = (units + 7) / 8 * 8 * DEC_PARTS;
+        if (nb < (int64_t)UINT32_MAX) {
+            dim3 g((unsigned)nb), b(DEC_LDS_THREADS);
 #define QVG_DECL(DD, CT, OT, TT)                                                                                  \
     do {                                                                                                          \
         (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, CT, OT, TT, DEC_PARTS>,                                     \
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)tab_bytes);                    \
         QVG_KERNEL((k_decode_lds<DD, CT, OT, TT, DEC_PARTS>), g, b, tab_bytes, s, a.codes, a.scales, a.assign,        \
                            (const CT *)a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.G, a.tok_begin,                  \
-                           a.tok_begin + a.ntok, c0, (OT *)a.out, a.out_hs);                                      \
+                           a.tok_begin + a.ntok, c0, units, (OT *)a.out, a.out_hs);                               \
     } while (0)
 #define QVG_DECL_T(DD, CT, OT)                             \
     do {                                                   \

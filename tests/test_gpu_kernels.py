@@ -118,13 +118,19 @@ def _assign_case(rng, which):
         X[0, 5] = C[0, 3]                    # tokens at distance zero from the copies
         X[0, 400] = C[0, 3]
         return X, C, 64
+    if which == "many_heads":
+        # two tiles per head: one workgroup's run spans five heads, taken in
+        # windows of two tables
+        X = oracle.bf16_round(rng.standard_normal((5, 40, 128))).astype(np.float32)
+        C = rng.standard_normal((5, 45, 128)).astype(np.float32)
+        return X, C, 128
     # fewer tokens than centroids, K not a multiple of 16
     X = oracle.bf16_round(rng.standard_normal((2, 37, 128))).astype(np.float32)
     C = rng.standard_normal((2, 45, 128)).astype(np.float32)
     return X, C, 128
 
 
-@pytest.mark.parametrize("which", ["kv", "dups", "small"])
+@pytest.mark.parametrize("which", ["kv", "dups", "small", "many_heads"])
 def test_assign_matches_oracle_within_tie_rule(which):
     say(f"kmeans_assign {which}")
     q = lib()
