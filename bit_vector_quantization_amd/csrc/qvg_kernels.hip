@@ -1006,13 +1006,20 @@ hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, 
 // update, segmented: exact means from a per-workgroup token list in LDS
 // ---------------------------------------------------------------------------
 //
-// One workgroup per (head, run of SEG_KR centroids); the runs of a head are
+// SEG_RUNS workgroups per head, each with a run of at most SEG_KR consecutive
+// centroids that holds about N / SEG_RUNS tokens: centroid k has token share
+// floor(P(k) SEG_RUNS / N), where P(k) = count(0) + ... + count(k - 1) is the
+// place of its first token in label order, and run r starts at the first
+// centroid of share r, moved where needed to keep every run within SEG_KR
+// centroids.  A workgroup takes as long as its run has tokens, so equal token
+// counts keep the workgroups equally busy (fixed runs of 32 centroids differ
+// by up to 1.6x in tokens after a few k-means rounds).  The runs of a head are
 // neighbours in xcd_tile order, so they share one XCD's L2 (the head's
 // assignments and centroid tables).
-//  1. The run's histogram (from the assign) gives each centroid its place in a
-//     token list in LDS; one pass over the head's assignments puts every token
-//     of the run there, with its labels of the first two earlier stages packed
-//     beside it.  No global sort.
+//  1. The head's histogram (from the assign) gives the run and its centroids'
+//     places in a token list in LDS; one pass over the head's assignments puts
+//     every token of the run there, with its labels of the first two earlier
+//     stages packed beside it.  No global sort.
 //  2. The waves split the run's list evenly.  A wave reads one row per load
 //     instruction (64 lanes x D/64 channels, row addresses in scalar
 //     registers), rebuilds R(t-1), and sums in fp64 registers while the rows
@@ -1036,7 +1043,8 @@ hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, 
 //     a certificate is summed again by one wave with the interval test and the
 //     two-sum pass of k_update.
 
-constexpr int SEG_KR = 32;          // centroids per workgroup
+constexpr int SEG_KR = 32;          // centroids per accumulator window
+constexpr int SEG_RUNS = 9;         // workgroups (runs) per head
 constexpr int SEG_WAVES = 8;
 constexpr int SEG_U = 8;            // rows in flight per wave
 constexpr int SEG_EMPTY_E = 4096;   // lowest-bit exponent of a centroid with only zeros so far
@@ -1195,8 +1203,8 @@ __device__ __forceinline__ void seg_rows(const Src &s, int h, int N, const uint3
 }
 
 template <int D>
-constexpr size_t seg_lds_bytes(int N) {
-    return (size_t)SEG_KR * D * 8 + (size_t)(5 * SEG_KR + 1 + 4) * 4 + (size_t)N * 4;
+constexpr size_t seg_lds_bytes(int N, int K) {
+    return (size_t)SEG_KR * D * 8 + (size_t)(K + 3 * SEG_KR + 1 + 8 + SEG_WAVES + SEG_RUNS) * 4 + (size_t)N * 4;
 }
 
 // Phase 2 of k_update_seg for one wave: list entries [beg, end).  CERT: also
@@ -1271,19 +1279,23 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
     constexpr int NT = 64 * SEG_WAVES;
     extern __shared__ double seg_lds[];
     double *acc = seg_lds;                                              // [SEG_KR][D]
-    int32_t *s_cnt = reinterpret_cast<int32_t *>(acc + SEG_KR * D);   // [SEG_KR]
-    int32_t *s_fill = s_cnt + SEG_KR;                                   // [SEG_KR]
-    int32_t *s_emin = s_fill + SEG_KR;                                  // [SEG_KR]
+    // [K + SEG_KR + 1]: s_off[k] is the list offset of centroid k's first token
+    // (relative to the run), so centroid k has s_off[k + 1] - s_off[k] tokens;
+    // while the list is built s_off[k + 1] serves as centroid k's fill cursor
+    // and ends at its next centroid's offset
+    int32_t *s_off = reinterpret_cast<int32_t *>(acc + SEG_KR * D);
+    int32_t *s_emin = s_off + K + SEG_KR + 1;                           // [SEG_KR]
     uint32_t *s_amax = reinterpret_cast<uint32_t *>(s_emin + SEG_KR);  // [SEG_KR] bits of max|v|
-    int32_t *s_off = reinterpret_cast<int32_t *>(s_amax + SEG_KR);     // [SEG_KR + 1]
-    uint32_t *s_misc = reinterpret_cast<uint32_t *>(s_off + SEG_KR + 1);  // table min, table max, max count, run certified
-    uint32_t *list = s_misc + 4;                                        // [N]
+    // table min, table max, max count, run certified, tokens before the run,
+    // tokens of the run, centroids before the run, centroids of the run
+    uint32_t *s_misc = s_amax + SEG_KR;
+    int32_t *s_wsum = reinterpret_cast<int32_t *>(s_misc + 8);         // [SEG_WAVES] scan totals
+    uint32_t *s_rc = reinterpret_cast<uint32_t *>(s_wsum + SEG_WAVES); // [SEG_RUNS] centroids per token share
+    uint32_t *list = s_rc + SEG_RUNS;                                   // [N]
 
-    const int groups = (K + SEG_KR - 1) / SEG_KR;
-    const uint32_t r = xcd_tile(blockIdx.x, gridDim.x);
-    const int h = (int)(r / groups), k0 = (int)(r % groups) * SEG_KR;
+    const uint32_t rb = xcd_tile(blockIdx.x, gridDim.x);
+    const int h = (int)(rb / SEG_RUNS), r = (int)(rb % SEG_RUNS);
     if (h >= H) return;
-    const int nk = min(SEG_KR, K - k0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // The reads that do not depend on the counts are issued first, so that the
@@ -1306,6 +1318,7 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
         }
     };
     label_batch(0);
+    const int cnt_k = counts[(size_t)h * Kp + min(tid, K - 1)];   // (thread k < K holds centroid k)
     uint32_t tmn = 0xFFFFFFFFu, tmx = 0u;   // magnitudes of the earlier stages' stored tables
     if (xstats) {
         constexpr int PER = 16 / sizeof(KVT);
@@ -1332,41 +1345,65 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
         }
     }
 
+    // the head's exclusive prefix P(k), from wave-wide scans of the counts
+    const int ck = tid < K ? cnt_k : 0;
+    int incl = ck;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    if (tid < 8) s_misc[tid] = tid == 0 ? 0xFFFFFFFFu : 0u;
+    if (tid < SEG_RUNS) s_rc[tid] = 0;
     for (int i = tid; i < SEG_KR * D; i += NT) acc[i] = 0.0;
     if (tid < SEG_KR) {
-        const bool in = tid < nk;
-        s_cnt[tid] = in ? counts[(size_t)h * Kp + k0 + tid] : 0;
-        s_fill[tid] = 0;
         s_emin[tid] = SEG_EMPTY_E;
         s_amax[tid] = 0u;
-        if (in && zero_cnt) zero_cnt[(size_t)h * Kp + k0 + tid] = 0;
-        if (in && zero_fill) zero_fill[(size_t)h * Kp + k0 + tid] = 0;
-    }
-    if (tid == 0) {
-        s_misc[0] = 0xFFFFFFFFu;
-        s_misc[1] = 0u;
     }
     tmn = (uint32_t)wave_min_i((int)(tmn ^ 0x80000000u)) ^ 0x80000000u;   // unsigned minimum
     tmx = wave_max_u(tmx);
     __syncthreads();
-    if (wave == 0) {   // exclusive prefix of the run's counts, and their maximum
-        const int c = lane < SEG_KR ? s_cnt[lane] : 0;
-        int x = c;
-#pragma unroll
-        for (int o = 1; o < SEG_KR; o <<= 1) {
-            const int y = __shfl_up(x, o);
-            if (lane >= o) x += y;
-        }
-        if (lane < SEG_KR) s_off[lane] = x - c;
-        if (lane == SEG_KR - 1) s_off[SEG_KR] = x;
-        const uint32_t cm = wave_max_u((uint32_t)c);
-        if (lane == 0) s_misc[2] = cm;
-    }
+    int pk = incl - ck;   // P(tid); thread K holds P(K) = N
+    for (int w = 0; w < wave; ++w) pk += s_wsum[w];
+    // the token share floor(P(k) SEG_RUNS / N) of every centroid, counted per share
+    if (tid < K) atomicAdd(&s_rc[(int)min((int64_t)SEG_RUNS - 1, (int64_t)pk * SEG_RUNS / N)], 1u);
     if (xstats && lane == 0 && src.P > 0) {
         atomicMin(&s_misc[0], tmn);
         atomicMax(&s_misc[1], tmx);
     }
     __syncthreads();
+    // Run boundaries b_0 = 0 <= b_1 <= ... <= b_SEG_RUNS = K (the same in every
+    // workgroup of the head): b_{q+1} is the first centroid of token share
+    // q + 1, moved to keep every run within SEG_KR centroids (no more than
+    // SEG_KR after b_q, and no fewer than the later runs need to hold the rest).
+    int ka = 0, kb = 0;
+    {
+        int t = 0, b = 0;
+        for (int q = 0; q < SEG_RUNS; ++q) {
+            t += (int)s_rc[q];   // centroids whose share is at most q
+            const int lo = K - SEG_KR * (SEG_RUNS - 1 - q);
+            const int nb = q == SEG_RUNS - 1 ? K : max(b, min(b + SEG_KR, max(t, lo)));
+            if (q == r) {
+                ka = b;
+                kb = nb;
+            }
+            b = nb;
+        }
+    }
+    if (ka == kb) return;   // a cluster before this run holds its share of tokens
+    if (tid == ka) s_misc[4] = (uint32_t)pk;   // tokens before the run
+    if (tid == kb) s_misc[5] = (uint32_t)pk;   // tokens up to its end
+    if (tid >= ka && tid < kb) {
+        atomicMax(&s_misc[2], (uint32_t)ck);
+        if (zero_cnt) zero_cnt[(size_t)h * Kp + tid] = 0;
+        if (zero_fill) zero_fill[(size_t)h * Kp + tid] = 0;
+    }
+    __syncthreads();
+    const int p0 = (int)s_misc[4], S = (int)s_misc[5] - p0;   // the run's tokens: [p0, p0 + S) in label order
+    // fill cursors (s_off[k + 1] for centroid k) start at the offsets
+    if (tid < K + SEG_KR) s_off[tid + 1] = tid < ka ? 0 : tid < kb ? pk - p0 : S;
+    if (tid == 0) s_off[0] = 0;
     if (tid == 0) {   // the run certificate
         bool ok = xstats != nullptr;
         if (ok) {
@@ -1386,98 +1423,104 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
         }
         s_misc[3] = ok ? 1u : 0u;
     }
+    __syncthreads();
 
     // 1. the run's tokens, grouped by centroid
     for (int n0 = 0; n0 < N; n0 += NT * B) {
         if (n0 > 0) label_batch(n0);
 #pragma unroll
         for (int i = 0; i < B; ++i) {
-            const uint32_t k = n0 + i * NT + tid < N ? lk[i] - (uint32_t)k0 : 0xFFFFFFFFu;
-            if (k < (uint32_t)nk) {
-                const int pos = atomicAdd(&s_fill[k], 1);
-                if (pos < s_cnt[k])   // always, with counts taken from these labels
-                    list[s_off[k] + pos] = (uint32_t)(n0 + i * NT + tid) | ((la[i] & m1) << 16) | ((lb[i] & m2) << 24);
+            const uint32_t k = n0 + i * NT + tid < N ? lk[i] - (uint32_t)ka : 0xFFFFFFFFu;
+            if (k < (uint32_t)(kb - ka)) {
+                const int pos = atomicAdd(&s_off[ka + k + 1], 1);
+                if (pos < S)   // always, with counts taken from these labels
+                    list[pos] = (uint32_t)(n0 + i * NT + tid) | ((la[i] & m1) << 16) | ((lb[i] & m2) << 24);
             }
         }
     }
     __syncthreads();
 
-    // 2. segmented sums: wave w takes list entries [w per, (w + 1) per)
     const bool run_exact = s_misc[3] != 0u;
     {
-        const int S = s_off[SEG_KR];
-        const int per = (S + SEG_WAVES - 1) / SEG_WAVES;
-        const int beg = min(S, wave * per), end = min(S, beg + per);
-        if (beg < end) {
-            if (run_exact) seg_sums<D, KVT, false>(src, h, N, list, s_off, acc, s_emin, s_amax, beg, end);
-            else seg_sums<D, KVT, true>(src, h, N, list, s_off, acc, s_emin, s_amax, beg, end);
+        // the run's centroids [ka, ka + nk) and their list offsets off[0 .. nk]
+        const int w0 = ka, nk = kb - ka;
+        const int32_t *off = s_off + w0;
+        // 2. segmented sums: wave w takes entries [w per, (w + 1) per) of the window's list
+        {
+            const int W0 = off[0], W1 = off[nk];
+            const int per = (W1 - W0 + SEG_WAVES - 1) / SEG_WAVES;
+            const int beg = min(W1, W0 + wave * per), end = min(W1, beg + per);
+            if (beg < end) {
+                if (run_exact) seg_sums<D, KVT, false>(src, h, N, list, off, acc, s_emin, s_amax, beg, end);
+                else seg_sums<D, KVT, true>(src, h, N, list, off, acc, s_emin, s_amax, beg, end);
+            }
         }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // 3. means: one wave per centroid
-    for (int i = wave; i < nk; i += SEG_WAVES) {
-        const int cnt = s_cnt[i];
-        if (cnt == 0) continue;   // an empty cluster keeps its centroid
-        const int k = k0 + i;
-        const double reach = (double)cnt * (double)__uint_as_float(s_amax[i]);
-        const bool exact = run_exact || reach < ldexp(1.0, min(53 + s_emin[i], 1023));
-        float mean[CPL];
-        if (exact) {
+        // 3. means: one wave per centroid
+        for (int i = wave; i < nk; i += SEG_WAVES) {
+            const int cnt = off[i + 1] - off[i];
+            if (cnt == 0) continue;   // an empty cluster keeps its centroid
+            const int k = w0 + i;
+            const double reach = (double)cnt * (double)__uint_as_float(s_amax[i]);
+            const bool exact = run_exact || reach < ldexp(1.0, min(53 + s_emin[i], 1023));
+            float mean[CPL];
+            if (exact) {
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) mean[c] = mean_of(acc[i * D + lane * CPL + c], cnt);
-        } else {
-            const int a = s_off[i], b = s_off[i + 1];
-            double hs[CPL];
-            float ab[CPL];
+                for (int c = 0; c < CPL; ++c) mean[c] = mean_of(acc[i * D + lane * CPL + c], cnt);
+            } else {
+                const int a = off[i], b = off[i + 1];
+                double hs[CPL];
+                float ab[CPL];
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) { hs[c] = 0.0; ab[c] = 0.f; }
-            for (int j = a; j < b; j += 4) {
-                float v[4][CPL];
-                seg_rows<D, KVT, 4>(src, h, N, list, j, min(4, b - j), v);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int c = 0; c < CPL; ++c) {
-                        hs[c] += (double)v[u][c];
-                        ab[c] += fabsf(v[u][c]);
-                    }
-            }
-            bool ok = cnt <= (1 << 20);
-#pragma unroll
-            for (int c = 0; c < CPL; ++c) {
-                const double bd = (double)ab[c] * (double)cnt * 0x1p-51 + fabs(hs[c]) * 0x1p-50;
-                const float lo = mean_of(hs[c] - bd, cnt), hi = mean_of(hs[c] + bd, cnt);
-                ok = ok && lo == hi;
-                mean[c] = lo;
-            }
-            if (!__all(ok)) {
-                double es[CPL];
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) { hs[c] = 0.0; es[c] = 0.0; }
+                for (int c = 0; c < CPL; ++c) { hs[c] = 0.0; ab[c] = 0.f; }
                 for (int j = a; j < b; j += 4) {
                     float v[4][CPL];
                     seg_rows<D, KVT, 4>(src, h, N, list, j, min(4, b - j), v);
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
 #pragma unroll
-                        for (int c = 0; c < CPL; ++c) two_sum(hs[c], es[c], (double)v[u][c]);
+                        for (int c = 0; c < CPL; ++c) {
+                            hs[c] += (double)v[u][c];
+                            ab[c] += fabsf(v[u][c]);
+                        }
                 }
+                bool ok = cnt <= (1 << 20);
 #pragma unroll
-                for (int c = 0; c < CPL; ++c) mean[c] = mean_of(hs[c] + es[c], cnt);
+                for (int c = 0; c < CPL; ++c) {
+                    const double bd = (double)ab[c] * (double)cnt * 0x1p-51 + fabs(hs[c]) * 0x1p-50;
+                    const float lo = mean_of(hs[c] - bd, cnt), hi = mean_of(hs[c] + bd, cnt);
+                    ok = ok && lo == hi;
+                    mean[c] = lo;
+                }
+                if (!__all(ok)) {
+                    double es[CPL];
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) { hs[c] = 0.0; es[c] = 0.0; }
+                    for (int j = a; j < b; j += 4) {
+                        float v[4][CPL];
+                        seg_rows<D, KVT, 4>(src, h, N, list, j, min(4, b - j), v);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+#pragma unroll
+                            for (int c = 0; c < CPL; ++c) two_sum(hs[c], es[c], (double)v[u][c]);
+                    }
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) mean[c] = mean_of(hs[c] + es[c], cnt);
+                }
             }
-        }
-        uint32_t bb[CPL];
+            uint32_t bb[CPL];
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) bb[c] = f32_to_bf16(mean[c]);
-        float *cr = C + ((size_t)h * K + k) * D + lane * CPL;
-        uint16_t *br = Cb + ((size_t)h * Kp + k) * D + lane * CPL;
-        if constexpr (CPL == 2) {
-            *reinterpret_cast<float2 *>(cr) = make_float2(mean[0], mean[1]);
-            *reinterpret_cast<uint32_t *>(br) = bb[0] | (bb[1] << 16);
-        } else {
-            cr[0] = mean[0];
-            br[0] = (uint16_t)bb[0];
+            for (int c = 0; c < CPL; ++c) bb[c] = f32_to_bf16(mean[c]);
+            float *cr = C + ((size_t)h * K + k) * D + lane * CPL;
+            uint16_t *br = Cb + ((size_t)h * Kp + k) * D + lane * CPL;
+            if constexpr (CPL == 2) {
+                *reinterpret_cast<float2 *>(cr) = make_float2(mean[0], mean[1]);
+                *reinterpret_cast<uint32_t *>(br) = bb[0] | (bb[1] << 16);
+            } else {
+                cr[0] = mean[0];
+                br[0] = (uint16_t)bb[0];
+            }
         }
     }
 }
@@ -1491,10 +1534,11 @@ hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &s
                              int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s) {
     if (!update_seg_fits(N)) return hipErrorInvalidValue;
     const int Kp = padded_k(K);
-    const int64_t nb = (int64_t)H * ((K + SEG_KR - 1) / SEG_KR);
-    if (nb >= (int64_t)1 << 31) return hipErrorInvalidValue;
+    const int64_t nb = (int64_t)H * SEG_RUNS;
+    // every run fits one window of SEG_KR centroids; thread k of a workgroup holds centroid k
+    if (nb >= (int64_t)1 << 31 || K > SEG_KR * SEG_RUNS || K >= 64 * SEG_WAVES - SEG_KR) return hipErrorInvalidValue;
     QVG_DISPATCH_DT(D, dtype, {
-        const size_t lds = seg_lds_bytes<DD>(N);
+        const size_t lds = seg_lds_bytes<DD>(N, K);
         (void)hipFuncSetAttribute((const void *)k_update_seg<DD, KVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
         QVG_KERNEL((k_update_seg<DD, KVT>), dim3((unsigned)nb), dim3(64 * SEG_WAVES), lds, s, src, H, N, K, Kp, pi,
