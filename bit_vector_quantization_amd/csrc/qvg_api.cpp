@@ -131,7 +131,7 @@ struct ProfScope {
 // residuals R(t) are never stored: each kernel rebuilds them from the input
 // and the earlier stages' stored centroids and assignments.
 struct EncodeWorkspace {
-    size_t C = 0, Cb = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, vstats = 0, total = 0;
+    size_t C = 0, Cb = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, vstats = 0, tstats = 0, total = 0;
 
     EncodeWorkspace(const qvg_config &c, int H, int N) {
         const size_t D = c.d, K = c.n_centroids, Kp = padded_k(c.n_centroids);
@@ -147,6 +147,7 @@ struct EncodeWorkspace {
         order = take((size_t)H * N * 4);
         idx = take((size_t)T * H * K * 4);
         vstats = take(value_stats_words(H) * 4);
+        tstats = take((size_t)T * H * TSTAT_BLOCKS * 2 * 4);
         total = off;
     }
 };
@@ -352,6 +353,7 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
     int32_t *order = at<int32_t>(workspace, ws.order);
     int32_t *idx = at<int32_t>(workspace, ws.idx);
     uint32_t *vstats = at<uint32_t>(workspace, ws.vstats);
+    uint32_t *tstats = at<uint32_t>(workspace, ws.tstats);   // [T][H][TSTAT_BLOCKS] stored-table magnitudes
     const bool warm_cache = cache && cache->valid;
     const bool need_draw = !init_centroids && !warm_cache;
     if (need_draw) QVG_LAUNCH("forgy", 0, (double)T * H * K * 4, launch_forgy(T, H, N, K, cfg->seed, idx, s));
@@ -368,6 +370,7 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
     Src src = src0;
     src.pi_hs = cap;
     src.K = K;
+    src.tstats = tstats;
     const double table = (double)H * Kp * D * 2;
     for (int t = 1; t <= T; ++t) {
         uint8_t *pi = dst->assign + (size_t)(t - 1) * H * cap + tok0;
@@ -402,7 +405,8 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
         void *cslot = static_cast<char *>(dst->centroids) +
                       (((size_t)chunk_index * T + (t - 1)) * H * K * D) * esz;
         QVG_LAUNCH("store_centroids", 0, (double)H * K * D * (4 + esz + (cache ? 4 : 0)),
-                   launch_store_centroids(D, H, K, C, cfg->dtype, cslot, cache ? cache->data + slice : nullptr, s));
+                   launch_store_centroids(D, H, K, C, cfg->dtype, cslot, cache ? cache->data + slice : nullptr,
+                                          tstats + (size_t)(t - 1) * H * TSTAT_BLOCKS * 2, s));
         if (t < T) {
             src.cent[t - 1] = cslot;
             src.pi[t - 1] = pi;

@@ -1035,9 +1035,10 @@ hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, 
 //     (|a| + |b|)(1 + 2^-24) in magnitude.  So every value of R(t-1) of a head
 //     is a multiple of the smallest ulp among the head's input values and
 //     stored centroid tables, and at most the sum of their largest magnitudes
-//     (times 1 + 2^-20).  k_value_stats provides the input's part; each
-//     workgroup scans the tables.  When (largest count of the run) x (that
-//     magnitude) < 2^(53+e), every centroid of the run is certified.
+//     (times 1 + 2^-20).  The first assign or k_value_stats provides the
+//     input's part, k_store_centroids the tables' (when it stores them).  When
+//     (largest count of the run) x (that magnitude) < 2^(53+e), every centroid
+//     of the run is certified.
 //     Otherwise each centroid collects max|v| and the lowest set bit of its
 //     values during the sums and is certified on its own; a centroid without
 //     a certificate is summed again by one wave with the interval test and the
@@ -1319,30 +1320,18 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
     };
     label_batch(0);
     const int cnt_k = counts[(size_t)h * Kp + min(tid, K - 1)];   // (thread k < K holds centroid k)
-    uint32_t tmn = 0xFFFFFFFFu, tmx = 0u;   // magnitudes of the earlier stages' stored tables
-    if (xstats) {
-        constexpr int PER = 16 / sizeof(KVT);
-        const int nv = K * D / PER;
+    // magnitudes of the earlier stages' stored tables (folded in when they were stored)
+    uint32_t tmn = 0xFFFFFFFFu, tmx = 0u;
+    const bool tables_known = src.P == 0 || src.tstats != nullptr;
+    if (xstats && src.tstats) {
 #pragma unroll 1
-        for (int p = 0; p < src.P; ++p) {
-            const uint4 *tp = reinterpret_cast<const uint4 *>(static_cast<const KVT *>(src.cent[p]) + (size_t)h * K * D);
-            for (int i = tid; i < nv; i += NT) {
-                const uint4 q = tp[i];
-                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        for (int p = 0; p < src.P; ++p)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    if constexpr (sizeof(KVT) == 2) {
-                        const uint32_t lo = w[jj] & 0x7FFFu, hi = (w[jj] >> 16) & 0x7FFFu;
-                        tmx = max(tmx, max(lo, hi));
-                        tmn = min(tmn, min(lo - 1u, hi - 1u));
-                    } else {
-                        const uint32_t a = w[jj] & 0x7FFFFFFFu;
-                        tmx = max(tmx, a);
-                        tmn = min(tmn, a - 1u);
-                    }
-                }
+            for (int b = 0; b < TSTAT_BLOCKS; ++b) {
+                const uint32_t *t = src.tstats + (((size_t)p * H + h) * TSTAT_BLOCKS + b) * 2;
+                tmn = min(tmn, t[0]);
+                tmx = max(tmx, t[1]);
             }
-        }
     }
 
     // the head's exclusive prefix P(k), from wave-wide scans of the counts
@@ -1354,24 +1343,18 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
         if (lane >= o) incl += y;
     }
     if (lane == 63) s_wsum[wave] = incl;
-    if (tid < 8) s_misc[tid] = tid == 0 ? 0xFFFFFFFFu : 0u;
+    if (tid < 8) s_misc[tid] = tid == 0 ? tmn : tid == 1 ? tmx : 0u;
     if (tid < SEG_RUNS) s_rc[tid] = 0;
     for (int i = tid; i < SEG_KR * D; i += NT) acc[i] = 0.0;
     if (tid < SEG_KR) {
         s_emin[tid] = SEG_EMPTY_E;
         s_amax[tid] = 0u;
     }
-    tmn = (uint32_t)wave_min_i((int)(tmn ^ 0x80000000u)) ^ 0x80000000u;   // unsigned minimum
-    tmx = wave_max_u(tmx);
     __syncthreads();
     int pk = incl - ck;   // P(tid); thread K holds P(K) = N
     for (int w = 0; w < wave; ++w) pk += s_wsum[w];
     // the token share floor(P(k) SEG_RUNS / N) of every centroid, counted per share
     if (tid < K) atomicAdd(&s_rc[(int)min((int64_t)SEG_RUNS - 1, (int64_t)pk * SEG_RUNS / N)], 1u);
-    if (xstats && lane == 0 && src.P > 0) {
-        atomicMin(&s_misc[0], tmn);
-        atomicMax(&s_misc[1], tmx);
-    }
     __syncthreads();
     // Run boundaries b_0 = 0 <= b_1 <= ... <= b_SEG_RUNS = K (the same in every
     // workgroup of the head): b_{q+1} is the first centroid of token share
@@ -1405,7 +1388,7 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
     if (tid < K + SEG_KR) s_off[tid + 1] = tid < ka ? 0 : tid < kb ? pk - p0 : S;
     if (tid == 0) s_off[0] = 0;
     if (tid == 0) {   // the run certificate
-        bool ok = xstats != nullptr;
+        bool ok = xstats != nullptr && tables_known;
         if (ok) {
             uint32_t mn = s_misc[0], mx = s_misc[1];
             double mag = (double)magnitude_of<KVT>(mx);   // the tables' largest magnitudes, summed over stages
@@ -1551,30 +1534,81 @@ hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &s
 // stored centroids and the streaming cache
 // ---------------------------------------------------------------------------
 
-// Eight consecutive values per thread over the H K D values.
-__global__ __launch_bounds__(256) void k_store_centroids(int64_t n8, const float *C, int dtype, void *dst,
-                                                         float *cache) {
-    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (g >= n8) return;
-    const float4 a = reinterpret_cast<const float4 *>(C)[2 * g], b = reinterpret_cast<const float4 *>(C)[2 * g + 1];
-    if (dtype == DT_BF16) {
-        reinterpret_cast<uint4 *>(dst)[g] = make_uint4(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
-                                                       pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w));
-    } else {
-        reinterpret_cast<float4 *>(dst)[2 * g] = a;
-        reinterpret_cast<float4 *>(dst)[2 * g + 1] = b;
+// TSTAT_BLOCKS workgroups per head, each with up to 1024 eight-value chunks of
+// the head's K D values (four per thread, all loads issued together).  With
+// tstats, each workgroup also writes the smallest nonzero and largest magnitude
+// (bits of the stored dtype, without sign) of its stored values: partial pair
+// tstats[h][b] = {smallest - 1 (0xFFFFFFFF: all zero), largest}.
+__global__ __launch_bounds__(256) void k_store_centroids(int64_t per_head8, const float *C, int dtype, void *dst,
+                                                         float *cache, uint32_t *tstats) {
+    constexpr int CPT = 4;
+    const int h = blockIdx.y, b = blockIdx.x;
+    const int64_t beg = (int64_t)h * per_head8 + (int64_t)b * 256 * CPT;
+    const int64_t end = (int64_t)h * per_head8 + min(per_head8, (int64_t)(b + 1) * 256 * CPT);
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    if (beg < end) {
+        float4 a[CPT], c[CPT];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {   // chunks past the end read the last one again
+            const int64_t g = min(beg + i * 256 + threadIdx.x, end - 1);
+            a[i] = reinterpret_cast<const float4 *>(C)[2 * g];
+            c[i] = reinterpret_cast<const float4 *>(C)[2 * g + 1];
+        }
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int64_t g = beg + i * 256 + threadIdx.x;
+            const bool in = g < end;
+            if (dtype == DT_BF16) {
+                const uint4 q = make_uint4(pack_bf16x2(a[i].x, a[i].y), pack_bf16x2(a[i].z, a[i].w),
+                                           pack_bf16x2(c[i].x, c[i].y), pack_bf16x2(c[i].z, c[i].w));
+                if (in) reinterpret_cast<uint4 *>(dst)[g] = q;
+                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+                    mx = max(mx, max(lo, hi));
+                    mn = min(mn, min(lo - 1u, hi - 1u));   // zero wraps to the largest value
+                }
+            } else {
+                if (in) {
+                    reinterpret_cast<float4 *>(dst)[2 * g] = a[i];
+                    reinterpret_cast<float4 *>(dst)[2 * g + 1] = c[i];
+                }
+                const float f[8] = {a[i].x, a[i].y, a[i].z, a[i].w, c[i].x, c[i].y, c[i].z, c[i].w};
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t m = __float_as_uint(f[j]) & 0x7FFFFFFFu;
+                    mx = max(mx, m);
+                    mn = min(mn, m - 1u);
+                }
+            }
+            if (cache && in) {
+                reinterpret_cast<float4 *>(cache)[2 * g] = a[i];
+                reinterpret_cast<float4 *>(cache)[2 * g + 1] = c[i];
+            }
+        }
     }
-    if (cache) {
-        reinterpret_cast<float4 *>(cache)[2 * g] = a;
-        reinterpret_cast<float4 *>(cache)[2 * g + 1] = b;
+    if (!tstats) return;
+    __shared__ uint32_t red[2][4];
+    mn = (uint32_t)wave_min_i((int)(mn ^ 0x80000000u)) ^ 0x80000000u;   // unsigned minimum
+    mx = wave_max_u(mx);
+    if ((threadIdx.x & 63) == 0) {
+        red[0][threadIdx.x >> 6] = mn;
+        red[1][threadIdx.x >> 6] = mx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t *o = tstats + ((size_t)h * TSTAT_BLOCKS + b) * 2;
+        o[0] = min(min(red[0][0], red[0][1]), min(red[0][2], red[0][3]));
+        o[1] = max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3]));
     }
 }
 
 hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype, void *dst, float *cache,
-                                  hipStream_t s) {
-    const int64_t n8 = (int64_t)H * K * D / 8;   // D is a multiple of 8
-    if ((n8 + 255) / 256 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-    QVG_KERNEL(k_store_centroids, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, n8, C, dtype, dst, cache);
+                                  uint32_t *tstats, hipStream_t s) {
+    const int64_t per_head8 = (int64_t)K * D / 8;   // D is a multiple of 8
+    if (per_head8 > (int64_t)TSTAT_BLOCKS * 256 * 4 || H >= 65536) return hipErrorInvalidValue;
+    QVG_KERNEL(k_store_centroids, dim3(TSTAT_BLOCKS, H), dim3(256), 0, s, per_head8, C, dtype, dst, cache, tstats);
     return hipGetLastError();
 }
 

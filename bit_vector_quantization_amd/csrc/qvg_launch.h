@@ -28,6 +28,9 @@ struct Src {
     int64_t pi_hs;
     int P;
     int K;
+    // magnitude statistics of the earlier stages' stored tables,
+    // [P][H][TSTAT_BLOCKS] partial pairs (see launch_store_centroids), or null
+    const uint32_t *tstats;
 };
 
 // Cold start: indices [T][H][K] of the Forgy rows of every (stage, head).
@@ -85,9 +88,13 @@ hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &s
                              int64_t pi_hs, const int32_t *counts, const uint32_t *xstats, float *C, uint16_t *Cb,
                              int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s);
 
-// dst_slice [H][K][D] = C rounded to dtype; cache_slice [H][K][D] = C (if non-null).
+// dst_slice [H][K][D] = C rounded to dtype; cache_slice [H][K][D] = C (if non-null);
+// tstats (if non-null) receives TSTAT_BLOCKS partial pairs per head of the
+// stored magnitudes: {smallest nonzero - 1 (0xFFFFFFFF: all zero), largest} of
+// the bf16 (15-bit) or fp32 (31-bit) magnitude bits.  K D <= 8192 TSTAT_BLOCKS.
+constexpr int TSTAT_BLOCKS = 4;
 hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype, void *dst_slice,
-                                  float *cache_slice, hipStream_t s);
+                                  float *cache_slice, uint32_t *tstats, hipStream_t s);
 
 // r = R(t-1) - cent[pi] (cent non-null; cent [H][cent_rows][D] of the tensor
 // dtype) or r = R(t-1); then 2-bit codes and E4M3 scales of r, head stride
