@@ -362,8 +362,10 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
 // decision is that of |c|^2 - 2 <x, c>, lowest index on ties.
 //
 // A workgroup is 16 waves, each taking 32-token tiles; the bf16 tables of up
-// to two heads (swizzled 16-byte chunks, 64 KiB each at 256 x 128) and their
-// norms sit in LDS: one workgroup per CU, four waves per SIMD.
+// to two heads (rows of D / 8 + 1 16-byte chunks, the last unused, so that the
+// 16 rows of an operand read start on 16 different chunk positions: 68 KiB
+// each at 256 x 128) and their norms sit in LDS: one workgroup per CU, four
+// waves per SIMD.
 
 constexpr int ASSIGN_TB = 2;              // 16-token blocks per wave
 constexpr int TILE = 16 * ASSIGN_TB;      // tokens per wave
@@ -372,6 +374,13 @@ constexpr float PAD_HALF_NORM = -1e30f;   // padding rows: never the nearest
 
 __device__ __forceinline__ float fmax_key(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, __FLT_MAX__); }
 __device__ __forceinline__ float fmin_key(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, -__FLT_MAX__); }
+// the largest of three keys in one instruction (the compiler would guard a
+// chain of maxima with canonicalising moves; keys are never NaN)
+__device__ __forceinline__ float fmax3_key(float a, float b, float c) {
+    float d;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
 
 // fp32(x - c) of eight bf16 pairs, rounded back to bf16.
 __device__ __forceinline__ uint4 sub_bf16x8(uint4 x, uint4 c) {
@@ -496,16 +505,16 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
     for (int b = 0; b < ASSIGN_TB; ++b) q1[b] = q2[b] = -__FLT_MAX__;
     const uint32_t sel = 0x07060500u;   // bytes 3..1 from the accumulator, byte 0 from the number
     const int ncb = Kp / 16;
-    // row cb * 16 + r16 of the table: its swizzle (row & (CH - 1)) does not depend on cb
-    const uint4 *arow[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) arow[s] = lds + r16 * CH + ((4 * s + g) ^ (r16 & (CH - 1)));
+    // row cb * 16 + r16 of the table, the lane's chunk 4 s + g of step s: rows
+    // are CH + 1 chunks apart, so every address is a constant offset from one
+    // base (and the 16 rows of a read fall on 16 different chunk positions)
+    const uint4 *arow = lds + r16 * (CH + 1) + g;
     const float4 *cnp = reinterpret_cast<const float4 *>(lhcn + 4 * g);
     // accumulators of the centroid block at offset j blocks from the pointers
     auto dots = [&](int j, f32x4_t (&acc)[ASSIGN_TB]) {
         bf16x8_t a[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) a[s] = __builtin_bit_cast(bf16x8_t, arow[s][j * 16 * CH]);
+        for (int s = 0; s < KS; ++s) a[s] = __builtin_bit_cast(bf16x8_t, arow[j * 16 * (CH + 1) + 4 * s]);
         const float4 cn = cnp[j * 4];
 #pragma unroll
         for (int b = 0; b < ASSIGN_TB; ++b)
@@ -517,16 +526,20 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
             for (int b = 0; b < ASSIGN_TB; ++b)
                 acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bt[b][s], acc[b], 0, 0, 0);
     };
-    // fold the accumulators of centroid block cb into the two best keys
+    // fold the accumulators of centroid block cb into the two best keys, two
+    // keys at a time: with q1 >= q2, the second largest of {q1, q2, ka, kb} is
+    // max(q2, med3(q1, ka, kb))
     auto keys = [&](int cb, const f32x4_t (&acc)[ASSIGN_TB]) {
 #pragma unroll
         for (int b = 0; b < ASSIGN_TB; ++b) {
+            float key[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float key =
-                    __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(acc[b][r]), (uint32_t)(4 * cb + r), sel));
-                q2[b] = __builtin_amdgcn_fmed3f(q1[b], q2[b], key);
-                q1[b] = fmax_key(q1[b], key);
+            for (int r = 0; r < 4; ++r)
+                key[r] = __uint_as_float(__builtin_amdgcn_perm(__float_as_uint(acc[b][r]), (uint32_t)(4 * cb + r), sel));
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+                q2[b] = fmax_key(q2[b], __builtin_amdgcn_fmed3f(q1[b], key[r], key[r + 1]));
+                q1[b] = fmax3_key(q1[b], key[r], key[r + 1]);
             }
         }
     };
@@ -540,8 +553,7 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
         keys(cb, accA);
         dots(2, accA);
         keys(cb + 1, accB);
-#pragma unroll
-        for (int s = 0; s < KS; ++s) arow[s] += 32 * CH;
+        arow += 32 * (CH + 1);
         cnp += 8;
     }
     if (cb + 1 < ncb) {
@@ -598,8 +610,8 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
         double p1 = 0.0, p2 = 0.0;   // <x, c1>, <x, c2>
         if (j < n_list && sub < CH) {
             const uint4 xv = src_row8_bf16<D, KVT>(src, h, n, 8 * sub);
-            const uint4 a1 = lds[c1 * CH + (sub ^ (c1 & (CH - 1)))];
-            const uint4 a2 = lds[c2 * CH + (sub ^ (c2 & (CH - 1)))];
+            const uint4 a1 = lds[c1 * (CH + 1) + sub];
+            const uint4 a2 = lds[c2 * (CH + 1) + sub];
             const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
             const uint32_t aw[4] = {a1.x, a1.y, a1.z, a1.w};
             const uint32_t bw[4] = {a2.x, a2.y, a2.z, a2.w};
@@ -641,7 +653,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
     constexpr int NT = 64 * ASSIGN_WAVES;
     constexpr int STAGE = (256 * CH + NT - 1) / NT;   // table chunks per thread at 256 centroids
     extern __shared__ uint4 lds[];                      // two table slots
-    double *lcn64 = reinterpret_cast<double *>(lds + 2 * Kp * CH);
+    double *lcn64 = reinterpret_cast<double *>(lds + 2 * Kp * (CH + 1));
     float *lhcn = reinterpret_cast<float *>(lcn64 + 2 * Kp);
     int32_t *lists = reinterpret_cast<int32_t *>(lhcn + 2 * Kp);
     int32_t *next = lists + ASSIGN_WAVES * TILE;
@@ -667,12 +679,12 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
                 const int i = t0 + NT * k;
                 st[k] = csrc[i < nch ? i : nch - 1];
             }
-            uint4 *slot = lds + sl * nch;
+            uint4 *slot = lds + sl * Kp * (CH + 1);
 #pragma unroll
             for (int k = 0; k < STAGE; ++k) {
                 const int i = t0 + NT * k;
                 const int row = i / CH, q = i - row * CH;
-                if (i < nch) slot[row * CH + (q ^ (row & (CH - 1)))] = st[k];
+                if (i < nch) slot[row * (CH + 1) + q] = st[k];
                 // |c|^2 of the row: the CH lanes holding its chunks are neighbours;
                 // every bf16 square is exact in fp64
                 const uint32_t w[4] = {st[k].x, st[k].y, st[k].z, st[k].w};
@@ -726,7 +738,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
                     }
                 }
             }
-            assign_wave<D, KVT>(src, h, N, tok0, bt, lds + sl * nch, lcn64 + sl * Kp, lhcn + sl * Kp,
+            assign_wave<D, KVT>(src, h, N, tok0, bt, lds + sl * Kp * (CH + 1), lcn64 + sl * Kp, lhcn + sl * Kp,
                                 lists + wave * TILE, Kp, pi, pi_hs, counts);
         }
         __syncthreads();   // the tables are replaced only once every wave is done with them
@@ -749,7 +761,7 @@ static int device_cus() {
 hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, const uint16_t *Cb, uint8_t *pi,
                          int64_t pi_hs, int32_t *counts, uint32_t *vstats, hipStream_t s) {
     const int Kp = padded_k(K);
-    const size_t lds = 2 * ((size_t)Kp * D * 2 + (size_t)Kp * 12) + (ASSIGN_WAVES * TILE + 4) * sizeof(int32_t);
+    const size_t lds = 2 * ((size_t)Kp * (D / 8 + 1) * 16 + (size_t)Kp * 12) + (ASSIGN_WAVES * TILE + 4) * sizeof(int32_t);
     // one resident workgroup per CU, at least a tile per wave
     const int64_t units = (int64_t)H * ((N + TILE - 1) / TILE);
     if (units >= (int64_t)1 << 31) return hipErrorInvalidValue;
