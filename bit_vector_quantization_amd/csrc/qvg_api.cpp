@@ -131,7 +131,8 @@ struct ProfScope {
 // residuals R(t) are never stored: each kernel rebuilds them from the input
 // and the earlier stages' stored centroids and assignments.
 struct EncodeWorkspace {
-    size_t C = 0, Cb = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, vstats = 0, tstats = 0, total = 0;
+    size_t C = 0, Cb = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, vstats = 0, tstats = 0, r1 = 0,
+           total = 0;
 
     EncodeWorkspace(const qvg_config &c, int H, int N) {
         const size_t D = c.d, K = c.n_centroids, Kp = padded_k(c.n_centroids);
@@ -148,6 +149,7 @@ struct EncodeWorkspace {
         idx = take((size_t)T * H * K * 4);
         vstats = take(value_stats_words(H) * 4);
         tstats = take((size_t)T * H * TSTAT_BLOCKS * 2 * 4);
+        if (c.dtype == QVG_BF16 && T >= 2) r1 = take((size_t)H * N * D * 2);   // R(1) as the stage-2 operand
         total = off;
     }
 };
@@ -354,6 +356,10 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
     int32_t *idx = at<int32_t>(workspace, ws.idx);
     uint32_t *vstats = at<uint32_t>(workspace, ws.vstats);
     uint32_t *tstats = at<uint32_t>(workspace, ws.tstats);   // [T][H][TSTAT_BLOCKS] stored-table magnitudes
+    // bf16 tensors: the final assign of stage 1 leaves bf16(R(1)) [H][N][D], which
+    // the assigns of stage 2 read in place of x less the stage-1 rows
+    uint16_t *r1 = cfg->dtype == QVG_BF16 && T >= 2 ? at<uint16_t>(workspace, ws.r1) : nullptr;
+    Src r1src = plain_src(r1, (int64_t)N * D);
     const bool warm_cache = cache && cache->valid;
     const bool need_draw = !init_centroids && !warm_cache;
     if (need_draw) QVG_LAUNCH("forgy", 0, (double)T * H * K * 4, launch_forgy(T, H, N, K, cfg->seed, idx, s));
@@ -380,14 +386,17 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
         // algorithmic traffic: the input row plus one assignment byte per earlier stage
         const double row_bytes = HND * esz + (double)H * N * (t - 1);
         const double assign_flops = 2.0 * H * N * K * D;
+        const bool use_r1 = r1 && t == 2;
+        const Src &asrc = use_r1 ? r1src : src;   // what the assigns read
+        const double assign_bytes = (use_r1 ? HND * 2 : row_bytes) + H * N + table;
         QVG_LAUNCH("init_centroids", 0, (double)H * K * D * (esz + 4) + table,
                    launch_init_centroids(D, cfg->dtype, H, K, src, idx + (size_t)(t - 1) * H * K, warm, C, Cb,
                                          cnt[0], fill[0], t == 1 && stats_in_assign ? vstats : nullptr, s));
         for (int it = 0; it < iters; ++it) {
             const int c = it & 1;
-            QVG_LAUNCH("assign", assign_flops, row_bytes + H * N + table,
-                       launch_assign(D, cfg->dtype, H, N, K, src, Cb, pi, cap, cnt[c],
-                                     t == 1 && it == 0 && stats_in_assign ? vstats : nullptr, s));
+            QVG_LAUNCH("assign", assign_flops, assign_bytes,
+                       launch_assign(D, cfg->dtype, H, N, K, asrc, Cb, pi, cap, cnt[c],
+                                     t == 1 && it == 0 && stats_in_assign ? vstats : nullptr, nullptr, s));
             if (seg) {
                 QVG_LAUNCH("update", HND, row_bytes + H * N + (double)H * K * D * 4 + table,
                            launch_update_seg(D, cfg->dtype, H, N, K, src, pi, cap, cnt[c], vstats, C, Cb,
@@ -400,8 +409,9 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
                                          fill[c ^ 1], s));
             }
         }
-        QVG_LAUNCH("assign", assign_flops, row_bytes + H * N + table,
-                   launch_assign(D, cfg->dtype, H, N, K, src, Cb, pi, cap, nullptr, nullptr, s));
+        uint16_t *rout = r1 && t == 1 ? r1 : nullptr;
+        QVG_LAUNCH("assign", assign_flops, assign_bytes + (rout ? HND * 2 : 0.0),
+                   launch_assign(D, cfg->dtype, H, N, K, asrc, Cb, pi, cap, nullptr, nullptr, rout, s));
         void *cslot = static_cast<char *>(dst->centroids) +
                       (((size_t)chunk_index * T + (t - 1)) * H * K * D) * esz;
         QVG_LAUNCH("store_centroids", 0, (double)H * K * D * (4 + esz + (cache ? 4 : 0)),
@@ -491,7 +501,7 @@ qvg_status qvg_kmeans_assign(const void *x, int32_t x_dtype, int64_t x_head_stri
     QVG_LAUNCH("assign", 2.0 * heads * n_tokens * n_centroids * d,
                (double)heads * n_tokens * (d * dtype_size(x_dtype) + 1) + table,
                launch_assign(d, x_dtype, heads, n_tokens, n_centroids, src, Cb, assign_out, assign_head_stride, nullptr,
-                             nullptr, s));
+                             nullptr, nullptr, s));
     return QVG_OK;
 }
 

@@ -476,7 +476,8 @@ __device__ __forceinline__ void assign_load(const Src &src, int h, int N, int to
 template <int D, typename KVT>
 __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int tok0, const bf16x8_t (&bt)[ASSIGN_TB][D / 32],
                                             const uint4 *lds, const double *lcn64, const float *lhcn, int32_t *list,
-                                            int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts) {
+                                            uint8_t *labs, int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts,
+                                            uint16_t *rout) {
     constexpr int KS = D / 32;
     constexpr int CH = D / 8;
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
@@ -590,6 +591,7 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
         if (mine && !tie) {
             pi[(size_t)h * pi_hs + n] = (uint8_t)c1;
             if (counts) atomicAdd(&counts[(size_t)h * Kp + c1], 1);
+            if (rout) labs[16 * b + r16] = (uint8_t)c1;
         }
         const uint64_t m = __ballot(mine && tie);
         if (mine && tie) {
@@ -598,7 +600,6 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
         }
         n_list += __popcll(m);
     }
-    if (n_list == 0) return;
     __builtin_amdgcn_wave_barrier();
     // near ties: 16 lanes per token, 8 channels each, fp64 distances
     const int sub = lane & 15, grp = lane >> 4;
@@ -635,6 +636,20 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
             const int best = (e2 < e1 || (e2 == e1 && c2 < c1)) ? c2 : c1;
             pi[(size_t)h * pi_hs + n] = (uint8_t)best;
             if (counts) atomicAdd(&counts[(size_t)h * Kp + best], 1);
+            if (rout) labs[nl] = (uint8_t)best;
+        }
+    }
+    if (!rout) return;
+    // the next stage's operand: bf16(fp32(x - c)) with c the token's stored row
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int b = 0; b < ASSIGN_TB; ++b) {
+        const int n = tok0 + 16 * b + r16;
+        const int L = n < N ? (int)labs[16 * b + r16] : 0;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const uint4 r = sub_bf16x8(__builtin_bit_cast(uint4, bt[b][s]), lds[L * (CH + 1) + 4 * s + g]);
+            if (n < N) *reinterpret_cast<uint4 *>(rout + ((size_t)h * N + n) * D + 32 * s + 8 * g) = r;
         }
     }
 }
@@ -648,7 +663,8 @@ template <int D, typename KVT, bool ANYP>
 __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H, int N, const uint16_t *__restrict__ Cb,
                                                                  int K, int Kp, uint8_t *__restrict__ pi,
                                                                  int64_t pi_hs, int32_t *__restrict__ counts,
-                                                                 uint32_t *__restrict__ vstats) {
+                                                                 uint32_t *__restrict__ vstats,
+                                                                 uint16_t *__restrict__ rout) {
     constexpr int CH = D / 8;
     constexpr int NT = 64 * ASSIGN_WAVES;
     constexpr int STAGE = (256 * CH + NT - 1) / NT;   // table chunks per thread at 256 centroids
@@ -657,6 +673,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
     float *lhcn = reinterpret_cast<float *>(lcn64 + 2 * Kp);
     int32_t *lists = reinterpret_cast<int32_t *>(lhcn + 2 * Kp);
     int32_t *next = lists + ASSIGN_WAVES * TILE;
+    uint8_t *labs = reinterpret_cast<uint8_t *>(next + 4);   // [ASSIGN_WAVES][TILE] labels for rout
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int T = (N + TILE - 1) / TILE;   // tiles per head
     const int64_t U = (int64_t)H * T;
@@ -739,7 +756,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
                 }
             }
             assign_wave<D, KVT>(src, h, N, tok0, bt, lds + sl * Kp * (CH + 1), lcn64 + sl * Kp, lhcn + sl * Kp,
-                                lists + wave * TILE, Kp, pi, pi_hs, counts);
+                                lists + wave * TILE, labs + wave * TILE, Kp, pi, pi_hs, counts, rout);
         }
         __syncthreads();   // the tables are replaced only once every wave is done with them
         u = e;
@@ -759,9 +776,10 @@ static int device_cus() {
 }
 
 hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, const uint16_t *Cb, uint8_t *pi,
-                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, hipStream_t s) {
+                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, uint16_t *rout, hipStream_t s) {
     const int Kp = padded_k(K);
-    const size_t lds = 2 * ((size_t)Kp * (D / 8 + 1) * 16 + (size_t)Kp * 12) + (ASSIGN_WAVES * TILE + 4) * sizeof(int32_t);
+    const size_t lds = 2 * ((size_t)Kp * (D / 8 + 1) * 16 + (size_t)Kp * 12) + (ASSIGN_WAVES * TILE + 4) * sizeof(int32_t) +
+                       ASSIGN_WAVES * TILE;
     // one resident workgroup per CU, at least a tile per wave
     const int64_t units = (int64_t)H * ((N + TILE - 1) / TILE);
     if (units >= (int64_t)1 << 31) return hipErrorInvalidValue;
@@ -770,17 +788,18 @@ hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, 
     // bf16 tensors with at most one earlier stage (every stage at T <= 2) take the
     // specialised operand load
     const bool anyp = !(dtype == DT_BF16 && src.P <= 1);
+    if (rout && (anyp || src.P != 0)) return hipErrorInvalidValue;
     QVG_DISPATCH_DT(D, dtype, {
         if (anyp || sizeof(KVT) != 2) {
             (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT, true>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             QVG_KERNEL((k_assign<DD, KVT, true>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts,
-                       (uint32_t *)nullptr);
+                       (uint32_t *)nullptr, (uint16_t *)nullptr);
         } else {
             using KB = uint16_t;   // (this branch is only taken for bf16)
             (void)hipFuncSetAttribute((const void *)k_assign<DD, KB, false>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            QVG_KERNEL((k_assign<DD, KB, false>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts, vstats);
+            QVG_KERNEL((k_assign<DD, KB, false>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts, vstats, rout);
         }
     });
     return hipGetLastError();

@@ -53,8 +53,11 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
 // exactly in fp64.  counts (non-null) [H][Kp] += tokens per centroid.  vstats
 // (non-null; a bf16 tensor without earlier stages only): the input's value
 // statistics are folded into partial 0 of each head (cleared beforehand).
+// rout (non-null; a bf16 tensor without earlier stages only) [H][N][D] bf16
+// receives bf16(fp32(x - Cb[pi])), the operand that the next stage's assign
+// would otherwise rebuild from x, its table and its assignment.
 hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, const uint16_t *Cb, uint8_t *pi,
-                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, hipStream_t s);
+                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, uint16_t *rout, hipStream_t s);
 
 // Histogram of an assignment (counts must be zero on entry).
 hipError_t launch_count(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, int32_t *counts,
