@@ -1338,7 +1338,7 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
     const uint8_t *l1 = src.P >= 1 ? src.pi[0] + (size_t)h * src.pi_hs : lab;
     const uint8_t *l2 = src.P >= 2 ? src.pi[1] + (size_t)h * src.pi_hs : lab;
     const uint32_t m1 = src.P >= 1 ? 0xFFu : 0u, m2 = src.P >= 2 ? 0xFFu : 0u;
-    constexpr int B = 8;
+    constexpr int B = 10;   // labels per thread and batch: one batch up to 5,120 tokens
     uint32_t lk[B], la[B], lb[B];
     auto label_batch = [&](int n0) {   // unconditional loads, all in flight together
 #pragma unroll
@@ -1351,6 +1351,15 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
     };
     label_batch(0);
     const int cnt_k = counts[(size_t)h * Kp + min(tid, K - 1)];   // (thread k < K holds centroid k)
+    // the input's value statistics, read now for the run certificate
+    uint32_t xmn = 0xFFFFFFFFu, xmx = 0u;
+    if (xstats) {
+#pragma unroll
+        for (int b = 0; b < VSTAT_BLOCKS; ++b) {
+            xmn = min(xmn, xstats[((size_t)h * VSTAT_BLOCKS + b) * 2]);
+            xmx = max(xmx, xstats[((size_t)h * VSTAT_BLOCKS + b) * 2 + 1]);
+        }
+    }
     // magnitudes of the earlier stages' stored tables (folded in when they were stored)
     uint32_t tmn = 0xFFFFFFFFu, tmx = 0u;
     const bool tables_known = src.P == 0 || src.tstats != nullptr;
@@ -1424,11 +1433,6 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
             uint32_t mn = s_misc[0], mx = s_misc[1];
             double mag = (double)magnitude_of<KVT>(mx);   // the tables' largest magnitudes, summed over stages
             if (src.P > 1) mag *= (double)src.P;          // (a bound: each table's maximum is at most mx)
-            uint32_t xmn = 0xFFFFFFFFu, xmx = 0u;
-            for (int b = 0; b < VSTAT_BLOCKS; ++b) {
-                xmn = min(xmn, xstats[((size_t)h * VSTAT_BLOCKS + b) * 2]);
-                xmx = max(xmx, xstats[((size_t)h * VSTAT_BLOCKS + b) * 2 + 1]);
-            }
             mag += (double)magnitude_of<KVT>(xmx);
             mn = min(mn, xmn);
             const int e = mn == 0xFFFFFFFFu ? 1000 : ulp_exp_of<KVT>(mn + 1u);
