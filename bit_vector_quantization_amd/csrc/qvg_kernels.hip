@@ -1078,7 +1078,7 @@ hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, 
 constexpr int SEG_KR = 32;          // centroids per accumulator window
 constexpr int SEG_RUNS = 9;         // workgroups (runs) per head
 constexpr int SEG_WAVES = 8;
-constexpr int SEG_U = 8;            // rows in flight per wave
+constexpr int SEG_U = 12;           // rows in flight per wave
 constexpr int SEG_EMPTY_E = 4096;   // lowest-bit exponent of a centroid with only zeros so far
 
 // Smallest nonzero and largest magnitude bits (bf16: 15 bits, fp32: 31 bits) of
@@ -1193,36 +1193,38 @@ __device__ __forceinline__ int lowest_bit_exp(float v) {
 
 // Rows list[j .. j + m) (1 <= m <= U) of R(P), this lane's channels; slots
 // u >= m read row list[j] again and come out zero.  A list entry is
-// token | label(stage 1) << 16 | label(stage 2) << 24; entries are the same
-// in every lane, so row addresses are formed in scalar registers.  Every load
-// is issued unconditionally (a load under a branch is waited for inside it).
+// token | label(stage 1) << 16 | label(stage 2) << 24; entries are the same in
+// every lane (read into scalar registers).  A row is addressed as the head's
+// base plus a 32-bit byte offset, which keeps the scalar registers per row in
+// flight to one, and every load is issued unconditionally (a load under a
+// branch is waited for inside it).
 template <int D, typename KVT, int U>
 __device__ __forceinline__ void seg_rows(const Src &s, int h, int N, const uint32_t *list, int j, int m,
                                          float (&v)[U][D / 64]) {
     constexpr int CPL = D / 64;
-    const int c0 = (threadIdx.x & 63) * CPL;
+    constexpr uint32_t ROW = D * sizeof(KVT);
+    const uint32_t c0 = (threadIdx.x & 63) * CPL * sizeof(KVT);
     uint32_t e[U];
-    int n[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) e[u] = __builtin_amdgcn_readfirstlane(list[j + (u < m ? u : 0)]);
+    const char *x = reinterpret_cast<const char *>(static_cast<const KVT *>(s.x) + (size_t)h * s.x_hs);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        e[u] = __builtin_amdgcn_readfirstlane(list[j + (u < m ? u : 0)]);
         // a token index is below N by construction; the clamp keeps every row read in bounds
-        n[u] = min((int)(e[u] & 0xFFFFu), N - 1);
+        const uint32_t n = min(e[u] & 0xFFFFu, (uint32_t)N - 1u);
+        load_part<KVT, CPL>(reinterpret_cast<const KVT *>(x + (n * ROW + c0)), v[u]);
     }
-    const KVT *x = static_cast<const KVT *>(s.x) + (size_t)h * s.x_hs + c0;
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_part<KVT, CPL>(x + (size_t)n[u] * D, v[u]);
 #pragma unroll 1
     for (int p = 0; p < s.P; ++p) {
-        const KVT *cp = static_cast<const KVT *>(s.cent[p]) + (size_t)h * s.K * D + c0;
-        int k[U];
+        const char *cp = reinterpret_cast<const char *>(static_cast<const KVT *>(s.cent[p]) + (size_t)h * s.K * D);
+        uint32_t k[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
-            k[u] = p < 2 ? (int)((e[u] >> (16 + 8 * p)) & 0xFFu)
-                         : __builtin_amdgcn_readfirstlane((int)s.pi[p][(size_t)h * s.pi_hs + n[u]]);
+            k[u] = p < 2 ? (e[u] >> (16 + 8 * p)) & 0xFFu
+                         : (uint32_t)s.pi[p][(size_t)h * s.pi_hs + min(e[u] & 0xFFFFu, (uint32_t)N - 1u)];
         float c[U][CPL];
 #pragma unroll
-        for (int u = 0; u < U; ++u) load_part<KVT, CPL>(cp + (size_t)k[u] * D, c[u]);
+        for (int u = 0; u < U; ++u) load_part<KVT, CPL>(reinterpret_cast<const KVT *>(cp + (k[u] * ROW + c0)), c[u]);
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
