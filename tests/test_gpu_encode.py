@@ -44,6 +44,20 @@ def test_tiny_fp32_chunk():
     np.testing.assert_array_equal(to_np(y), oracle.decode(ora[0][0], oc.group_size, "f32"))
 
 
+def test_fp32_three_stages_cold_then_warm():
+    """fp32 tensor, three stages, a cold and a warm chunk: the general operand
+    loader rebuilds R(1) and R(2) from fp32 tables (no stored bf16 operand), and
+    the update's run certificate uses the fp32 stored-table statistics."""
+    say("e2e fp32, T = 3, cold then warm")
+    p = synthkv.PRESETS[1]
+    oc, X, dst, ora, mis = _run(p, "V", n_tokens=2 * p.chunk_tokens, n_stages=3)
+    assert mis == 0
+    q = lib()
+    y = q.decode(gcfg(oc), dst, 0, X.shape[1], out_dtype="f32")
+    ref = np.concatenate([oracle.decode(ora[c][0], oc.group_size, "f32") for c in range(2)], axis=1)
+    np.testing.assert_array_equal(to_np(y), ref)
+
+
 @pytest.mark.parametrize("tensor", ["K", "V"])
 def test_single_head_chunk(tensor):
     say(f"e2e single-head chunk {tensor}")
