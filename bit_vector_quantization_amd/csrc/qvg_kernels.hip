@@ -402,14 +402,9 @@ template <int D, typename KVT, bool ANYP>
 __device__ __forceinline__ void assign_load(const Src &src, int h, int N, int tok0, bf16x8_t (&bt)[ASSIGN_TB][D / 32]) {
     constexpr int KS = D / 32;
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
-    int n[ASSIGN_TB];
-    bool ok[ASSIGN_TB];
+    int n[ASSIGN_TB];   // tokens past N read row N - 1 again; their results are never stored
 #pragma unroll
-    for (int b = 0; b < ASSIGN_TB; ++b) {
-        const int t = tok0 + 16 * b + r16;
-        ok[b] = t < N;
-        n[b] = ok[b] ? t : N - 1;
-    }
+    for (int b = 0; b < ASSIGN_TB; ++b) n[b] = min(tok0 + 16 * b + r16, N - 1);
     if constexpr (sizeof(KVT) == 2 && !ANYP) {
         {   // the input, or the input less one stored bf16 table
             uint4 xr[ASSIGN_TB][KS];
@@ -440,8 +435,7 @@ __device__ __forceinline__ void assign_load(const Src &src, int h, int N, int to
 #pragma unroll
             for (int b = 0; b < ASSIGN_TB; ++b)
 #pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    bt[b][s] = __builtin_bit_cast(bf16x8_t, ok[b] ? xr[b][s] : make_uint4(0, 0, 0, 0));
+                for (int s = 0; s < KS; ++s) bt[b][s] = __builtin_bit_cast(bf16x8_t, xr[b][s]);
         }
         return;
     }
@@ -467,7 +461,7 @@ __device__ __forceinline__ void assign_load(const Src &src, int h, int N, int to
         for (int s = 0; s < KS; ++s) {
             const uint4 w = make_uint4(pack_bf16x2(v[s][0], v[s][1]), pack_bf16x2(v[s][2], v[s][3]),
                                        pack_bf16x2(v[s][4], v[s][5]), pack_bf16x2(v[s][6], v[s][7]));
-            bt[b][s] = __builtin_bit_cast(bf16x8_t, ok[b] ? w : make_uint4(0, 0, 0, 0));
+            bt[b][s] = __builtin_bit_cast(bf16x8_t, w);
         }
     }
 }
