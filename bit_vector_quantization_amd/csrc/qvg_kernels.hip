@@ -620,11 +620,8 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
                 p2 = fma(xh, (double)__uint_as_float(bw[i] & 0xFFFF0000u), p2);
             }
         }
-#pragma unroll
-        for (int o = 1; o < 16; o <<= 1) {
-            p1 += __shfl_xor(p1, o);
-            p2 += __shfl_xor(p2, o);
-        }
+        p1 = group_sum<16>(p1);
+        p2 = group_sum<16>(p2);
         if (j < n_list && sub == 0) {
             const double e1 = lcn64[c1] - 2.0 * p1, e2 = lcn64[c2] - 2.0 * p2;
             const int best = (e2 < e1 || (e2 == e1 && c2 < c1)) ? c2 : c1;
