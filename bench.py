@@ -18,8 +18,11 @@ generated on the device before timing and stay resident in HBM.
 Also reported on the same line: encode-only and warm-chunk rates, the fused
 decode's algorithmic GB/s (timed with HIP events around each decode launch on
 its stream), a per-kernel breakdown from the library's event profiler, the
-roofline of the dominant kernel, the long-horizon decode stress (12 heads,
-700 frames, 1.09 M tokens) and the CPU oracle timed on a bounded sample.
+roofline of the dominant kernel, the same decode with the 40 key heads
+rotated by a 3-D rotary position table in the same pass (keys are cached
+before the rotation) next to the rotation run as a separate pass, the
+long-horizon decode stress (12 heads, 700 frames, 1.09 M tokens) and the CPU
+oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -43,6 +46,8 @@ def parse():
                     help="extra steps run with the library's per-kernel event profiler")
     ap.add_argument("--stress-reps", type=int, default=20,
                     help="timed decodes of the 1.09M-token cache (0 skips the stress part)")
+    ap.add_argument("--rope-reps", type=int, default=10,
+                    help="timed decodes of the layer's cache with the key heads rotated (0 skips)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=3, help="heads in the oracle's timed sample")
     return ap.parse_args()
@@ -183,6 +188,14 @@ def main():
     torch.cuda.synchronize()
     copy_gbs = 2 * src.numel() * 2 / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
 
+    # the same whole-cache decode with the 40 key heads rotated by the latent
+    # grid's 3-D position table in the same pass, and for comparison the
+    # rotation as a separate pass of torch ops over the decoded keys
+    rope_rec = None
+    if args.rope_reps > 0:
+        rope_rec = run_rope(q, synthkv, torch, p, cfg, dst, out, stream, ev, args.rope_reps, H, dec_b,
+                            dec_avg_ms)
+
     # per-kernel breakdown with the library's event profiler
     kernels, raw_stats = {}, {}
     if args.profile_steps > 0:
@@ -212,6 +225,8 @@ def main():
                     avg_launch_us=round(dec_avg_ms * 1e3, 2), algorithmic_per_launch=int(dec_b),
                     timed="HIP events around every decode launch of the timed steps, on its stream")
     roofs["decode"] = dec_roof
+    if rope_rec is not None:
+        roofs["decode_rope"] = rope_rec.pop("roofline")
     for name in ("assign", "update"):
         if name not in raw_stats:
             continue
@@ -263,11 +278,67 @@ def main():
         "decode": {"launch_us": round(dec_avg_ms * 1e3, 2), "algorithmic_bytes": int(dec_b),
                    "gbs": round(decode_gbs, 1), "frac_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4),
                    "copy_kernel_gbs": round(copy_gbs, 1)},
+        "decode_rope": rope_rec,
         "decode_stress": stress,
         "kernels": kernels,
         "profiled_ms_per_step": None if prof_ms_step is None else round(prof_ms_step, 4),
     }
     print(json.dumps(line), flush=True)
+
+
+def run_rope(q, synthkv, torch, p, cfg, dst, out, stream, ev, reps, n_rot, dec_b, dec_avg_ms):
+    Ntot, d = p.n_tokens, p.d
+    rope = torch.from_numpy(synthkv.rope_table(p, 0, Ntot)).to(out.device)
+    log(f"rotated decode: {reps} timed decodes of the whole cache, heads 0..{n_rot - 1} rotated")
+    # before each timed launch a read of 1 GiB evicts the inputs from the
+    # caches (L2 and the 256 MB last-level cache), as the encode's traffic does
+    # before the step's decode
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=out.device).fill_(1.0)
+
+    def timed(**kw):
+        for _ in range(2):
+            q.decode(cfg, dst, 0, Ntot, out=out, stream=stream, **kw)
+        t = 0.0
+        for _ in range(reps):
+            flush.sum()
+            e0 = ev()
+            q.decode(cfg, dst, 0, Ntot, out=out, stream=stream, **kw)
+            e1 = ev()
+            torch.cuda.synchronize()
+            t += e0.elapsed_time(e1)
+        return t / reps
+
+    ms = timed(rope=rope, rope_heads=n_rot)
+    plain_ms = timed()   # the plain decode timed the same way
+    del flush
+    b = dec_b + Ntot * d * 4   # plus the table, read once
+    gbs = b / (ms * 1e-3) / 1e9
+
+    # unfused: the rotation as its own pass over the decoded bf16 keys
+    c, s = rope[..., 0], rope[..., 1]
+
+    def rotate():
+        k = out[:n_rot].float().view(n_rot, Ntot, d // 2, 2)
+        a, bb = k[..., 0], k[..., 1]
+        out[:n_rot] = torch.stack((a * c - bb * s, a * s + bb * c), dim=-1).view(n_rot, Ntot, d).to(out.dtype)
+
+    rotate()
+    e0 = ev()
+    for _ in range(3):
+        rotate()
+    e1 = ev()
+    torch.cuda.synchronize()
+    sep_ms = e0.elapsed_time(e1) / 3
+    return {"launch_us": round(ms * 1e3, 2), "algorithmic_bytes": int(b), "gbs": round(gbs, 1),
+            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "rotated_heads": n_rot,
+            "plain_decode_us": round(plain_ms * 1e3, 2),
+            "plain_decode_in_step_us": round(dec_avg_ms * 1e3, 2),
+            "separate_rotation_pass_us": round(sep_ms * 1e3, 2),
+            "table": "3-D (frame, row, col) rotary table of the 30x52 latent grid, fp32 (cos, sin) per pair",
+            "roofline": dict(kernel="decode_rope", bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS,
+                             unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4), traffic=hbm_traffic("decode_rope"),
+                             avg_launch_us=round(ms * 1e3, 2), algorithmic_per_launch=int(b),
+                             timed="HIP events around each rotated decode launch, on its stream")}
 
 
 def run_stress(q, synthkv, torch, dev, stream, reps):

@@ -71,6 +71,8 @@ _SIGNATURES = {
     "qvg_encode_chunk": (c_int32, [_CFG, c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p,
                                    _VIEW, c_int32, c_void_p, c_uint64, c_void_p]),
     "qvg_decode": (c_int32, [_CFG, _VIEW, c_int64, c_int64, c_void_p, c_int64, c_int32, c_void_p]),
+    "qvg_decode_rope": (c_int32, [_CFG, _VIEW, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int64,
+                                  c_int32, c_void_p]),
     "qvg_kmeans_assign": (c_int32, [c_void_p, c_int32, c_int64, c_void_p, c_int32, c_int32, c_int32,
                                     c_int32, c_void_p, c_int64, c_void_p, c_uint64, c_void_p]),
     "qvg_centroid_update": (c_int32, [c_void_p, c_int32, c_int64, c_void_p, c_int64, c_int32, c_int32,
@@ -208,6 +210,13 @@ def qvg_decode(cfg: qvg_config, src: qvg_cache_view, tok_begin: int, tok_end: in
                out_head_stride: int, out_dtype: int, stream=None) -> None:
     _check(LIB.qvg_decode(ctypes.byref(cfg), ctypes.byref(src), tok_begin, tok_end, _ptr(out),
                           out_head_stride, out_dtype, _stream(stream)), "qvg_decode")
+
+
+def qvg_decode_rope(cfg: qvg_config, src: qvg_cache_view, tok_begin: int, tok_end: int, rope,
+                    rope_heads: int, out, out_head_stride: int, out_dtype: int, stream=None) -> None:
+    _check(LIB.qvg_decode_rope(ctypes.byref(cfg), ctypes.byref(src), tok_begin, tok_end, _ptr(rope),
+                               rope_heads, _ptr(out), out_head_stride, out_dtype, _stream(stream)),
+           "qvg_decode_rope")
 
 
 def qvg_kmeans_assign(x, x_dtype: int, x_head_stride: int, centroids, heads: int, n_tokens: int,

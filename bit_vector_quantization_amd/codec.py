@@ -94,12 +94,22 @@ class Encoder:
 
 
 def decode(cfg: L.qvg_config, src: CompressedKV, tok_begin: int, tok_end: int,
-           out: torch.Tensor | None = None, out_dtype: str = "bf16", stream=None) -> torch.Tensor:
+           out: torch.Tensor | None = None, out_dtype: str = "bf16", stream=None,
+           rope: torch.Tensor | None = None, rope_heads: int | None = None) -> torch.Tensor:
+    """Tokens [tok_begin, tok_end) of every head.  With ``rope`` (fp32
+    [tok_end - tok_begin][d/2][2] of (cos, sin), contiguous, on the device) the
+    first ``rope_heads`` heads (all by default) come out rotated."""
     if out is None:
         dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
         out = torch.empty((src.heads, tok_end - tok_begin, cfg.d), dtype=dt, device=src.codes.device)
     odt = L.QVG_BF16 if out.dtype == torch.bfloat16 else L.QVG_F32
     assert out.stride(2) == 1 and out.stride(1) == cfg.d
-    L.qvg_decode(cfg, src.view, tok_begin, tok_end, out, out.stride(0), odt,
-                 stream or torch.cuda.current_stream())
+    if rope is None:
+        L.qvg_decode(cfg, src.view, tok_begin, tok_end, out, out.stride(0), odt,
+                     stream or torch.cuda.current_stream())
+    else:
+        assert rope.dtype == torch.float32 and rope.is_contiguous()
+        assert tuple(rope.shape) == (tok_end - tok_begin, cfg.d // 2, 2)
+        L.qvg_decode_rope(cfg, src.view, tok_begin, tok_end, rope, src.heads if rope_heads is None else rope_heads,
+                          out, out.stride(0), odt, stream or torch.cuda.current_stream())
     return out

@@ -435,8 +435,9 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
     return QVG_OK;
 }
 
-qvg_status qvg_decode(const qvg_config *cfg, const qvg_cache_view *src, int64_t tok_begin, int64_t tok_end,
-                      void *out, int64_t out_head_stride, int32_t out_dtype, void *stream) {
+static qvg_status decode_impl(const qvg_config *cfg, const qvg_cache_view *src, int64_t tok_begin,
+                              int64_t tok_end, const float *rope, int32_t rope_heads, void *out,
+                              int64_t out_head_stride, int32_t out_dtype, void *stream) {
     qvg_status st = check_config(cfg);
     if (st != QVG_OK) return st;
     if (!src || src->heads < 1 || src->chunk_tokens < 1 || src->cap_tokens < 1) return QVG_ERR_INVALID_ARG;
@@ -468,12 +469,33 @@ qvg_status qvg_decode(const qvg_config *cfg, const qvg_cache_view *src, int64_t 
     a.out = out;
     a.out_dtype = out_dtype;
     a.out_hs = out_head_stride;
+    a.rope = rope;
+    a.rope_heads = rope ? rope_heads : 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t chunks = (tok_end - 1) / a.chunk_tokens - tok_begin / a.chunk_tokens + 1;
-    const double bytes = (double)a.H * ntok * (a.D / 4 + a.D / a.G + a.T + a.D * dtype_size(out_dtype)) +
-                         (double)chunks * a.T * a.H * a.K * a.D * dtype_size(cfg->dtype);
-    QVG_LAUNCH("decode", (double)a.H * ntok * a.D * (a.T + 1), bytes, launch_decode(a, s));
+    double bytes = (double)a.H * ntok * (a.D / 4 + a.D / a.G + a.T + a.D * dtype_size(out_dtype)) +
+                   (double)chunks * a.T * a.H * a.K * a.D * dtype_size(cfg->dtype);
+    double flops = (double)a.H * ntok * a.D * (a.T + 1);
+    if (rope && rope_heads > 0) {
+        bytes += (double)ntok * a.D * 4;             // the rotation table, read once
+        flops += (double)rope_heads * ntok * a.D * 3;  // two products and one sum per output
+        QVG_LAUNCH("decode_rope", flops, bytes, launch_decode(a, s));
+    } else {
+        QVG_LAUNCH("decode", flops, bytes, launch_decode(a, s));
+    }
     return QVG_OK;
+}
+
+qvg_status qvg_decode(const qvg_config *cfg, const qvg_cache_view *src, int64_t tok_begin, int64_t tok_end,
+                      void *out, int64_t out_head_stride, int32_t out_dtype, void *stream) {
+    return decode_impl(cfg, src, tok_begin, tok_end, nullptr, 0, out, out_head_stride, out_dtype, stream);
+}
+
+qvg_status qvg_decode_rope(const qvg_config *cfg, const qvg_cache_view *src, int64_t tok_begin, int64_t tok_end,
+                           const float *rope, int32_t rope_heads, void *out, int64_t out_head_stride,
+                           int32_t out_dtype, void *stream) {
+    if (!rope || !aligned16(rope) || !src || rope_heads < 0 || rope_heads > src->heads) return QVG_ERR_INVALID_ARG;
+    return decode_impl(cfg, src, tok_begin, tok_end, rope, rope_heads, out, out_head_stride, out_dtype, stream);
 }
 
 qvg_status qvg_kmeans_assign(const void *x, int32_t x_dtype, int64_t x_head_stride, const float *centroids,

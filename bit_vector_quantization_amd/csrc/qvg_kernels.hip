@@ -1799,6 +1799,26 @@ __device__ __forceinline__ void store8_out(OutT *p, const float *v) {
     }
 }
 
+// Rotary position embedding of 8 consecutive channels, four adjacent pairs:
+// (a, b) -> (a cos - b sin, a sin + b cos) with cs = cos, sin, cos, sin, ... of
+// the pairs' angles.  Each product and each sum is rounded to fp32 on its own
+// (no fused multiply-add), so the result does not depend on the compiler.
+__device__ __forceinline__ void rope8(const float *cs, float *y) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float a = y[2 * p], b = y[2 * p + 1], c = cs[2 * p], sn = cs[2 * p + 1];
+        y[2 * p] = a * c - b * sn;
+        y[2 * p + 1] = a * sn + b * c;
+    }
+}
+
+__device__ __forceinline__ void load8_f32(const float *p, float *v) {
+    const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
 // The per-token inputs of slice j: two 16-bit code words and two scales.
 template <int D>
 __device__ __forceinline__ void slice_inputs(const uint8_t *codes, const uint8_t *scales, size_t row, int G, int j,
@@ -1811,10 +1831,11 @@ __device__ __forceinline__ void slice_inputs(const uint8_t *codes, const uint8_t
 }
 
 // Dequantise slice j, add the stages' centroid chunks from fetch(t, half, uint4*)
-// for t = T-1 .. 0, and store the two half rows of rb.
+// for t = T-1 .. 0, rotate by the token's cos/sin row rp when it is not null,
+// and store the two half rows of rb.
 template <int D, typename CentT, typename OutT, typename Fetch>
 __device__ __forceinline__ void decode_slice(int T, uint32_t w0, uint32_t w1, uint32_t sc0, uint32_t sc1, int j,
-                                             OutT *rb, Fetch fetch) {
+                                             const float *rp, OutT *rb, Fetch fetch) {
     float y[16];
     dequant8(w0, e4m3_decode(sc0), y);
     dequant8(w1, e4m3_decode(sc1), y + 8);
@@ -1825,6 +1846,13 @@ __device__ __forceinline__ void decode_slice(int T, uint32_t w0, uint32_t w1, ui
             fetch(t, hf, c);
             add8<CentT>(c, y + 8 * hf);
         }
+    }
+    if (rp) {
+        float cs[8];
+        load8_f32(rp + 8 * j, cs);
+        rope8(cs, y);
+        load8_f32(rp + D / 2 + 8 * j, cs);
+        rope8(cs, y + 8);
     }
     store8_out<OutT>(rb + 8 * j, y);
     store8_out<OutT>(rb + D / 2 + 8 * j, y + 8);
@@ -1840,8 +1868,9 @@ template <int D, typename CentT, typename OutT, int TT>
 __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                                 const uint8_t *__restrict__ assign, const CentT *__restrict__ cent,
                                                 int64_t cap, int chunk_tokens, int H, int K, int T_rt, int G,
-                                                int64_t tok_begin, int64_t ntok, OutT *__restrict__ out,
-                                                int64_t out_hs, uint32_t blocks_per_head) {
+                                                int64_t tok_begin, int64_t ntok, const float *__restrict__ rope,
+                                                int rope_heads, OutT *__restrict__ out, int64_t out_hs,
+                                                uint32_t blocks_per_head) {
     constexpr int SL = D / 16;
     constexpr int TPB = 256 / SL;
     constexpr int TS = TT > 0 ? TT : 1;
@@ -1873,7 +1902,8 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ code
         if (!ok[u]) continue;
         const int64_t c = n[u] / chunk_tokens;
         OutT *rb = out + (size_t)h * out_hs + (size_t)(n[u] - tok_begin) * D;
-        decode_slice<D, CentT, OutT>(T, w0[u], w1[u], sc0[u], sc1[u], j, rb, [&](int t, int hf, uint4 *cv) {
+        const float *rp = rope && h < rope_heads ? rope + (size_t)(n[u] - tok_begin) * D : nullptr;
+        decode_slice<D, CentT, OutT>(T, w0[u], w1[u], sc0[u], sc1[u], j, rp, rb, [&](int t, int hf, uint4 *cv) {
             int kk;
             if constexpr (TT > 0) {
                 kk = k[u][t];
@@ -1901,7 +1931,7 @@ constexpr int DEC_LDS_U = 4;
 constexpr int DEC_PARTS = 2;   // workgroups per (chunk, head), each with its part of every row
 constexpr size_t DEC_LDS_MAX = 160 * 1024 - 1024;   // table bytes that fit one workgroup
 
-template <int D, typename CentT, typename OutT, int TT, int PARTS>
+template <int D, typename CentT, typename OutT, int TT, int PARTS, bool ROPE>
 __global__ __launch_bounds__(DEC_LDS_THREADS, PARTS == 2 ? 8 : 4) void k_decode_lds(const uint8_t *__restrict__ codes,
                                                                    const uint8_t *__restrict__ scales,
                                                                    const uint8_t *__restrict__ assign,
@@ -1909,6 +1939,7 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, PARTS == 2 ? 8 : 4) void k_decode_
                                                                    int chunk_tokens, int H, int K, int G,
                                                                    int64_t tok_begin, int64_t tok_end,
                                                                    int64_t c_first, int64_t n_units,
+                                                                   const float *__restrict__ rope, int rope_heads,
                                                                    OutT *__restrict__ out, int64_t out_hs) {
     constexpr int LPT = D / 8 / PARTS;                        // lanes per token (8 channels each)
     constexpr int CHH = D / PARTS * (int)sizeof(CentT) / 16;  // 16-byte chunks per part of a row
@@ -1944,6 +1975,10 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, PARTS == 2 ? 8 : 4) void k_decode_
     const uint8_t *ap = assign + (size_t)h * cap + n0;
     const size_t a_stage = (size_t)H * cap;
     OutT *op = out + (size_t)h * out_hs + (size_t)(n0 - tok_begin) * D + c0;
+    // the rotation table has the output's token rows; pair p of a row is the
+    // float pair (cos, sin) at channels 2p, 2p + 1
+    const float *rp = ROPE ? rope + (size_t)(n0 - tok_begin) * D + c0 : nullptr;
+    const bool rot = ROPE && h < rope_heads;
     const int ntok = (int)(te - n0);   // this thread's tokens: 0, STEP, 2 STEP, ... < ntok
     for (int i0 = 0; i0 < ntok; i0 += STEP * DEC_LDS_U) {
         uint32_t w[DEC_LDS_U], sc[DEC_LDS_U];
@@ -1975,6 +2010,11 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, PARTS == 2 ? 8 : 4) void k_decode_
                 for (int q = 0; q < CP8; ++q) cv[q] = tab[r * CHH + ((CP8 * jj + q) ^ (r & (CHH - 1)))];
                 add8<CentT>(cv, y);
             }
+            if (rot) {
+                float cs[8];
+                load8_f32(rp + (size_t)(i0 + u * STEP) * D, cs);
+                rope8(cs, y);
+            }
             store8_out<OutT>(op + (size_t)(i0 + u * STEP) * D, y);
         }
     }
@@ -1988,13 +2028,18 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
         const int64_t nb = (units + 7) / 8 * 8 * DEC_PARTS;
         if (nb < (int64_t)UINT32_MAX) {
             dim3 g((unsigned)nb), b(DEC_LDS_THREADS);
-#define QVG_DECL(DD, CT, OT, TT)                                                                                  \
+#define QVG_DECL_R(DD, CT, OT, TT, RO)                                                                            \
     do {                                                                                                          \
-        (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, CT, OT, TT, DEC_PARTS>,                                     \
+        (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, CT, OT, TT, DEC_PARTS, RO>,                      \
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)tab_bytes);                    \
-        QVG_KERNEL((k_decode_lds<DD, CT, OT, TT, DEC_PARTS>), g, b, tab_bytes, s, a.codes, a.scales, a.assign,        \
-                           (const CT *)a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.G, a.tok_begin,                  \
-                           a.tok_begin + a.ntok, c0, units, (OT *)a.out, a.out_hs);                               \
+        QVG_KERNEL((k_decode_lds<DD, CT, OT, TT, DEC_PARTS, RO>), g, b, tab_bytes, s, a.codes, a.scales, a.assign, \
+                   (const CT *)a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.G, a.tok_begin, a.tok_begin + a.ntok,   \
+                   c0, units, a.rope, a.rope_heads, (OT *)a.out, a.out_hs);                                       \
+    } while (0)
+#define QVG_DECL(DD, CT, OT, TT)                                   \
+    do {                                                           \
+        if (a.rope) QVG_DECL_R(DD, CT, OT, TT, true);              \
+        else QVG_DECL_R(DD, CT, OT, TT, false);                    \
     } while (0)
 #define QVG_DECL_T(DD, CT, OT)                             \
     do {                                                   \
@@ -2020,6 +2065,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
 #undef QVG_DECL_O
 #undef QVG_DECL_T
 #undef QVG_DECL
+#undef QVG_DECL_R
             return hipGetLastError();
         }
     }
@@ -2028,7 +2074,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     dim3 g(bph * a.H), b(256);
 #define QVG_DEC(DD, CT, OT, TT)                                                                                   \
     QVG_KERNEL((k_decode<DD, CT, OT, TT>), g, b, 0, s, a.codes, a.scales, a.assign, (const CT *)a.cent,    \
-                       a.cap, a.chunk_tokens, a.H, a.K, a.T, a.G, a.tok_begin, a.ntok, (OT *)a.out, a.out_hs, bph)
+                       a.cap, a.chunk_tokens, a.H, a.K, a.T, a.G, a.tok_begin, a.ntok, a.rope, a.rope_heads,     \
+                       (OT *)a.out, a.out_hs, bph)
 #define QVG_DEC_T(DD, CT, OT)                              \
     do {                                                   \
         switch (a.T) {                                     \

@@ -106,7 +106,8 @@ hipError_t launch_quant(int D, int dtype, int H, int N, const Src &src, const vo
                         const uint8_t *pi, int64_t pi_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap,
                         int G, hipStream_t s);
 
-// Fused dequantise + reconstruct of tokens [tok_begin, tok_begin + ntok).
+// Fused dequantise + reconstruct of tokens [tok_begin, tok_begin + ntok), with an
+// optional rotary position embedding of the first rope_heads heads.
 struct DecodeArgs {
     const uint8_t *codes, *scales, *assign;
     const void *cent;
@@ -114,6 +115,10 @@ struct DecodeArgs {
     int64_t cap;
     int chunk_tokens, H, K, T, G, D;
     int64_t tok_begin, ntok;
+    // rotation table [ntok][D/2] of (cos, sin) fp32 pairs for heads < rope_heads,
+    // or null
+    const float *rope = nullptr;
+    int rope_heads = 0;
     void *out;
     int out_dtype;
     int64_t out_hs;

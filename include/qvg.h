@@ -187,6 +187,25 @@ qvg_status qvg_decode(const qvg_config *cfg, const qvg_cache_view *src, int64_t 
                       int64_t tok_end, void *out, int64_t out_head_stride, int32_t out_dtype,
                       void *stream);
 
+/* qvg_decode with the rotary position embedding applied in the same pass.  Keys
+ * are cached before the rotation because that distribution quantises better
+ * (163.com article, section 5, implementation details), so a consumer of the
+ * decoded keys must still rotate them; here that happens before the single
+ * rounding to out_dtype.  The pages do not fix the rotation's layout: pair p of a
+ * row is channels (2p, 2p + 1), and with (c, s) the cos and sin of the pair's
+ * angle for that token,
+ *   (a, b) -> (a*c - b*s, a*s + b*c), every product and sum rounded to fp32.
+ *   rope        device fp32 [tok_end - tok_begin][d/2][2]: (cos, sin) of every pair
+ *               of every decoded token, the same for all heads (any 1-D or
+ *               per-axis 3-D position scheme); 16-byte aligned
+ *   rope_heads  heads [0, rope_heads) are rotated (the keys of a K-then-V
+ *               cache), the rest are decoded as by qvg_decode; 0 <= rope_heads <= H
+ * Other arguments and errors as qvg_decode; a null or misaligned rope, or
+ * rope_heads out of range, is QVG_ERR_INVALID_ARG. */
+qvg_status qvg_decode_rope(const qvg_config *cfg, const qvg_cache_view *src, int64_t tok_begin,
+                           int64_t tok_end, const float *rope, int32_t rope_heads, void *out,
+                           int64_t out_head_stride, int32_t out_dtype, void *stream);
+
 /* ---- stage-level entry points (same conventions), for parity checks and profiling ---- */
 
 /* Workspace the stage-level k-means calls need for (heads, n_tokens, d, K). Host only. */

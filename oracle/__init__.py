@@ -12,5 +12,5 @@ hand-derived fixtures under tests/golden/); no function is "parity unpinned".
 from .formats import bf16_round, e4m3_decode, e4m3_encode, e4m3_values, E4M3_MAX
 from .rng import forgy_indices, forgy_key, shuffle_prefix, splitmix64_next
 from .qvg import (CodecConfig, Encoded, assign, update, lloyd, group_quant, pack2, unpack2,
-                  dequant, encode_chunk, decode_chunk, decode, rtn_reconstruct, mse,
+                  dequant, encode_chunk, decode_chunk, decode, rope_rotate, rtn_reconstruct, mse,
                   kv_cache_bytes, chunk_bytes, compression_ratio, bits_per_value_ratio)

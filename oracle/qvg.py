@@ -39,6 +39,11 @@ Readings taken where the pages are silent (each is also used by the HIP path):
   the low bits.
 * Decode: y = (q - 1.5) * s, then y += C(t)[pi(t)] for t = T .. 1 in fp32,
   then round to the output type.
+* Keys are cached before the rotary position embedding (163.com article,
+  section 5, implementation details), so a decode may rotate them.  The pages
+  do not fix the rotation's layout; pair p is channels (2p, 2p + 1), rotated
+  by the caller's (cos, sin) for that token and pair, each product and sum
+  rounded to fp32, before the one rounding to the output type.
 
 "exact" mode drops the bf16 operand rounding and the float32 rounding of the
 centroids; it exists for the textbook pins (SciPy's k-means) only.
@@ -264,25 +269,48 @@ def encode_chunk(X: np.ndarray, cfg: CodecConfig, cache: Optional[np.ndarray] = 
     return Encoded(codes, scales, asg, cent, new_cache, residuals, sse)
 
 
+def rope_rotate(y: np.ndarray, table: np.ndarray) -> np.ndarray:
+    """Rotary position embedding of fp32 rows y [..., N, d] by table [N][d/2][2]
+    of (cos, sin): channels (2p, 2p + 1) = (a, b) become (a cos - b sin,
+    a sin + b cos).  numpy's float32 arithmetic rounds every product and every
+    sum on its own, which is the rounding the reading above fixes."""
+    y = np.asarray(y, dtype=F32)
+    table = np.asarray(table, dtype=F32)
+    a, b = y[..., 0::2], y[..., 1::2]
+    c, s = table[..., 0], table[..., 1]
+    out = np.empty_like(y)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = a * s + b * c
+    return out
+
+
 def decode_chunk(codes: np.ndarray, scales: np.ndarray, asg: np.ndarray,
-                 cent: np.ndarray, G: int, out: str = "f32") -> np.ndarray:
+                 cent: np.ndarray, G: int, out: str = "f32",
+                 rope: Optional[np.ndarray] = None, rope_heads: Optional[int] = None) -> np.ndarray:
     """Rebuild [H][N][d] from one chunk's stored encoding.
 
     out="f32": fp32 sums in the order dequant + C(T) + ... + C(1);
     out="bf16": the same, rounded to bf16 (returned as float32 values);
-    out="f64": the exact float64 sum (for error bounds)."""
+    out="f64": the exact float64 sum (for error bounds).
+    rope: [N][d/2][2] (cos, sin) that rotates heads [0, rope_heads) (all heads
+    when rope_heads is None) after the fp32 sums and before the rounding to the
+    output type (f32 and bf16 only)."""
     H, N, _ = codes.shape
     T = asg.shape[0]
+    nrot = 0 if rope is None else (H if rope_heads is None else rope_heads)
     ys = []
     for h in range(H):
         y = dequant(codes[h], scales[h], G)
         if out == "f64":
+            assert rope is None
             y = y.astype(np.float64)
             for t in range(T - 1, -1, -1):
                 y = y + cent[t, h].astype(np.float64)[asg[t, h]]
         else:
             for t in range(T - 1, -1, -1):
                 y = (y + cent[t, h][asg[t, h]]).astype(F32)
+            if h < nrot:
+                y = rope_rotate(y, rope)
             if out == "bf16":
                 y = bf16_round(y).astype(F32)
         ys.append(y)

@@ -246,3 +246,31 @@ def gen_torch(p: Preset, tensor: str, device, n_tokens: Optional[int] = None,
         yield X.to(dt)
         done += take
         f += nf
+
+
+def rope_axis_pairs(d: int) -> Tuple[int, int, int]:
+    """How the d/2 rotation pairs of a head split over the three latent axes
+    (frame, grid row, grid column): the rows and columns get 2*(d//6) channels
+    each and the frames the rest (22/21/21 pairs at d = 128)."""
+    hw = 2 * (d // 6)
+    return (d - 2 * hw) // 2, hw // 2, hw // 2
+
+
+def rope_table(p: Preset, tok_begin: int, tok_end: int, base: float = 10000.0) -> np.ndarray:
+    """Per-token rotation table ``[tok_end - tok_begin][d/2][2]`` float32 of
+    (cos, sin) for a 3-D rotary position scheme over the preset's latent grid.
+
+    Token n sits at (frame, row, col) in the token order above.  Pair i of the
+    axis group with g pairs turns by ``position * base**(-i / g)`` radians; the
+    angle, cos and sin are taken in float64 and rounded to float32 once.  This
+    is an input of the decode (the model's position encoding), not part of the
+    codec."""
+    n = np.arange(tok_begin, tok_end, dtype=np.int64)
+    rows, cols = p.grid
+    pos = (n // (rows * cols), (n // cols) % rows, n % cols)
+    ang = []
+    for a, g in enumerate(rope_axis_pairs(p.d)):
+        inv = base ** (-np.arange(g, dtype=np.float64) / g)
+        ang.append(pos[a].astype(np.float64)[:, None] * inv[None, :])
+    ang = np.concatenate(ang, axis=1)
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32)

@@ -146,6 +146,23 @@ def test_decode_argument_errors_launch_nothing(q):
     assert call(view=_view(q, ptr=0)) == q.QVG_ERR_INVALID_ARG
 
 
+def test_decode_rope_argument_errors_launch_nothing(q):
+    g, _ = _cfg(q, synthkv.PRESETS[2])
+    v = _view(q)
+
+    def call(rope=8192, rh=1, b=0, e=100, out=4096, view=v):
+        return q.LIB.qvg_decode_rope(ctypes.byref(g), ctypes.byref(view), b, e, rope, rh, out, 100 * 128,
+                                     q.QVG_BF16, None)
+
+    assert call(rope=None) == q.QVG_ERR_INVALID_ARG
+    assert call(rope=8200) == q.QVG_ERR_INVALID_ARG               # misaligned
+    assert call(rh=-1) == q.QVG_ERR_INVALID_ARG
+    assert call(rh=3) == q.QVG_ERR_INVALID_ARG                    # view holds 2 heads
+    assert call(view=_view(q, ptr=0)) == q.QVG_ERR_INVALID_ARG    # then qvg_decode's own checks
+    assert call(e=101) == q.QVG_ERR_INVALID_ARG
+    assert call(out=None) == q.QVG_ERR_INVALID_ARG
+
+
 def test_stage_entry_point_errors(q):
     L = q.LIB
     assert L.qvg_kmeans_assign(4096, q.QVG_BF16, 128, 4096, 1, 1, 96, 4, 4096, 1, 4096, 1 << 30, None) == -2

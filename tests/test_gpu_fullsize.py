@@ -6,7 +6,9 @@ from the same inputs.
 * 13B-shaped layer: K and V of 40 heads as one 80-head tensor, 38,000 tokens
   in 9 chunks (the last 560 tokens).  Two sampled heads (one key, one value)
   are replayed by the oracle over all 9 chunks, warm starts included, and
-  compared bit for bit, decoded rows too.
+  compared bit for bit, decoded rows too.  The whole cache is then decoded
+  with the 40 key heads rotated by the latent grid's 3-D position table;
+  sampled heads and chunks match the oracle's decode + rotation bit for bit.
 * Aggressive setting: 24 heads, 4 stages, groups of 16, 2 chunks; three heads
   replayed.
 * Long-horizon cache: 24 heads x 1,092,000 tokens (234 chunks).  The oracle
@@ -83,6 +85,22 @@ def test_layer_13b_full_size():
     oc = ocfg(p, "K")   # one codec seed for the layer; the draw is keyed per head
     dst = _encode_all(p, oc, X)
     assert _replay(p, oc, X, dst, heads=[7, 40 + 29], chunks=p.n_chunks) == 0
+    # the whole cache decoded with the keys (heads 0-39) rotated by the latent
+    # grid's 3-D position table, as the benchmark's rotated decode runs it
+    say("  decode with the rotation of the 40 key heads, whole cache")
+    q = lib()
+    rope = synthkv.rope_table(p, 0, p.n_tokens)
+    rope_d = torch.from_numpy(rope).to(DEV)
+    y = q.decode(gcfg(oc), dst, 0, p.n_tokens, out_dtype="bf16", rope=rope_d, rope_heads=p.heads)
+    torch.cuda.synchronize()
+    for c in (0, 4, p.n_chunks - 1):
+        b, e = p.chunk_range(c)
+        g = fetch(dst, c, oc)
+        for h in (0, 7, 39, 40, 69):
+            ref = oracle.decode_chunk(g["codes"][h:h + 1], g["scales"][h:h + 1], g["assign"][:, h:h + 1],
+                                      g["centroids"][:, h:h + 1], oc.group_size, "bf16",
+                                      rope=rope[b:e] if h < p.heads else None)[0]
+            np.testing.assert_array_equal(to_np(y[h, b:e]), ref)
 
 
 def test_aggressive_full_24_heads():
