@@ -20,8 +20,8 @@ decode's algorithmic GB/s (timed with HIP events around each decode launch on
 its stream), a per-kernel breakdown from the library's event profiler, the
 roofline of the dominant kernel, the same decode with the 40 key heads
 rotated by a 3-D rotary position table in the same pass (keys are cached
-before the rotation) next to the rotation run as a separate pass, the
-long-horizon decode stress (12 heads, 700 frames, 1.09 M tokens) and the CPU
+before the rotation) next to the rotation run as a separate pass, one step of
+the aggressive setting (4 stages, groups of 16), the long-horizon decode stress (12 heads, 700 frames, 1.09 M tokens) and the CPU
 oracle timed on a bounded sample.
 """
 from __future__ import annotations
@@ -48,6 +48,8 @@ def parse():
                     help="timed decodes of the 1.09M-token cache (0 skips the stress part)")
     ap.add_argument("--rope-reps", type=int, default=10,
                     help="timed decodes of the layer's cache with the key heads rotated (0 skips)")
+    ap.add_argument("--aggressive-reps", type=int, default=5,
+                    help="timed steps of the aggressive setting (4 stages, G=16; 0 skips)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=3, help="heads in the oracle's timed sample")
     return ap.parse_args()
@@ -247,6 +249,11 @@ def main():
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"]) if kernels else "decode"
     roof = roofs.get(dom, dec_roof)
 
+    # the aggressive setting: 4 stages, groups of 16 (24 heads, 2 chunks)
+    aggressive = None
+    if args.aggressive_reps > 0:
+        aggressive = run_aggressive(q, synthkv, torch, dev, stream, args.aggressive_reps)
+
     # long-horizon decode stress: 12 heads x 128, 700 frames (1,092,000 tokens)
     stress = None
     if args.stress_reps > 0:
@@ -279,6 +286,7 @@ def main():
                    "gbs": round(decode_gbs, 1), "frac_hbm_peak": round(decode_gbs / HBM_PEAK_GBS, 4),
                    "copy_kernel_gbs": round(copy_gbs, 1)},
         "decode_rope": rope_rec,
+        "aggressive": aggressive,
         "decode_stress": stress,
         "kernels": kernels,
         "profiled_ms_per_step": None if prof_ms_step is None else round(prof_ms_step, 4),
@@ -339,6 +347,53 @@ def run_rope(q, synthkv, torch, p, cfg, dst, out, stream, ev, reps, n_rot, dec_b
                              unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4), traffic=hbm_traffic("decode_rope"),
                              avg_launch_us=round(ms * 1e3, 2), algorithmic_per_launch=int(b),
                              timed="HIP events around each rotated decode launch, on its stream")}
+
+
+def run_aggressive(q, synthkv, torch, dev, stream, reps):
+    """One step of the aggressive setting: K and V of 24 heads as one 48-head
+    tensor, 9,360 tokens in 2 chunks (cold, then warm), 4 stages, groups of
+    16, then the decode of both chunks."""
+    p = synthkv.PRESETS[4]
+    H, Ntot, d, K, T, G = p.heads, p.n_tokens, p.d, p.n_centroids, p.n_stages, p.group_size
+    HK = 2 * H
+    log(f"aggressive setting: {HK} heads, {Ntot} tokens, T={T}, G={G}")
+    X = torch.empty((2, H, Ntot, d), dtype=torch.bfloat16, device=dev)
+    for i, t in enumerate(("K", "V")):
+        X[i] = torch.cat(list(synthkv.gen_torch(p, t, dev, frames_per_call=p.chunk_frames)), dim=1)
+    X = X.view(HK, Ntot, d)
+    cfg = q.config(d, K, T, G, p.iters_cold, p.iters_warm, p.codec_seed("K"), p.dtype)
+    dst = q.CompressedKV(cfg, HK, Ntot, p.chunk_tokens, dev)
+    cache = q.CentroidCache(cfg, HK)
+    enc = q.Encoder(cfg, HK, p.chunk_tokens, dev)
+    out = torch.empty((HK, Ntot, d), dtype=torch.bfloat16, device=dev)
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step():
+        cache.reset()
+        marks = [ev()]
+        for c in range(p.n_chunks):
+            b, e = p.chunk_range(c)
+            enc.encode(X[:, b:e], dst, c, cache=cache, stream=stream)
+            marks.append(ev())
+        q.decode(cfg, dst, 0, Ntot, out=out, stream=stream)
+        marks.append(ev())
+        return marks
+
+    step()
+    torch.cuda.synchronize()
+    all_marks = [step() for _ in range(reps)]
+    torch.cuda.synchronize()
+    seg = [sum(m[i].elapsed_time(m[i + 1]) for m in all_marks) / reps for i in range(len(all_marks[0]) - 1)]
+    ms = sum(seg)
+    return {"workload": "aggressive setting: K and V of 24 heads x 128 as one 48-head tensor, 9,360 tokens in "
+                        "2 chunks (cold, warm), 4 stages, 256 centroids, G=16, then the decode",
+            "ms_per_step": round(ms, 4), "vectors_per_s": round(HK * Ntot / (ms * 1e-3), 1),
+            "cold_chunk_ms": round(seg[0], 4), "warm_chunk_ms": round(seg[1], 4),
+            "decode_us": round(seg[-1] * 1e3, 2), "reps": reps}
 
 
 def run_stress(q, synthkv, torch, dev, stream, reps):
