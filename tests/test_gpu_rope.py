@@ -53,14 +53,17 @@ def _same(got, ref):
     np.testing.assert_array_equal(got.view(np.uint32)[~np.isnan(got)], ref.view(np.uint32)[~np.isnan(ref)])
 
 
-def _run(q, arrs, H, cap, chunk, d, K, T, G, dtype, tb, te, rope, rope_heads, out_dtype):
+def _run(q, arrs, H, cap, chunk, d, K, T, G, dtype, tb, te, rope, rope_heads, out_dtype, pad=0):
     codes, scales, asg, cent = arrs
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     keep = [dev(codes), dev(scales), dev(asg), to_dev(cent, dtype)]
     view = q.qvg_cache_view(keep[0].data_ptr(), keep[1].data_ptr(), keep[2].data_ptr(), keep[3].data_ptr(),
                             cap, chunk, H)
     cfg = q.config(d, K, T, G, 2, 2, 7, dtype)
-    out = torch.empty((H, te - tb, d), dtype=torch.float32 if out_dtype == "f32" else torch.bfloat16, device=DEV)
+    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    # pad > 0: heads pad rows apart in a larger buffer whose gaps must stay untouched
+    big = torch.full((H, te - tb + pad, d), 7.0, dtype=dt, device=DEV)
+    out = big[:, :te - tb]
     odt = q.QVG_F32 if out_dtype == "f32" else q.QVG_BF16
     if rope is None:
         q.qvg_decode(cfg, view, tb, te, out, out.stride(0), odt)
@@ -68,6 +71,8 @@ def _run(q, arrs, H, cap, chunk, d, K, T, G, dtype, tb, te, rope, rope_heads, ou
         keep.append(to_dev(rope, "f32"))
         q.qvg_decode_rope(cfg, view, tb, te, keep[-1], rope_heads, out, out.stride(0), odt)
     torch.cuda.synchronize()
+    if pad:
+        assert (big[:, te - tb:] == 7.0).all()
     return to_np(out)
 
 
@@ -114,3 +119,18 @@ def test_decode_rope_zero_heads_and_3d_table():
     got = _run(q, arrs, H, cap, chunk, d, K, T, G, "bf16", tb, te, rope, 1, "bf16")
     _same(got, _reference(arrs, chunk, T, G, tb, te, "bf16", rope, 1))
     _same(got[1], plain[1])
+
+
+def test_decode_rope_head_stride_with_gaps():
+    """Heads written out_head_stride elements apart with gaps between them (the
+    gaps keep their contents), a range that starts and ends inside chunks."""
+    say("decode_rope: output heads with gaps")
+    q = lib()
+    H, cap, chunk, d, K, T, G = 3, 1000, 400, 128, 64, 2, 64
+    rng = np.random.default_rng(9)
+    arrs = _cache(rng, H, cap, chunk, d, K, T, G, "bf16")
+    tb, te = 37, 911
+    rope = _table(rng, te - tb, d)
+    for out in ("bf16", "f32"):
+        got = _run(q, arrs, H, cap, chunk, d, K, T, G, "bf16", tb, te, rope, 2, out, pad=24)
+        _same(got, _reference(arrs, chunk, T, G, tb, te, out, rope, 2))
