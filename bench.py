@@ -50,6 +50,9 @@ def parse():
                     help="timed decodes of the layer's cache with the key heads rotated (0 skips)")
     ap.add_argument("--aggressive-reps", type=int, default=5,
                     help="timed steps of the aggressive setting (4 stages, G=16; 0 skips)")
+    ap.add_argument("--share-reps", type=int, default=5,
+                    help="timed steps of one GPU's share of the layer when its heads are split over 8 GPUs "
+                         "(5 key + 5 value heads; 0 skips)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=3, help="heads in the oracle's timed sample")
     return ap.parse_args()
@@ -249,6 +252,11 @@ def main():
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"]) if kernels else "decode"
     roof = roofs.get(dom, dec_roof)
 
+    # one GPU's share when the layer's 40 heads are split over 8 GPUs by head
+    share = None
+    if args.share_reps > 0:
+        share = run_share(q, synthkv, torch, dev, stream, args.share_reps, H // 8)
+
     # the aggressive setting: 4 stages, groups of 16 (24 heads, 2 chunks)
     aggressive = None
     if args.aggressive_reps > 0:
@@ -287,6 +295,7 @@ def main():
                    "copy_kernel_gbs": round(copy_gbs, 1)},
         "decode_rope": rope_rec,
         "aggressive": aggressive,
+        "head_share_of_8": share,
         "decode_stress": stress,
         "kernels": kernels,
         "profiled_ms_per_step": None if prof_ms_step is None else round(prof_ms_step, 4),
@@ -347,6 +356,47 @@ def run_rope(q, synthkv, torch, p, cfg, dst, out, stream, ev, reps, n_rot, dec_b
                              unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4), traffic=hbm_traffic("decode_rope"),
                              avg_launch_us=round(ms * 1e3, 2), algorithmic_per_launch=int(b),
                              timed="HIP events around each rotated decode launch, on its stream")}
+
+
+def run_share(q, synthkv, torch, dev, stream, reps, heads):
+    """The bench step on one GPU's share of the 13B layer when its heads are
+    split over 8 GPUs (the codec shards by head with no exchange): K and V of
+    `heads` heads, the same 38,000 tokens, 9 chunks, cache, decode."""
+    p = synthkv.PRESETS[3]
+    Ntot, d = p.n_tokens, p.d
+    HK = 2 * heads
+    log(f"one GPU's share of 8: {HK} heads x {Ntot} tokens")
+    X = torch.empty((2, heads, Ntot, d), dtype=torch.bfloat16, device=dev)
+    for i, t in enumerate(("K", "V")):
+        X[i] = torch.cat(list(synthkv.gen_torch(p, t, dev, heads=heads)), dim=1)
+    X = X.view(HK, Ntot, d)
+    cfg = q.config(d, p.n_centroids, p.n_stages, p.group_size, p.iters_cold, p.iters_warm, p.codec_seed("K"),
+                   p.dtype)
+    dst = q.CompressedKV(cfg, HK, Ntot, p.chunk_tokens, dev)
+    cache = q.CentroidCache(cfg, HK)
+    enc = q.Encoder(cfg, HK, p.chunk_tokens, dev)
+    out = torch.empty((HK, Ntot, d), dtype=torch.bfloat16, device=dev)
+
+    def step():
+        cache.reset()
+        for c in range(p.n_chunks):
+            b, e = p.chunk_range(c)
+            enc.encode(X[:, b:e], dst, c, cache=cache, stream=stream)
+        q.decode(cfg, dst, 0, Ntot, out=out, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"workload": f"13B layer, K and V of {heads} heads ({HK} heads), 38,000 tokens in 9 chunks, then the "
+                        "decode: one GPU's share when the 40 heads are split over 8 GPUs",
+            "ms_per_step": round(ms, 4), "vectors_per_s": round(HK * Ntot / (ms * 1e-3), 1), "reps": reps}
 
 
 def run_aggressive(q, synthkv, torch, dev, stream, reps):
