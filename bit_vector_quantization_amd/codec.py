@@ -17,6 +17,21 @@ def _dtype_of(cfg: L.qvg_config) -> torch.dtype:
     return torch.bfloat16 if cfg.dtype == L.QVG_BF16 else torch.float32
 
 
+def _contiguous_for(t: torch.Tensor, stream) -> torch.Tensor:
+    """t itself when contiguous; otherwise a contiguous copy that the caching
+    allocator will not hand out again before the work enqueued on `stream` is
+    done (the library reads it asynchronously there)."""
+    if t.is_contiguous():
+        return t
+    c = t.contiguous()
+    if stream is None or isinstance(stream, torch.cuda.Stream):
+        if stream is not None and stream != torch.cuda.current_stream(c.device):
+            c.record_stream(stream)
+        return c
+    raise ValueError("a non-contiguous tensor needs a torch.cuda.Stream (or none): a raw stream "
+                     "handle cannot keep its contiguous copy alive")
+
+
 class CompressedKV:
     """The compressed cache of one tensor of one layer: codes, scales,
     assignments and per-chunk centroids, plus the qvg_cache_view over them."""
@@ -59,7 +74,7 @@ class CentroidCache:
         return out
 
     def load(self, src: torch.Tensor, stream=None) -> None:
-        L.qvg_centroid_cache_import(self.handle, src.contiguous(), stream or torch.cuda.current_stream())
+        L.qvg_centroid_cache_import(self.handle, _contiguous_for(src, stream), stream or torch.cuda.current_stream())
 
     def close(self) -> None:
         if self.handle is not None:
@@ -88,7 +103,7 @@ class Encoder:
         H, N, d = x.shape
         assert x.stride(2) == 1 and x.stride(1) == d and x.dtype == _dtype_of(self.cfg)
         L.qvg_encode_chunk(self.cfg, x, x.stride(0), H, N,
-                           None if init is None else init.contiguous(),
+                           None if init is None else _contiguous_for(init, stream),
                            None if cache is None else cache.handle, dst.view, chunk_index,
                            self.ws, self.ws_bytes, stream or torch.cuda.current_stream())
 

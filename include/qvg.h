@@ -113,7 +113,10 @@ const char *qvg_status_string(qvg_status status);
  * (out-of-range field) or QVG_ERR_UNSUPPORTED (valid but not implemented). */
 qvg_status qvg_config_validate(const qvg_config *cfg);
 
-/* Bytes one encoded chunk of `heads` x `n_tokens` occupies, by component:
+/* Bytes one encoded chunk of `heads` x `n_tokens` occupies, by component, in
+ * the storage format of the 163.com article (section 5, implementation details:
+ * 2-bit codes with FP8 E4M3 per-group scales; section 7: uint8 assignments of
+ * 256 centroids, group sizes 16 / 64; the stored centroids of every stage):
  * out[0] codes = H*N*d/4, out[1] scales = H*N*d/G, out[2] assignments = T*H*N,
  * out[3] centroids = T*H*K*d*sizeof(dtype).  Host only. */
 qvg_status qvg_chunk_bytes(const qvg_config *cfg, int32_t heads, int32_t n_tokens, uint64_t out[4]);
@@ -224,8 +227,10 @@ qvg_status qvg_kmeans_assign(const void *x, int32_t x_dtype, int64_t x_head_stri
                              void *workspace, uint64_t workspace_bytes, void *stream);
 
 /* k-means update step (same sections): every centroid with at least one token
- * becomes the mean of its tokens' unrounded rows (sum in fp64 in ascending token
- * order, one rounding to fp32); a centroid with none keeps its value.
+ * becomes the mean of its tokens' unrounded rows, defined exactly so that it does
+ * not depend on the order of summation: the exact column sum, rounded once to
+ * fp64, divided by the count in fp64, rounded to fp32.  A centroid with no token
+ * keeps its value.
  *   centroids  device fp32 [H][K][d], read and overwritten
  *   counts_out NULL or device int32 [H][K] tokens per centroid */
 qvg_status qvg_centroid_update(const void *x, int32_t x_dtype, int64_t x_head_stride,
@@ -244,7 +249,9 @@ qvg_status qvg_group_quant(const float *r, int64_t r_head_stride, int32_t heads,
                            void *stream);
 
 /* Fused dequantise-and-reconstruct of one chunk's raw arrays (the kernel behind
- * qvg_decode):
+ * qvg_decode; 163.com article, section 4: reconstruction from the final
+ * quantised residual, adding back each stage's stored centroids in reverse;
+ * section 5: the fused dequantisation kernel; storage format of sections 5 and 7):
  *   codes [H][N][d/4], scales [H][N][d/G], assign [T][H][N] uint8,
  *   centroids [T][H][K][d] (cfg->dtype)  ->  out [H][N][d] (out_dtype), contiguous. */
 qvg_status qvg_dequant_reconstruct(const qvg_config *cfg, int32_t heads, int32_t n_tokens,

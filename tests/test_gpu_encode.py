@@ -168,3 +168,22 @@ def test_tiny_values_need_exact_sums():
 
 def check_chunk_exact(oc, X, g, ora):
     return _check_chunk(oc, X, g, ora, 0, 0, "chunk 0")
+
+
+def test_chunk_over_16384_tokens_uses_the_global_sort_update():
+    """A chunk longer than the LDS token list (16,384): inside the stage loop
+    every update orders the tokens by label in global memory (scatter) and sums
+    one centroid per wave; the encoding must equal the oracle's bit for bit."""
+    say("e2e chunk of 20,000 tokens (global-sort update), 2 heads, K and V")
+    p = synthkv.PRESETS[2]
+    for tensor in ("K", "V"):
+        oc = ocfg(p, tensor, iters_cold=3)
+        X = synthkv.gen_numpy(p, tensor, heads=2, n_tokens=20000)
+        dst, _ = gpu_encode_chunks(oc, X, 20000)
+        g = fetch(dst, 0, oc)
+        q = lib()
+        y = to_np(q.decode(gcfg(oc), dst, 0, 20000, out_dtype="bf16"))
+        for h in range(2):
+            ora = oracle.encode_chunk(X[h:h + 1], oc, head_offset=h)
+            assert _check_chunk(oc, X, g, ora, 0, h, f"{tensor} chunk 0") == 0
+            np.testing.assert_array_equal(y[h], oracle.decode(ora, oc.group_size, "bf16")[0])

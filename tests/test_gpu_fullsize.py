@@ -9,13 +9,15 @@ from the same inputs.
   compared bit for bit, decoded rows too.  The whole cache is then decoded
   with the 40 key heads rotated by the latent grid's 3-D position table;
   sampled heads and chunks match the oracle's decode + rotation bit for bit.
-* Aggressive setting: 24 heads, 4 stages, groups of 16, 2 chunks; three heads
-  replayed.
+* Aggressive setting: 24 heads, 4 stages, groups of 16, 2 chunks, keys and
+  values; three heads of each replayed.
 * Long-horizon cache: 24 heads x 1,092,000 tokens (234 chunks).  The oracle
-  replays chunks 0-1 of two heads; two late chunks of the same heads are
-  checked through properties that hold for any chunk (labels nearest under
-  the HIP path's own centroids, codes the oracle's quantiser of the resulting
-  residual, decoded rows the oracle's reconstruction).
+  replays chunks 0-1 of two heads.  Two late chunks of the same heads are
+  replayed by the oracle from the streaming cache the HIP path held just
+  before them (exported through the C ABI), and also checked through
+  properties that hold for any chunk (labels nearest under the HIP path's own
+  centroids, codes the oracle's quantiser of the resulting residual, decoded
+  rows the oracle's reconstruction).
 
 Inputs come from the device generator; the sampled heads' rows are copied to
 the host for the oracle."""
@@ -31,19 +33,24 @@ from gpu_util import (DEV, check_chunk, check_chunk_properties, fetch, gcfg, lay
 pytestmark = pytest.mark.gpu
 
 
-def _encode_all(p, oc, X):
-    """The benchmark's loop: one encode call per chunk over all heads."""
+def _encode_all(p, oc, X, export_before=()):
+    """The benchmark's loop: one encode call per chunk over all heads.  With
+    export_before, also returns the streaming cache's content (fp32, on the
+    host) just before each of those chunks was encoded."""
     q = lib()
     cfg = gcfg(oc)
     H, N, _ = X.shape
     dst = q.CompressedKV(cfg, H, N, p.chunk_tokens, DEV)
     enc = q.Encoder(cfg, H, p.chunk_tokens, DEV)
     cache = q.CentroidCache(cfg, H)
+    saved = {}
     for c in range(p.n_chunks):
         b, e = p.chunk_range(c)
+        if c in export_before:
+            saved[c] = to_np(cache.export(DEV))
         enc.encode(X[:, b:e], dst, c, cache=cache)
     torch.cuda.synchronize()
-    return dst
+    return (dst, saved) if export_before else dst
 
 
 def _host_heads(X, heads):
@@ -103,11 +110,12 @@ def test_layer_13b_full_size():
             np.testing.assert_array_equal(to_np(y[h, b:e]), ref)
 
 
-def test_aggressive_full_24_heads():
+@pytest.mark.parametrize("tensor", ["K", "V"])
+def test_aggressive_full_24_heads(tensor):
     p = synthkv.PRESETS[4]
-    say("full size: aggressive setting, 24 heads, 4 stages, G=16, 2 chunks")
-    X = torch.cat(list(synthkv.gen_torch(p, "V", DEV, frames_per_call=p.chunk_frames)), dim=1)
-    oc = ocfg(p, "V")
+    say(f"full size: aggressive setting, {tensor}, 24 heads, 4 stages, G=16, 2 chunks")
+    X = torch.cat(list(synthkv.gen_torch(p, tensor, DEV, frames_per_call=p.chunk_frames)), dim=1)
+    oc = ocfg(p, tensor)
     dst = _encode_all(p, oc, X)
     assert _replay(p, oc, X, dst, heads=[0, 11, 23], chunks=p.n_chunks) == 0
 
@@ -117,17 +125,25 @@ def test_long_horizon_sampled_chunks():
     say("full size: long-horizon cache, 24 heads x 1,092,000 tokens, 234 chunks")
     X = layer_on_device(p)
     oc = ocfg(p, "K")
-    dst = _encode_all(p, oc, X)
+    late = (117, p.n_chunks - 1)
+    dst, saved = _encode_all(p, oc, X, export_before=late)
     heads = [3, 12 + 8]
     assert _replay(p, oc, X, dst, heads=heads, chunks=2) == 0
     q = lib()
     hx = _host_heads(X, heads)
-    for c in (117, p.n_chunks - 1):
+    for c in late:
         b, e = p.chunk_range(c)
         g = fetch(dst, c, oc)
         y = to_np(q.decode(gcfg(oc), dst, b, e, out_dtype="bf16"))
         for h in heads:
-            check_chunk_properties(oc, _slice(hx, h, b, e, X.shape[0]), g, h, f"chunk {c}")
+            xs = _slice(hx, h, b, e, X.shape[0])
+            check_chunk_properties(oc, xs, g, h, f"chunk {c}")
+            # the whole chunk replayed by the oracle from the HIP path's own
+            # streaming state: every Lloyd round (labels, exact means, empty
+            # clusters), the stored tables, codes and scales must agree bit for bit
+            say(f"  oracle replay of head {h}, chunk {c}, from the exported cache")
+            ora = oracle.encode_chunk(hx[h][:, b:e], oc, cache=saved[c][:, h:h + 1], head_offset=h)
+            assert check_chunk(oc, xs, g, ora, 0, h, f"chunk {c}") == 0
             ref = oracle.decode_chunk(g["codes"][h:h + 1], g["scales"][h:h + 1], g["assign"][:, h:h + 1],
                                       g["centroids"][:, h:h + 1], oc.group_size, "bf16")[0]
             np.testing.assert_array_equal(y[h], ref)

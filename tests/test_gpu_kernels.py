@@ -153,6 +153,45 @@ def test_assign_matches_oracle_within_tie_rule(which):
         assert not np.any(np.isin(got, [7, 19]))
 
 
+def test_assign_three_centroids_inside_the_fp32_band():
+    """Each token has three candidate centroids whose exact distances differ by
+    2^-14 .. 9 * 2^-14 while |x|^2 is about 2e6 (value-like outlier channels),
+    far inside the matrix cores' fp32 error band, and the exact nearest has the
+    highest index of the three.  The fp32 ranking of the three is then noise,
+    and the fp64 re-decision sees only the fp32 top two, so the exact nearest
+    can be missed.  Whatever the kernel returns must obey the near-tie rule
+    (relative gap < 1e-4) and be one of the three; the outcome is printed."""
+    say("kmeans_assign, three centroids within the fp32 error band")
+    q = lib()
+    rng = np.random.default_rng(21)
+    d, B, K = 128, 64, 256
+    base = oracle.bf16_round(rng.standard_normal((B, d))).astype(np.float32)
+    base[:, 7] = oracle.bf16_round(1000.0 * (1 + 0.1 * rng.standard_normal(B)))
+    base[:, 99] = oracle.bf16_round(-1000.0 * (1 + 0.1 * rng.standard_normal(B)))
+    base[:, 10:13] = 1.0 + np.float32(2.0 ** -7) * rng.integers(0, 64, (B, 3))
+    C = np.empty((1, K, d), np.float32)
+    C[0, 3 * B:] = oracle.bf16_round(rng.standard_normal((K - 3 * B, d)) * 30)
+    for b in range(B):
+        for j in range(3):                       # distances (3 - j)^2 2^-14: index 3b + 2 is nearest
+            C[0, 3 * b + j] = base[b]
+            C[0, 3 * b + j, 10 + j] += np.float32((3 - j) * 2.0 ** -7)
+    X = np.repeat(base, 16, axis=0)[None].copy()   # 16 tokens per base, all equal to it
+    N = X.shape[1]
+    ws_bytes = q.qvg_stage_workspace_bytes(1, N, d, K)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    out = torch.empty((1, N), dtype=torch.uint8, device=DEV)
+    q.qvg_kmeans_assign(to_dev(X, "bf16"), q.QVG_BF16, N * d, to_dev(C, "f32"), 1, N, d, K, out, N, ws, ws_bytes)
+    torch.cuda.synchronize()
+    got = to_np(out)[0].astype(int)
+    ref = oracle.assign(X[0], C[0], "parity")
+    np.testing.assert_array_equal(ref, 3 * (np.arange(N) // 16) + 2)
+    n_mis, worst = gap_ok(X[0], C[0], got, ref)
+    say(f"  tokens {N}: exact nearest returned for {N - n_mis}, another of the three for {n_mis} "
+        f"(worst relative gap {worst:.3g})")
+    assert worst < 1e-4
+    assert np.all(got // 3 == np.arange(N) // 16)
+
+
 def test_assign_from_fp32_input_rounds_operands():
     say("kmeans_assign fp32 input")
     q = lib()
