@@ -70,6 +70,8 @@ _SIGNATURES = {
     "qvg_centroid_cache_import": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "qvg_encode_chunk": (c_int32, [_CFG, c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p,
                                    _VIEW, c_int32, c_void_p, c_uint64, c_void_p]),
+    "qvg_encode_chunk_static": (c_int32, [_CFG, c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p,
+                                          _VIEW, c_int32, c_void_p]),
     "qvg_decode": (c_int32, [_CFG, _VIEW, c_int64, c_int64, c_void_p, c_int64, c_int32, c_void_p]),
     "qvg_decode_rope": (c_int32, [_CFG, _VIEW, c_int64, c_int64, c_void_p, c_int32, c_void_p, c_int64,
                                   c_int32, c_void_p]),
@@ -204,6 +206,17 @@ def qvg_encode_chunk(cfg: qvg_config, x, x_head_stride: int, heads: int, n_token
                                 _ptr(init_centroids), cache, ctypes.byref(dst), chunk_index,
                                 _ptr(workspace), workspace_bytes, _stream(stream)),
            "qvg_encode_chunk")
+
+
+QVG_STATIC_SCRATCH_BYTES = 64 << 20   # the fixed scratch array of qvg_encode_chunk_static
+
+
+def qvg_encode_chunk_static(cfg: qvg_config, x, x_head_stride: int, heads: int, n_tokens: int,
+                            init_centroids, cache, dst: qvg_cache_view, chunk_index: int, stream=None) -> None:
+    _check(LIB.qvg_encode_chunk_static(ctypes.byref(cfg), _ptr(x), x_head_stride, heads, n_tokens,
+                                       _ptr(init_centroids), cache, ctypes.byref(dst), chunk_index,
+                                       _stream(stream)),
+           "qvg_encode_chunk_static")
 
 
 def qvg_decode(cfg: qvg_config, src: qvg_cache_view, tok_begin: int, tok_end: int, out,

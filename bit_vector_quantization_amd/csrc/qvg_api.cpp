@@ -310,10 +310,10 @@ qvg_status qvg_centroid_cache_import(qvg_centroid_cache *cache, const float *src
     return QVG_OK;
 }
 
-qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head_stride, int32_t heads,
-                            int32_t n_tokens, const float *init_centroids, qvg_centroid_cache *cache,
-                            const qvg_cache_view *dst, int32_t chunk_index, void *workspace,
-                            uint64_t workspace_bytes, void *stream) {
+static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_head_stride, int32_t heads,
+                              int32_t n_tokens, const float *init_centroids, qvg_centroid_cache *cache,
+                              const qvg_cache_view *dst, int32_t chunk_index, void *workspace,
+                              uint64_t workspace_bytes, void *stream) {
     qvg_status st = check_config(cfg);
     if (st != QVG_OK) return st;
     const int H = heads, N = n_tokens, D = cfg->d, K = cfg->n_centroids, T = cfg->n_stages, G = cfg->group_size;
@@ -433,6 +433,27 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
     }
     if (cache) cache->valid = 1;
     return QVG_OK;
+}
+
+qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head_stride, int32_t heads,
+                            int32_t n_tokens, const float *init_centroids, qvg_centroid_cache *cache,
+                            const qvg_cache_view *dst, int32_t chunk_index, void *workspace,
+                            uint64_t workspace_bytes, void *stream) {
+    return encode_impl(cfg, x, x_head_stride, heads, n_tokens, init_centroids, cache, dst, chunk_index, workspace,
+                       workspace_bytes, stream);
+}
+
+qvg_status qvg_encode_chunk_static(const qvg_config *cfg, const void *x, int64_t x_head_stride, int32_t heads,
+                                   int32_t n_tokens, const float *init_centroids, qvg_centroid_cache *cache,
+                                   const qvg_cache_view *dst, int32_t chunk_index, void *stream) {
+    qvg_status st = check_config(cfg);
+    if (st != QVG_OK) return st;
+    if (heads < 1 || n_tokens < 1) return QVG_ERR_INVALID_ARG;
+    if (EncodeWorkspace(*cfg, heads, n_tokens).total > STATIC_SCRATCH_BYTES) return QVG_ERR_WORKSPACE;
+    void *ws = nullptr;
+    QVG_TRY(static_scratch(&ws));
+    return encode_impl(cfg, x, x_head_stride, heads, n_tokens, init_centroids, cache, dst, chunk_index, ws,
+                       STATIC_SCRATCH_BYTES, stream);
 }
 
 static qvg_status decode_impl(const qvg_config *cfg, const qvg_cache_view *src, int64_t tok_begin,

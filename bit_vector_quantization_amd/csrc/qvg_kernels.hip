@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 
 
 #include "qvg_launch.h"
@@ -2103,6 +2104,35 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
 #undef QVG_DEC_T
 #undef QVG_DEC
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fixed device scratch of the entry point that allocates nothing
+// ---------------------------------------------------------------------------
+
+// One array per GPU, loaded with the code object and held until the process
+// ends.  In host code `scratch` names only a host-side stand-in: kernels get
+// the device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
+
+hipError_t static_scratch(void **ptr) {
+    constexpr int MAX_DEVICES = 64;
+    static std::mutex mu;
+    static void *addr[MAX_DEVICES] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

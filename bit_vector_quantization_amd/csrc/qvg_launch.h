@@ -133,6 +133,11 @@ struct LaunchEvents {
 };
 LaunchEvents &launch_events();
 
+// Device address, on the current device, of the library's fixed scratch array
+// of STATIC_SCRATCH_BYTES (looked up once per device, then reused).
+constexpr size_t STATIC_SCRATCH_BYTES = (size_t)64 << 20;
+hipError_t static_scratch(void **ptr);
+
 // Fills n int32 with zero.
 hipError_t launch_zero(int32_t *p, int64_t n, hipStream_t s);
 

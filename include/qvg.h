@@ -178,6 +178,26 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
                             int32_t chunk_index, void *workspace, uint64_t workspace_bytes,
                             void *stream);
 
+/* qvg_encode_chunk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same encode, bit for bit, with the workspace taken from a fixed device
+ * array of QVG_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends.  The call allocates and frees nothing.
+ *   Limit: qvg_encode_workspace_bytes(cfg, heads, n_tokens) must not exceed
+ *   QVG_STATIC_SCRATCH_BYTES (at d = 128, K = 256, T = 2, bf16: up to 45 heads
+ *   of a 4,680-token chunk); a larger call returns QVG_ERR_WORKSPACE and
+ *   launches nothing.
+ *   Every call on one GPU uses that GPU's one array, and its contents on entry
+ *   do not matter: calls that overlap on one GPU (two streams, or two threads)
+ *   race on it and must not be made.  The first call on a device looks the
+ *   array's address up (QVG_ERR_HIP if that fails).
+ * Other arguments, results and errors as qvg_encode_chunk. */
+#define QVG_STATIC_SCRATCH_BYTES ((uint64_t)64 << 20)
+qvg_status qvg_encode_chunk_static(const qvg_config *cfg, const void *x, int64_t x_head_stride,
+                                   int32_t heads, int32_t n_tokens, const float *init_centroids,
+                                   qvg_centroid_cache *cache, const qvg_cache_view *dst,
+                                   int32_t chunk_index, void *stream);
+
 /* Rebuilds tokens [tok_begin, tok_end) of every head from `src` in one fused pass
  * (163.com article, sections 4-5: reconstruction in reverse stage order; fused
  * dequantise-and-centroid kernel; gist.science summaries, section 2C):
