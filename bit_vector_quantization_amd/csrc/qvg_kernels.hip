@@ -1922,30 +1922,55 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ code
 
 // Tables in LDS: one workgroup per (chunk, head, half row) stages that half of
 // the chunk's T centroid tables of the head (swizzled 16-byte chunks, 64 KiB at
-// T = 2, K = 256, d = 128, so two workgroups share a CU; PARTS = 1 would take
-// whole rows) and streams the chunk's tokens.  Lane jj of a token's D/16 lanes owns 8 channels, so one store
-// instruction writes 128 contiguous bytes per token; each thread keeps its lane
-// and walks tokens with a fixed stride, DEC_LDS_U tokens per trip with all their
-// global loads issued together.
+// T = 2, K = 256, d = 128, so two workgroups share a CU) and streams the chunk's
+// tokens in trips of DEC_TRIP.  Each trip's codes, scales and assignments are
+// first brought into LDS by one wide load per thread (the half row's codes of a
+// token in one 8- or 16-byte load, its scale bytes in one load, one assignment
+// byte per stage), instead of the 2 + 1 + T loads of 1-2 bytes that every lane
+// of a token would otherwise issue.  Lane jj of a token's D/16 lanes then owns
+// 8 channels, so one store instruction writes 128 contiguous bytes per token.
 constexpr int DEC_LDS_THREADS = 1024;
-constexpr int DEC_LDS_U = 4;
-constexpr int DEC_PARTS = 2;   // workgroups per (chunk, head), each with its part of every row
-constexpr size_t DEC_LDS_MAX = 160 * 1024 - 1024;   // table bytes that fit one workgroup
+constexpr int DEC_TRIP = 512;   // tokens per trip
+constexpr int DEC_PARTS = 2;    // workgroups per (chunk, head), each with its part of every row
+constexpr size_t DEC_LDS_MAX = 160 * 1024 - 1024;   // LDS bytes one workgroup may take
 
-template <int D, typename CentT, typename OutT, int TT, int PARTS, bool ROPE>
-__global__ __launch_bounds__(DEC_LDS_THREADS, PARTS == 2 ? 8 : 4) void k_decode_lds(const uint8_t *__restrict__ codes,
+// LDS bytes of one trip's staged codes, scales and assignments.
+constexpr size_t dec_meta_bytes(int D, int G, int T) {
+    return (size_t)DEC_TRIP * (D / 4 / DEC_PARTS) + (size_t)DEC_TRIP * (D / DEC_PARTS >= G ? D / DEC_PARTS / G : 1) +
+           (size_t)T * DEC_TRIP;
+}
+
+// One token's scale bytes of part hf: SPT bytes (1, 2 or 4) in one load.
+template <int SPT>
+__device__ __forceinline__ uint32_t load_scales(const uint8_t *p) {
+    if constexpr (SPT == 4) return *reinterpret_cast<const uint32_t *>(p);
+    else if constexpr (SPT == 2) return *reinterpret_cast<const uint16_t *>(p);
+    else return *p;
+}
+
+template <int D, int G, typename CentT, typename OutT, int TT, bool ROPE>
+__global__ __launch_bounds__(DEC_LDS_THREADS, 8) void k_decode_lds(const uint8_t *__restrict__ codes,
                                                                    const uint8_t *__restrict__ scales,
                                                                    const uint8_t *__restrict__ assign,
                                                                    const CentT *__restrict__ cent, int64_t cap,
-                                                                   int chunk_tokens, int H, int K, int G,
+                                                                   int chunk_tokens, int H, int K,
                                                                    int64_t tok_begin, int64_t tok_end,
                                                                    int64_t c_first, int64_t n_units,
                                                                    const float *__restrict__ rope, int rope_heads,
                                                                    OutT *__restrict__ out, int64_t out_hs) {
-    constexpr int LPT = D / 8 / PARTS;                        // lanes per token (8 channels each)
-    constexpr int CHH = D / PARTS * (int)sizeof(CentT) / 16;  // 16-byte chunks per part of a row
+    constexpr int PARTS = DEC_PARTS;
+    constexpr int DP = D / PARTS;                             // channels of a part
+    constexpr int LPT = DP / 8;                               // lanes per token (8 channels each)
+    constexpr int CHH = DP * (int)sizeof(CentT) / 16;         // 16-byte chunks per part of a row
     constexpr int CP8 = 8 * (int)sizeof(CentT) / 16;          // chunks per 8 channels (1 bf16, 2 fp32)
+    constexpr int CB = DP / 4;                                // code bytes of a part of a token (8 or 16)
+    constexpr int SPT = DP >= G ? DP / G : 1;                 // scale bytes of a part of a token
+    constexpr int STEP = DEC_LDS_THREADS / LPT;               // tokens per pass
+    static_assert(DEC_TRIP % STEP == 0 && 2 * DEC_TRIP <= DEC_LDS_THREADS, "trip layout");
     extern __shared__ uint4 tab[];
+    uint8_t *mcodes = reinterpret_cast<uint8_t *>(tab + TT * K * CHH);   // [DEC_TRIP][CB]
+    uint8_t *msc = mcodes + DEC_TRIP * CB;                                 // [DEC_TRIP][SPT]
+    uint8_t *mlab = msc + DEC_TRIP * SPT;                                  // [TT][DEC_TRIP]
     // The PARTS workgroups of one (chunk, head) are 8 apart in dispatch order:
     // the same XCD, running together, so a code line fetched by one is still in
     // that XCD's L2 for the other.  Workgroups past the last (chunk, head) of a
@@ -1964,104 +1989,138 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, PARTS == 2 ? 8 : 4) void k_decode_
             tab[r * CHH + (q ^ (r & (CHH - 1)))] = src[(size_t)row * PARTS * CHH + hf * CHH + q];
         }
     }
-    __syncthreads();
     const int64_t tb = max(tok_begin, c * chunk_tokens), te = min(tok_end, (c + 1) * chunk_tokens);
-    constexpr int STEP = DEC_LDS_THREADS / LPT;
-    const int jj = tid % LPT;
-    const int c0 = hf * (D / PARTS) + 8 * jj;   // first channel of the lane
-    const int64_t n0 = tb + tid / LPT;
-    const size_t row0 = (size_t)h * cap + n0;
-    const uint16_t *cp = reinterpret_cast<const uint16_t *>(codes) + row0 * (D / 8) + c0 / 8;
-    const uint8_t *sp = scales + row0 * (D / G) + c0 / G;
-    const uint8_t *ap = assign + (size_t)h * cap + n0;
+    const size_t hrow = (size_t)h * cap;
     const size_t a_stage = (size_t)H * cap;
-    OutT *op = out + (size_t)h * out_hs + (size_t)(n0 - tok_begin) * D + c0;
-    // the rotation table has the output's token rows; pair p of a row is the
-    // float pair (cos, sin) at channels 2p, 2p + 1
-    const float *rp = ROPE ? rope + (size_t)(n0 - tok_begin) * D + c0 : nullptr;
+    const int jj = tid % LPT, slot = tid / LPT;
+    const int c0 = hf * DP + 8 * jj;   // first channel of the lane
+    const int sofs = DP >= G ? (8 * jj) / G : 0;   // the lane's scale byte among its token's SPT
+    OutT *const oh = out + (size_t)h * out_hs + c0;
     const bool rot = ROPE && h < rope_heads;
-    const int ntok = (int)(te - n0);   // this thread's tokens: 0, STEP, 2 STEP, ... < ntok
-    for (int i0 = 0; i0 < ntok; i0 += STEP * DEC_LDS_U) {
-        uint32_t w[DEC_LDS_U], sc[DEC_LDS_U];
-        int k[DEC_LDS_U][TT];
-        bool ok[DEC_LDS_U];
-#pragma unroll
-        for (int u = 0; u < DEC_LDS_U; ++u) {
-            const int i = i0 + u * STEP;
-            ok[u] = i < ntok;
-            const int ii = ok[u] ? i : i0;
-            w[u] = cp[(size_t)ii * (D / 8)];
-            sc[u] = sp[(size_t)ii * (D / G)];
-#pragma unroll
-            for (int t = 0; t < TT; ++t) {
-                const int kk = ap[t * a_stage + ii];
-                k[u][t] = kk < K ? kk : K - 1;   // a corrupt byte cannot leave the chunk's table
+    for (int64_t i0 = tb; i0 < te; i0 += DEC_TRIP) {
+        const int nt = (int)min((int64_t)DEC_TRIP, te - i0);
+        // this trip's inputs, one wide load per thread (tokens past the trip's
+        // end read its last token again and are never used)
+        const int ms = tid & (DEC_TRIP - 1);
+        const int64_t n = i0 + min(ms, nt - 1);
+        uint4 cv = make_uint4(0, 0, 0, 0);
+        uint32_t sv = 0;
+        uint32_t lv[(TT + 1) / 2];
+        if (tid < DEC_TRIP) {
+            const uint8_t *cp = codes + (hrow + n) * (D / 4) + hf * CB;
+            if constexpr (CB == 16) {
+                cv = *reinterpret_cast<const uint4 *>(cp);
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2 *>(cp);
+                cv.x = v.x;
+                cv.y = v.y;
             }
+        } else {
+            sv = load_scales<SPT>(scales + (hrow + n) * (D / G) + (DP >= G ? hf * SPT : (hf * DP) / G));
         }
 #pragma unroll
-        for (int u = 0; u < DEC_LDS_U; ++u) {
-            if (!ok[u]) continue;
+        for (int m = 0; m < (TT + 1) / 2; ++m) {   // stage 2m + (tid >= DEC_TRIP)
+            const int t = 2 * m + (tid >= DEC_TRIP ? 1 : 0);
+            lv[m] = t < TT ? assign[t * a_stage + hrow + n] : 0u;
+        }
+        __syncthreads();   // the previous trip's readers are done
+        if (tid < DEC_TRIP) {
+            if constexpr (CB == 16) reinterpret_cast<uint4 *>(mcodes)[ms] = cv;
+            else reinterpret_cast<uint2 *>(mcodes)[ms] = make_uint2(cv.x, cv.y);
+        } else {
+            if constexpr (SPT == 4) reinterpret_cast<uint32_t *>(msc)[ms] = sv;
+            else if constexpr (SPT == 2) reinterpret_cast<uint16_t *>(msc)[ms] = (uint16_t)sv;
+            else msc[ms] = (uint8_t)sv;
+        }
+#pragma unroll
+        for (int m = 0; m < (TT + 1) / 2; ++m) {
+            const int t = 2 * m + (tid >= DEC_TRIP ? 1 : 0);
+            if (t < TT) mlab[t * DEC_TRIP + ms] = (uint8_t)lv[m];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < DEC_TRIP / STEP; ++u) {
+            const int i = u * STEP + slot;
+            if (i >= nt) break;
+            const uint32_t w = reinterpret_cast<const uint16_t *>(mcodes)[i * (CB / 2) + jj];
             float y[8];
-            dequant8(w[u], e4m3_decode(sc[u]), y);
+            dequant8(w, e4m3_decode(msc[i * SPT + sofs]), y);
 #pragma unroll
             for (int t = TT - 1; t >= 0; --t) {
-                const int r = t * K + k[u][t];
-                uint4 cv[CP8];
+                const int kk = mlab[t * DEC_TRIP + i];
+                const int r = t * K + (kk < K ? kk : K - 1);   // a corrupt byte cannot leave the chunk's table
+                uint4 cv8[CP8];
 #pragma unroll
-                for (int q = 0; q < CP8; ++q) cv[q] = tab[r * CHH + ((CP8 * jj + q) ^ (r & (CHH - 1)))];
-                add8<CentT>(cv, y);
+                for (int q = 0; q < CP8; ++q) cv8[q] = tab[r * CHH + ((CP8 * jj + q) ^ (r & (CHH - 1)))];
+                add8<CentT>(cv8, y);
             }
+            const size_t orow = (size_t)(i0 + i - tok_begin) * D;
             if (rot) {
+                // the rotation table has the output's token rows; pair p of a row
+                // is the float pair (cos, sin) at channels 2p, 2p + 1
                 float cs[8];
-                load8_f32(rp + (size_t)(i0 + u * STEP) * D, cs);
+                load8_f32(rope + orow + c0, cs);
                 rope8(cs, y);
             }
-            store8_out<OutT>(op + (size_t)(i0 + u * STEP) * D, y);
+            store8_out<OutT>(oh + orow, y);
         }
     }
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const size_t tab_bytes = (size_t)a.T * a.K * (a.D / DEC_PARTS) * (a.cent_dtype == DT_BF16 ? 2 : 4);
-    if (a.T >= 1 && a.T <= 4 && tab_bytes <= DEC_LDS_MAX) {
+    const size_t lds = tab_bytes + dec_meta_bytes(a.D, a.G, a.T);
+    // the staged loads need the scale bytes of a part aligned to their size
+    const bool scales_aligned = (reinterpret_cast<uintptr_t>(a.scales) & 3u) == 0;
+    if (a.T >= 1 && a.T <= 4 && lds <= DEC_LDS_MAX && scales_aligned) {
         const int64_t c0 = a.tok_begin / a.chunk_tokens, c1 = (a.tok_begin + a.ntok - 1) / a.chunk_tokens;
         const int64_t units = (c1 - c0 + 1) * a.H;   // (chunk, head) pairs
         const int64_t nb = (units + 7) / 8 * 8 * DEC_PARTS;
         if (nb < (int64_t)UINT32_MAX) {
             dim3 g((unsigned)nb), b(DEC_LDS_THREADS);
-#define QVG_DECL_R(DD, CT, OT, TT, RO)                                                                            \
+#define QVG_DECL_R(DD, GG, CT, OT, TT, RO)                                                                        \
     do {                                                                                                          \
-        (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, CT, OT, TT, DEC_PARTS, RO>,                      \
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)tab_bytes);                    \
-        QVG_KERNEL((k_decode_lds<DD, CT, OT, TT, DEC_PARTS, RO>), g, b, tab_bytes, s, a.codes, a.scales, a.assign, \
-                   (const CT *)a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.G, a.tok_begin, a.tok_begin + a.ntok,   \
-                   c0, units, a.rope, a.rope_heads, (OT *)a.out, a.out_hs);                                       \
+        (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, GG, CT, OT, TT, RO>,                             \
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                          \
+        QVG_KERNEL((k_decode_lds<DD, GG, CT, OT, TT, RO>), g, b, lds, s, a.codes, a.scales, a.assign,             \
+                   (const CT *)a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.tok_begin, a.tok_begin + a.ntok, c0,    \
+                   units, a.rope, a.rope_heads, (OT *)a.out, a.out_hs);                                           \
     } while (0)
-#define QVG_DECL(DD, CT, OT, TT)                                   \
+#define QVG_DECL(DD, GG, CT, OT, TT)                               \
     do {                                                           \
-        if (a.rope) QVG_DECL_R(DD, CT, OT, TT, true);              \
-        else QVG_DECL_R(DD, CT, OT, TT, false);                    \
+        if (a.rope) QVG_DECL_R(DD, GG, CT, OT, TT, true);          \
+        else QVG_DECL_R(DD, GG, CT, OT, TT, false);                \
     } while (0)
-#define QVG_DECL_T(DD, CT, OT)                             \
+#define QVG_DECL_T(DD, GG, CT, OT)                         \
     do {                                                   \
         switch (a.T) {                                     \
-            case 1: QVG_DECL(DD, CT, OT, 1); break;        \
-            case 2: QVG_DECL(DD, CT, OT, 2); break;        \
-            case 3: QVG_DECL(DD, CT, OT, 3); break;        \
-            default: QVG_DECL(DD, CT, OT, 4); break;       \
+            case 1: QVG_DECL(DD, GG, CT, OT, 1); break;    \
+            case 2: QVG_DECL(DD, GG, CT, OT, 2); break;    \
+            case 3: QVG_DECL(DD, GG, CT, OT, 3); break;    \
+            default: QVG_DECL(DD, GG, CT, OT, 4); break;   \
         }                                                  \
     } while (0)
-#define QVG_DECL_O(DD, CT)                                 \
+#define QVG_DECL_O(DD, GG, CT)                             \
     do {                                                   \
-        if (a.out_dtype == DT_BF16) QVG_DECL_T(DD, CT, uint16_t); \
-        else QVG_DECL_T(DD, CT, float);                    \
+        if (a.out_dtype == DT_BF16) QVG_DECL_T(DD, GG, CT, uint16_t); \
+        else QVG_DECL_T(DD, GG, CT, float);                \
     } while (0)
-#define QVG_DECL_C(DD)                                     \
+#define QVG_DECL_C(DD, GG)                                 \
     do {                                                   \
-        if (a.cent_dtype == DT_BF16) QVG_DECL_O(DD, uint16_t); \
-        else QVG_DECL_O(DD, float);                        \
+        if (a.cent_dtype == DT_BF16) QVG_DECL_O(DD, GG, uint16_t); \
+        else QVG_DECL_O(DD, GG, float);                    \
     } while (0)
-            if (a.D == 128) QVG_DECL_C(128); else QVG_DECL_C(64);
+#define QVG_DECL_G(DD)                                     \
+    do {                                                   \
+        switch (a.G) {                                     \
+            case 16: QVG_DECL_C(DD, 16); break;            \
+            case 32: QVG_DECL_C(DD, 32); break;            \
+            case 64: QVG_DECL_C(DD, 64); break;            \
+            default: QVG_DECL_C(DD, 128); break;           \
+        }                                                  \
+    } while (0)
+            if (a.D == 128) QVG_DECL_G(128); else QVG_DECL_G(64);
+#undef QVG_DECL_G
 #undef QVG_DECL_C
 #undef QVG_DECL_O
 #undef QVG_DECL_T
