@@ -37,7 +37,7 @@ class QvgError(RuntimeError):
 class qvg_config(ctypes.Structure):
     _fields_ = [("d", c_int32), ("n_centroids", c_int32), ("n_stages", c_int32),
                 ("group_size", c_int32), ("iters_cold", c_int32), ("iters_warm", c_int32),
-                ("seed", c_uint64), ("dtype", c_int32), ("reserved", c_int32)]
+                ("seed", c_uint64), ("dtype", c_int32), ("converge", c_int32)]
 
 
 class qvg_cache_view(ctypes.Structure):
@@ -70,6 +70,7 @@ _SIGNATURES = {
     "qvg_centroid_cache_import": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "qvg_encode_chunk": (c_int32, [_CFG, c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p,
                                    _VIEW, c_int32, c_void_p, c_uint64, c_void_p]),
+    "qvg_encode_rounds": (c_int32, [_CFG, c_int32, c_int32, c_void_p, c_uint64, c_void_p, c_void_p]),
     "qvg_encode_chunk_static": (c_int32, [_CFG, c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p,
                                           _VIEW, c_int32, c_void_p]),
     "qvg_decode": (c_int32, [_CFG, _VIEW, c_int64, c_int64, c_void_p, c_int64, c_int32, c_void_p]),
@@ -132,8 +133,8 @@ def _stream(s) -> int | None:
 
 
 def make_config(d: int, n_centroids: int, n_stages: int, group_size: int, iters_cold: int,
-                iters_warm: int, seed: int, dtype: int) -> qvg_config:
-    return qvg_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dtype, 0)
+                iters_warm: int, seed: int, dtype: int, converge: int = 0) -> qvg_config:
+    return qvg_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dtype, converge)
 
 
 # ---- entry points (same names as the C ABI) --------------------------------
@@ -206,6 +207,12 @@ def qvg_encode_chunk(cfg: qvg_config, x, x_head_stride: int, heads: int, n_token
                                 _ptr(init_centroids), cache, ctypes.byref(dst), chunk_index,
                                 _ptr(workspace), workspace_bytes, _stream(stream)),
            "qvg_encode_chunk")
+
+
+def qvg_encode_rounds(cfg: qvg_config, heads: int, n_tokens: int, workspace, workspace_bytes: int, rounds_out,
+                      stream=None) -> None:
+    _check(LIB.qvg_encode_rounds(ctypes.byref(cfg), heads, n_tokens, _ptr(workspace), workspace_bytes,
+                                 _ptr(rounds_out), _stream(stream)), "qvg_encode_rounds")
 
 
 QVG_STATIC_SCRATCH_BYTES = 64 << 20   # the fixed scratch array of qvg_encode_chunk_static

@@ -8,9 +8,9 @@ from . import _lib as L
 
 
 def config(d: int, n_centroids: int, n_stages: int, group_size: int, iters_cold: int,
-           iters_warm: int, seed: int, dtype: str) -> L.qvg_config:
+           iters_warm: int, seed: int, dtype: str, converge: int = 0) -> L.qvg_config:
     dt = {"bf16": L.QVG_BF16, "f32": L.QVG_F32}[dtype]
-    return L.make_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dt)
+    return L.make_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dt, converge)
 
 
 def _dtype_of(cfg: L.qvg_config) -> torch.dtype:
@@ -95,6 +95,14 @@ class Encoder:
         self.cfg, self.heads = cfg, heads
         self.ws_bytes = L.qvg_encode_workspace_bytes(cfg, heads, max_tokens)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        self.last_tokens = None
+
+    def rounds(self, stream=None) -> torch.Tensor:
+        """[T][H] int32 Lloyd rounds of the last encode (convergence mode only)."""
+        out = torch.empty((self.cfg.n_stages, self.heads), dtype=torch.int32, device=self.ws.device)
+        L.qvg_encode_rounds(self.cfg, self.heads, self.last_tokens, self.ws, self.ws_bytes, out,
+                            stream or torch.cuda.current_stream())
+        return out
 
     def encode(self, x: torch.Tensor, dst: CompressedKV, chunk_index: int,
                cache: CentroidCache | None = None, init: torch.Tensor | None = None, stream=None):
@@ -102,6 +110,7 @@ class Encoder:
         [H][Ntot][d] tensor is fine)."""
         H, N, d = x.shape
         assert x.stride(2) == 1 and x.stride(1) == d and x.dtype == _dtype_of(self.cfg)
+        self.last_tokens = N
         L.qvg_encode_chunk(self.cfg, x, x.stride(0), H, N,
                            None if init is None else _contiguous_for(init, stream),
                            None if cache is None else cache.handle, dst.view, chunk_index,

@@ -43,7 +43,7 @@ size_t dtype_size(int dt) { return dt == QVG_BF16 ? 2 : 4; }
 
 qvg_status check_config(const qvg_config *c) {
     if (!c) return QVG_ERR_INVALID_ARG;
-    if (c->reserved != 0) return QVG_ERR_INVALID_ARG;
+    if (c->converge < 0) return QVG_ERR_INVALID_ARG;
     if (c->d <= 0 || c->group_size <= 0) return QVG_ERR_INVALID_ARG;
     if (c->n_centroids < 1 || c->n_centroids > QVG_MAX_CENTROIDS) return QVG_ERR_INVALID_ARG;
     if (c->n_stages < 0 || c->n_stages > QVG_MAX_STAGES) return QVG_ERR_INVALID_ARG;
@@ -127,12 +127,15 @@ struct ProfScope {
         QVG_TRY(expr);                                         \
     } while (0)
 
+// Convergence-driven rounds: changed[2][H], done[H], ndone, rounds[T][H] (int32).
+size_t conv_words(int H, int T) { return (size_t)3 * H + 1 + (size_t)T * H; }
+
 // Carves one workspace into the buffers of the encode stage loop.  The
 // residuals R(t) are never stored: each kernel rebuilds them from the input
 // and the earlier stages' stored centroids and assignments.
 struct EncodeWorkspace {
     size_t C = 0, Cb = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, vstats = 0, tstats = 0, r1 = 0,
-           total = 0;
+           conv = 0, total = 0;
 
     EncodeWorkspace(const qvg_config &c, int H, int N) {
         const size_t D = c.d, K = c.n_centroids, Kp = padded_k(c.n_centroids);
@@ -150,6 +153,7 @@ struct EncodeWorkspace {
         vstats = take(value_stats_words(H) * 4);
         tstats = take((size_t)T * H * TSTAT_BLOCKS * 2 * 4);
         if (c.dtype == QVG_BF16 && T >= 2) r1 = take((size_t)H * N * D * 2);   // R(1) as the stage-2 operand
+        conv = take(conv_words(H, T) * 4);
         total = off;
     }
 };
@@ -362,6 +366,11 @@ static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_he
     Src r1src = plain_src(r1, (int64_t)N * D);
     const bool warm_cache = cache && cache->valid;
     const bool need_draw = !init_centroids && !warm_cache;
+    // convergence-driven rounds (cfg->converge >= 1): per-head state in the workspace
+    int32_t *conv = at<int32_t>(workspace, ws.conv);
+    int32_t *chg[2] = {conv, conv + H};
+    int32_t *done = conv + 2 * H, *ndone = conv + 3 * H, *rounds = conv + 3 * H + 1;
+    const bool cvg = cfg->converge > 0;
     if (need_draw) QVG_LAUNCH("forgy", 0, (double)T * H * K * 4, launch_forgy(T, H, N, K, cfg->seed, idx, s));
 
     // the exactness certificate of the update needs the input's value statistics:
@@ -392,26 +401,44 @@ static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_he
         QVG_LAUNCH("init_centroids", 0, (double)H * K * D * (esz + 4) + table,
                    launch_init_centroids(D, cfg->dtype, H, K, src, idx + (size_t)(t - 1) * H * K, warm, C, Cb,
                                          cnt[0], fill[0], t == 1 && stats_in_assign ? vstats : nullptr, s));
+        if (cvg) {   // every head active, no changes counted yet, the round budget as the default count
+            QVG_LAUNCH("zero", 0, (3.0 * H + 1) * 4, launch_zero(conv, 3 * (int64_t)H + 1, s));
+            QVG_LAUNCH("fill", 0, H * 4.0, launch_fill(rounds + (size_t)(t - 1) * H, H, iters, s));
+        }
         for (int it = 0; it < iters; ++it) {
             const int c = it & 1;
+            ConvState cv;
+            if (cvg) {
+                cv.changed = chg[c];
+                cv.changed_next = chg[c ^ 1];
+                cv.done = done;
+                cv.rounds = rounds + (size_t)(t - 1) * H;
+                cv.ndone = ndone;
+                cv.threshold = cfg->converge;
+                cv.round = it;
+            }
             QVG_LAUNCH("assign", assign_flops, assign_bytes,
                        launch_assign(D, cfg->dtype, H, N, K, asrc, Cb, pi, cap, cnt[c],
-                                     t == 1 && it == 0 && stats_in_assign ? vstats : nullptr, nullptr, s));
+                                     t == 1 && it == 0 && stats_in_assign ? vstats : nullptr, nullptr,
+                                     cvg ? done : nullptr, cvg ? ndone : nullptr,
+                                     cvg && it > 0 ? chg[c] : nullptr, s));
             if (seg) {
                 QVG_LAUNCH("update", HND, row_bytes + H * N + (double)H * K * D * 4 + table,
                            launch_update_seg(D, cfg->dtype, H, N, K, src, pi, cap, cnt[c], vstats, C, Cb,
-                                             cnt[c ^ 1], fill[c ^ 1], s));
+                                             cnt[c ^ 1], fill[c ^ 1], cv, s));
             } else {
                 QVG_LAUNCH("scatter", 0, H * N * 5.0 + H * Kp * 8.0,
-                           launch_scatter(H, N, Kp, pi, cap, cnt[c], fill[c], offsets, order, s));
+                           launch_scatter(H, N, Kp, pi, cap, cnt[c], fill[c], offsets, order, cvg ? done : nullptr,
+                                          s));
                 QVG_LAUNCH("update", HND, row_bytes + H * N * 4.0 + (double)H * K * D * 4 + table,
                            launch_update(D, cfg->dtype, H, N, K, src, cnt[c], offsets, order, C, Cb, cnt[c ^ 1],
-                                         fill[c ^ 1], s));
+                                         fill[c ^ 1], cv, s));
             }
         }
         uint16_t *rout = r1 && t == 1 ? r1 : nullptr;
         QVG_LAUNCH("assign", assign_flops, assign_bytes + (rout ? HND * 2 : 0.0),
-                   launch_assign(D, cfg->dtype, H, N, K, asrc, Cb, pi, cap, nullptr, nullptr, rout, s));
+                   launch_assign(D, cfg->dtype, H, N, K, asrc, Cb, pi, cap, nullptr, nullptr, rout, nullptr, nullptr,
+                                 nullptr, s));
         void *cslot = static_cast<char *>(dst->centroids) +
                       (((size_t)chunk_index * T + (t - 1)) * H * K * D) * esz;
         QVG_LAUNCH("store_centroids", 0, (double)H * K * D * (4 + esz + (cache ? 4 : 0)),
@@ -441,6 +468,20 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
                             uint64_t workspace_bytes, void *stream) {
     return encode_impl(cfg, x, x_head_stride, heads, n_tokens, init_centroids, cache, dst, chunk_index, workspace,
                        workspace_bytes, stream);
+}
+
+qvg_status qvg_encode_rounds(const qvg_config *cfg, int32_t heads, int32_t n_tokens, const void *workspace,
+                             uint64_t workspace_bytes, int32_t *rounds_out, void *stream) {
+    qvg_status st = check_config(cfg);
+    if (st != QVG_OK) return st;
+    if (heads < 1 || n_tokens < 1 || !workspace || !rounds_out) return QVG_ERR_INVALID_ARG;
+    if (cfg->converge == 0 || cfg->n_stages == 0) return QVG_ERR_STATE;
+    const EncodeWorkspace ws(*cfg, heads, n_tokens);
+    if (workspace_bytes < ws.total) return QVG_ERR_WORKSPACE;
+    const int32_t *rounds = at<int32_t>(const_cast<void *>(workspace), ws.conv) + 3 * (size_t)heads + 1;
+    QVG_TRY(hipMemcpyAsync(rounds_out, rounds, (size_t)cfg->n_stages * heads * 4, hipMemcpyDeviceToDevice,
+                           static_cast<hipStream_t>(stream)));
+    return QVG_OK;
 }
 
 qvg_status qvg_encode_chunk_static(const qvg_config *cfg, const void *x, int64_t x_head_stride, int32_t heads,
@@ -544,7 +585,7 @@ qvg_status qvg_kmeans_assign(const void *x, int32_t x_dtype, int64_t x_head_stri
     QVG_LAUNCH("assign", 2.0 * heads * n_tokens * n_centroids * d,
                (double)heads * n_tokens * (d * dtype_size(x_dtype) + 1) + table,
                launch_assign(d, x_dtype, heads, n_tokens, n_centroids, src, Cb, assign_out, assign_head_stride, nullptr,
-                             nullptr, nullptr, s));
+                             nullptr, nullptr, nullptr, nullptr, nullptr, s));
     return QVG_OK;
 }
 
@@ -580,15 +621,16 @@ qvg_status qvg_centroid_update(const void *x, int32_t x_dtype, int64_t x_head_st
         QVG_LAUNCH("update", HND, HND * dtype_size(x_dtype) + (double)heads * n_tokens + tables,
                    launch_update_seg(d, x_dtype, heads, n_tokens, n_centroids, plain_src(x, x_head_stride), assign,
                                      assign_head_stride, cnt, vstats, centroids, at<uint16_t>(workspace, ws.Cb),
-                                     nullptr, nullptr, s));
+                                     nullptr, nullptr, ConvState{}, s));
     } else {
         QVG_LAUNCH("zero", 0, heads * Kp * 8.0, launch_zero(fill, (int64_t)heads * Kp, s));
         QVG_LAUNCH("scatter", 0, heads * n_tokens * 5.0 + heads * Kp * 8.0,
-                   launch_scatter(heads, n_tokens, Kp, assign, assign_head_stride, cnt, fill, offsets, order, s));
+                   launch_scatter(heads, n_tokens, Kp, assign, assign_head_stride, cnt, fill, offsets, order, nullptr,
+                                  s));
         QVG_LAUNCH("update", HND, HND * dtype_size(x_dtype) + heads * n_tokens * 4.0 + tables,
                    launch_update(d, x_dtype, heads, n_tokens, n_centroids, plain_src(x, x_head_stride), cnt, offsets,
                                  order, centroids, at<uint16_t>(workspace, ws.Cb),
-                                 nullptr, nullptr, s));
+                                 nullptr, nullptr, ConvState{}, s));
     }
     if (counts_out)
         QVG_TRY(hipMemcpy2DAsync(counts_out, (size_t)n_centroids * 4, cnt, (size_t)Kp * 4, (size_t)n_centroids * 4,

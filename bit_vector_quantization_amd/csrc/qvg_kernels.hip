@@ -472,7 +472,7 @@ template <int D, typename KVT>
 __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int tok0, const bf16x8_t (&bt)[ASSIGN_TB][D / 32],
                                             const uint4 *lds, const double *lcn64, const float *lhcn, int32_t *list,
                                             uint8_t *labs, int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts,
-                                            uint16_t *rout) {
+                                            uint16_t *rout, int32_t *changed) {
     constexpr int KS = D / 32;
     constexpr int CH = D / 8;
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
@@ -565,6 +565,7 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
     __builtin_amdgcn_wave_barrier();
     // merge the four lanes of each token, settle the clear cases, list the near ties
     int n_list = 0;
+    int nchg = 0;   // labels this lane changed (counted when `changed` is set)
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
         uint32_t u1 = __float_as_uint(q1[b]), u2 = __float_as_uint(q2[b]);
@@ -584,7 +585,9 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
         const int n = tok0 + 16 * b + r16;
         const bool mine = g == 0 && n < N;
         if (mine && !tie) {
-            pi[(size_t)h * pi_hs + n] = (uint8_t)c1;
+            uint8_t *pp = pi + (size_t)h * pi_hs + n;
+            if (changed) nchg += (int)*pp != c1;
+            *pp = (uint8_t)c1;
             if (counts) atomicAdd(&counts[(size_t)h * Kp + c1], 1);
             if (rout) labs[16 * b + r16] = (uint8_t)c1;
         }
@@ -626,10 +629,17 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
         if (j < n_list && sub == 0) {
             const double e1 = lcn64[c1] - 2.0 * p1, e2 = lcn64[c2] - 2.0 * p2;
             const int best = (e2 < e1 || (e2 == e1 && c2 < c1)) ? c2 : c1;
-            pi[(size_t)h * pi_hs + n] = (uint8_t)best;
+            uint8_t *pp = pi + (size_t)h * pi_hs + n;
+            if (changed) nchg += (int)*pp != best;
+            *pp = (uint8_t)best;
             if (counts) atomicAdd(&counts[(size_t)h * Kp + best], 1);
             if (rout) labs[nl] = (uint8_t)best;
         }
+    }
+    if (changed) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) nchg += __shfl_xor(nchg, o);
+        if (lane == 0 && nchg) atomicAdd(&changed[h], nchg);
     }
     if (!rout) return;
     // the next stage's operand: bf16(fp32(x - c)) with c the token's stored row
@@ -656,7 +666,10 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
                                                                  int K, int Kp, uint8_t *__restrict__ pi,
                                                                  int64_t pi_hs, int32_t *__restrict__ counts,
                                                                  uint32_t *__restrict__ vstats,
-                                                                 uint16_t *__restrict__ rout) {
+                                                                 uint16_t *__restrict__ rout,
+                                                                 const int32_t *__restrict__ skip,
+                                                                 const int32_t *__restrict__ nskip,
+                                                                 int32_t *__restrict__ changed) {
     constexpr int CH = D / 8;
     constexpr int NT = 64 * ASSIGN_WAVES;
     constexpr int STAGE = (256 * CH + NT - 1) / NT;   // table chunks per thread at 256 centroids
@@ -667,6 +680,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
     int32_t *next = lists + ASSIGN_WAVES * TILE;
     uint8_t *labs = reinterpret_cast<uint8_t *>(next + 4);   // [ASSIGN_WAVES][TILE] labels for rout
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (nskip && *nskip >= H) return;   // every head has stopped
     const int T = (N + TILE - 1) / TILE;   // tiles per head
     const int64_t U = (int64_t)H * T;
     const int64_t r = xcd_tile(blockIdx.x, gridDim.x);
@@ -681,6 +695,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
         int t0 = tid;
         asm volatile("" : "+v"(t0));
         for (int sl = 0; sl < nh; ++sl) {
+            if (skip && skip[h0 + sl]) continue;   // a stopped head's tiles are not taken
             const uint4 *csrc = reinterpret_cast<const uint4 *>(Cb + (size_t)(h0 + sl) * Kp * D);
             uint4 st[STAGE];
 #pragma unroll
@@ -720,6 +735,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
             m = __builtin_amdgcn_readfirstlane(m);
             if (m >= e) break;
             const int h = m / T, sl = h - h0;
+            if (skip && skip[h]) continue;
             const int tok0 = (m - h * T) * TILE;
             bf16x8_t bt[ASSIGN_TB][D / 32];
             assign_load<D, KVT, ANYP>(src, h, N, tok0, bt);
@@ -748,7 +764,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
                 }
             }
             assign_wave<D, KVT>(src, h, N, tok0, bt, lds + sl * Kp * (CH + 1), lcn64 + sl * Kp, lhcn + sl * Kp,
-                                lists + wave * TILE, labs + wave * TILE, Kp, pi, pi_hs, counts, rout);
+                                lists + wave * TILE, labs + wave * TILE, Kp, pi, pi_hs, counts, rout, changed);
         }
         __syncthreads();   // the tables are replaced only once every wave is done with them
         u = e;
@@ -768,7 +784,8 @@ static int device_cus() {
 }
 
 hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, const uint16_t *Cb, uint8_t *pi,
-                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, uint16_t *rout, hipStream_t s) {
+                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, uint16_t *rout, const int32_t *skip,
+                         const int32_t *nskip, int32_t *changed, hipStream_t s) {
     const int Kp = padded_k(K);
     const size_t lds = 2 * ((size_t)Kp * (D / 8 + 1) * 16 + (size_t)Kp * 12) + (ASSIGN_WAVES * TILE + 4) * sizeof(int32_t) +
                        ASSIGN_WAVES * TILE;
@@ -786,12 +803,13 @@ hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, 
             (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT, true>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             QVG_KERNEL((k_assign<DD, KVT, true>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts,
-                       (uint32_t *)nullptr, (uint16_t *)nullptr);
+                       (uint32_t *)nullptr, (uint16_t *)nullptr, skip, nskip, changed);
         } else {
             using KB = uint16_t;   // (this branch is only taken for bf16)
             (void)hipFuncSetAttribute((const void *)k_assign<DD, KB, false>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            QVG_KERNEL((k_assign<DD, KB, false>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts, vstats, rout);
+            QVG_KERNEL((k_assign<DD, KB, false>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts, vstats, rout,
+                       skip, nskip, changed);
         }
     });
     return hipGetLastError();
@@ -816,10 +834,11 @@ hipError_t launch_count(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, 
 // and places its tokens with one atomic per token.
 __global__ __launch_bounds__(256) void k_scatter(int N, int Kp, const uint8_t *pi, int64_t pi_hs,
                                                  const int32_t *counts, int32_t *fill, int32_t *offsets,
-                                                 int32_t *order) {
+                                                 int32_t *order, const int32_t *skip) {
     __shared__ int32_t off[256];
     __shared__ int32_t wsum[4];
     const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (skip && skip[h]) return;   // a stopped head's counts are stale
     const int v = tid < Kp ? counts[(size_t)h * Kp + tid] : 0;
     int x = v;
 #pragma unroll
@@ -844,9 +863,9 @@ __global__ __launch_bounds__(256) void k_scatter(int N, int Kp, const uint8_t *p
 }
 
 hipError_t launch_scatter(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, const int32_t *counts,
-                          int32_t *fill, int32_t *offsets, int32_t *order, hipStream_t s) {
+                          int32_t *fill, int32_t *offsets, int32_t *order, const int32_t *skip, hipStream_t s) {
     QVG_KERNEL(k_scatter, dim3((N + 255) / 256, H), dim3(256), 0, s, N, Kp, pi, pi_hs, counts, fill,
-                       offsets, order);
+                       offsets, order, skip);
     return hipGetLastError();
 }
 
@@ -935,13 +954,32 @@ __device__ __forceinline__ void for_rows(const Src &src, int h, const int32_t *o
 // fp32(fp64(t) / n) for an fp64 t: the rounding of the mean.
 __device__ __forceinline__ float mean_of(double t, int cnt) { return (float)(t / (double)cnt); }
 
+// The convergence test at the start of an update launch (see ConvState): true
+// when head h has stopped (now or in an earlier round) and the workgroup has
+// nothing to do.  `first` marks the one workgroup of the head that records.
+__device__ __forceinline__ bool conv_stop(const ConvState &cv, int h, bool first) {
+    if (!cv.threshold) return false;
+    if (cv.done[h]) return true;
+    if (cv.round > 0 && cv.changed[h] < cv.threshold) {
+        if (first) {
+            cv.done[h] = 1;
+            cv.rounds[h] = cv.round;
+            atomicAdd(cv.ndone, 1);
+        }
+        return true;
+    }
+    if (first) cv.changed_next[h] = 0;
+    return false;
+}
+
 template <int D, typename KVT>
 __global__ __launch_bounds__(256) void k_update(Src src, int N, int K, int Kp, const int32_t *counts,
                                                 const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb,
-                                                int32_t *zero_cnt, int32_t *zero_fill) {
+                                                int32_t *zero_cnt, int32_t *zero_fill, ConvState cv) {
     constexpr int LPR = D / 8;        // lanes per row
     const int lane = threadIdx.x & 63;
     const int k = blockIdx.x * 4 + (threadIdx.x >> 6), h = blockIdx.y;
+    if (conv_stop(cv, h, blockIdx.x == 0 && threadIdx.x == 0)) return;
     if (k >= K) return;
     if (lane == 0 && zero_cnt) {
         zero_cnt[(size_t)h * Kp + k] = 0;
@@ -1017,11 +1055,11 @@ __global__ __launch_bounds__(256) void k_update(Src src, int N, int K, int Kp, c
 
 hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, const int32_t *counts,
                          const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb, int32_t *zero_cnt,
-                         int32_t *zero_fill, hipStream_t s) {
+                         int32_t *zero_fill, const ConvState &cv, hipStream_t s) {
     const int Kp = padded_k(K);
     QVG_DISPATCH_DT(D, dtype,
                     QVG_KERNEL((k_update<DD, KVT>), dim3((K + 3) / 4, H), dim3(256), 0, s, src, N, K, Kp,
-                                       counts, offsets, order, C, Cb, zero_cnt, zero_fill));
+                                       counts, offsets, order, C, Cb, zero_cnt, zero_fill, cv));
     return hipGetLastError();
 }
 
@@ -1300,7 +1338,7 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
                                                                const int32_t *__restrict__ counts,
                                                                const uint32_t *__restrict__ xstats, float *C,
                                                                uint16_t *Cb, int32_t *zero_cnt,
-                                                               int32_t *zero_fill) {
+                                                               int32_t *zero_fill, ConvState cv) {
     constexpr int CPL = D / 64;
     constexpr int NT = 64 * SEG_WAVES;
     extern __shared__ double seg_lds[];
@@ -1323,6 +1361,7 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
     const int h = (int)(rb / SEG_RUNS), r = (int)(rb % SEG_RUNS);
     if (h >= H) return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (conv_stop(cv, h, r == 0 && tid == 0)) return;
 
     // The reads that do not depend on the counts are issued first, so that the
     // label batch, the tables and the counts are in flight together.
@@ -1543,7 +1582,7 @@ size_t value_stats_words(int H) { return (size_t)H * VSTAT_BLOCKS * 2; }
 
 hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &src, const uint8_t *pi,
                              int64_t pi_hs, const int32_t *counts, const uint32_t *xstats, float *C, uint16_t *Cb,
-                             int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s) {
+                             int32_t *zero_cnt, int32_t *zero_fill, const ConvState &cv, hipStream_t s) {
     if (!update_seg_fits(N)) return hipErrorInvalidValue;
     const int Kp = padded_k(K);
     const int64_t nb = (int64_t)H * SEG_RUNS;
@@ -1554,7 +1593,7 @@ hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &s
         (void)hipFuncSetAttribute((const void *)k_update_seg<DD, KVT>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)lds);
         QVG_KERNEL((k_update_seg<DD, KVT>), dim3((unsigned)nb), dim3(64 * SEG_WAVES), lds, s, src, H, N, K, Kp, pi,
-                   pi_hs, counts, xstats, C, Cb, zero_cnt, zero_fill);
+                   pi_hs, counts, xstats, C, Cb, zero_cnt, zero_fill, cv);
     });
     return hipGetLastError();
 }
@@ -2201,6 +2240,16 @@ hipError_t static_scratch(void **ptr) {
 __global__ __launch_bounds__(256) void k_zero(int32_t *p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t *p, int64_t n, int32_t v) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill(int32_t *p, int64_t n, int32_t v, hipStream_t s) {
+    QVG_KERNEL(k_fill_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
 }
 
 hipError_t launch_zero(int32_t *p, int64_t n, hipStream_t s) {

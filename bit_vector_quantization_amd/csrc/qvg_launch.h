@@ -48,6 +48,18 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
                                  const float *warm, float *C, uint16_t *Cb, int32_t *cnt0, int32_t *fill0,
                                  uint32_t *vstats_clear, hipStream_t s);
 
+// Convergence-driven rounds (off when threshold == 0).  Round `round` of a
+// stage: its assign adds the labels it changed per head into changed[h]; its
+// update stops head h (done[h] = 1, rounds[h] = round, ndone += 1) when
+// round > 0 and changed[h] < threshold, and otherwise clears changed_next[h]
+// for the next round's assign.  Every later launch of the stage skips heads
+// with done[h] set.
+struct ConvState {
+    int32_t *changed = nullptr, *changed_next = nullptr, *done = nullptr, *rounds = nullptr, *ndone = nullptr;
+    int threshold = 0;
+    int round = 0;
+};
+
 // pi[h][n] = argmin_{k < K} |Cb[h][k]|^2 - 2 <bf16(R(t-1)[h][n]), Cb[h][k]>: bf16
 // MFMA with fp32 accumulation ranks the centroids, the best two are re-decided
 // exactly in fp64.  counts (non-null) [H][Kp] += tokens per centroid.  vstats
@@ -55,9 +67,13 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
 // statistics are folded into partial 0 of each head (cleared beforehand).
 // rout (non-null; a bf16 tensor without earlier stages only) [H][N][D] bf16
 // receives bf16(fp32(x - Cb[pi])), the operand that the next stage's assign
-// would otherwise rebuild from x, its table and its assignment.
+// would otherwise rebuild from x, its table and its assignment.  skip
+// (non-null) [H]: heads with skip[h] != 0 are left alone (and with *nskip ==
+// H nothing is done).  changed (non-null) [H] += labels that differ from
+// what pi held before.
 hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, const uint16_t *Cb, uint8_t *pi,
-                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, uint16_t *rout, hipStream_t s);
+                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, uint16_t *rout, const int32_t *skip,
+                         const int32_t *nskip, int32_t *changed, hipStream_t s);
 
 // Histogram of an assignment (counts must be zero on entry).
 hipError_t launch_count(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, int32_t *counts,
@@ -67,7 +83,7 @@ hipError_t launch_count(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, 
 // counts) and order [H][N]; fill [H][Kp] must be zero on entry.  The order of
 // the tokens of one centroid is unspecified.
 hipError_t launch_scatter(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, const int32_t *counts,
-                          int32_t *fill, int32_t *offsets, int32_t *order, hipStream_t s);
+                          int32_t *fill, int32_t *offsets, int32_t *order, const int32_t *skip, hipStream_t s);
 
 // Every centroid with tokens becomes the exactly summed mean of their rows of
 // R(t-1) (rounded once to fp64, divided by the count, rounded to fp32); C and
@@ -75,7 +91,7 @@ hipError_t launch_scatter(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs
 // [H][Kp] are cleared for the next round.
 hipError_t launch_update(int D, int dtype, int H, int N, int K, const Src &src, const int32_t *counts,
                          const int32_t *offsets, const int32_t *order, float *C, uint16_t *Cb, int32_t *zero_cnt,
-                         int32_t *zero_fill, hipStream_t s);
+                         int32_t *zero_fill, const ConvState &cv, hipStream_t s);
 
 // The same update without a global sort (k_update_seg): each workgroup lists the
 // tokens of a run of centroids in LDS from pi (uint8, head stride pi_hs, the
@@ -89,7 +105,7 @@ hipError_t launch_value_stats(int dtype, int H, const void *x, int64_t x_hs, int
                               hipStream_t s);
 hipError_t launch_update_seg(int D, int dtype, int H, int N, int K, const Src &src, const uint8_t *pi,
                              int64_t pi_hs, const int32_t *counts, const uint32_t *xstats, float *C, uint16_t *Cb,
-                             int32_t *zero_cnt, int32_t *zero_fill, hipStream_t s);
+                             int32_t *zero_cnt, int32_t *zero_fill, const ConvState &cv, hipStream_t s);
 
 // dst_slice [H][K][D] = C rounded to dtype; cache_slice [H][K][D] = C (if non-null);
 // tstats (if non-null) receives TSTAT_BLOCKS partial pairs per head of the
@@ -140,5 +156,7 @@ hipError_t static_scratch(void **ptr);
 
 // Fills n int32 with zero.
 hipError_t launch_zero(int32_t *p, int64_t n, hipStream_t s);
+// Fills n int32 with v.
+hipError_t launch_fill(int32_t *p, int64_t n, int32_t v, hipStream_t s);
 
 }  // namespace qvg

@@ -60,14 +60,25 @@ enum { QVG_F32 = 0, QVG_BF16 = 1 };
 
 /* Codec settings.  The pages fix 256 centroids with uint8 assignments and group
  * sizes 16 or 64 (163.com article, section 7); the rest are this library's
- * readings (cold start = Forgy rows from a SplitMix64-keyed shuffle; a fixed
- * number of Lloyd rounds, then one final assignment).
+ * readings (cold start = Forgy rows from a SplitMix64-keyed shuffle; a number
+ * of Lloyd rounds, then one final assignment).
  *   d            head dimension: 64 or 128
  *   n_centroids  K, 1..256
  *   n_stages     T, 0..8 (T = 0 quantises X directly: the round-to-nearest baseline)
  *   group_size   G in {16, 32, 64, 128}, dividing d (channels per scale)
  *   iters_cold   Lloyd rounds when the chunk starts from the seeded draw (>= 0)
  *   iters_warm   Lloyd rounds when it starts from cached/given centroids (>= 0)
+ *   converge     0: exactly iters_cold / iters_warm rounds.  c >= 1: those are
+ *                maxima, and a head's rounds of a stage stop at the first
+ *                assignment after the first round that moves fewer than c of
+ *                its tokens to another centroid, before that round's update
+ *                (k-means run until its labels settle; the pages report fewer
+ *                rounds when it starts from the cached centroids: 163.com
+ *                article, section 5; gist.science summaries, section 2C).
+ *                c = 1 stops at a fixed point, so the result equals that of any
+ *                larger fixed count.  The decision is taken on the device per
+ *                head, without a host synchronisation; qvg_encode_rounds
+ *                reports the rounds run.
  *   seed         codec seed; the cold draw of (head h, stage t) is keyed by
  *                ((seed * 65536 + h) * 64 + t) mod 2^64
  *   dtype        QVG_BF16 or QVG_F32: the input X and the stored centroids       */
@@ -80,7 +91,7 @@ typedef struct {
     int32_t iters_warm;
     uint64_t seed;
     int32_t dtype;
-    int32_t reserved; /* must be 0 */
+    int32_t converge; /* >= 0 */
 } qvg_config;
 
 /* The compressed cache of one tensor (K or V) of one layer, caller-allocated.
@@ -177,6 +188,14 @@ qvg_status qvg_encode_chunk(const qvg_config *cfg, const void *x, int64_t x_head
                             qvg_centroid_cache *cache, const qvg_cache_view *dst,
                             int32_t chunk_index, void *workspace, uint64_t workspace_bytes,
                             void *stream);
+
+/* Lloyd rounds (updates) that every (stage, head) ran in the last
+ * qvg_encode_chunk call made with `workspace` (same cfg, heads, n_tokens), when
+ * cfg->converge >= 1: device int32 [T][H], copied to rounds_out on `stream`
+ * (163.com article, section 5: the cache's saving in k-means rounds).
+ * QVG_ERR_STATE when cfg->converge == 0 or T == 0 (fixed counts). */
+qvg_status qvg_encode_rounds(const qvg_config *cfg, int32_t heads, int32_t n_tokens, const void *workspace,
+                             uint64_t workspace_bytes, int32_t *rounds_out, void *stream);
 
 /* qvg_encode_chunk for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):

@@ -72,6 +72,7 @@ class CodecConfig:
     iters_warm: int
     seed: int
     dtype: str = "bf16"        # "bf16" or "f32": input values and centroid storage
+    converge: int = 0          # 0: fixed round counts; c >= 1: stop once a round moves fewer than c tokens
 
 
 # --------------------------------------------------------------------------
@@ -137,18 +138,37 @@ def update(R: np.ndarray, lab: np.ndarray, C_prev: np.ndarray,
     return C, counts
 
 
-def lloyd(R: np.ndarray, C0: np.ndarray, iters: int, mode: str = "parity"):
+def lloyd(R: np.ndarray, C0: np.ndarray, iters: int, mode: str = "parity", converge: int = 0,
+          labels_history: Optional[list] = None):
     """`iters` rounds of (assign, update) then one final assign.
     Returns (centroids, labels, sse_history) where sse_history[i] is the
-    sum of squared distances after update i (float64, unrounded rows)."""
+    sum of squared distances after update i (float64, unrounded rows); its
+    length is the number of updates run.
+
+    converge = c >= 1 turns the round count into a maximum: the rounds stop
+    at the first assignment (after the first round) that moves fewer than c
+    tokens to another centroid than the round before, without running that
+    round's update.  This is the plain reading of the pages' statement that
+    k-means needs fewer rounds once it starts from the previous chunk's
+    centroids (163.com article, section 5; German summary, section 2C):
+    Lloyd's method is run until its labels settle.  With c = 1 the stop is exact: the same
+    labels give the same centroids, so every later round would repeat them
+    and the result equals that of any larger fixed count.  labels_history
+    (a list) receives every round's assignment, the final one excluded."""
     C = np.array(C0, dtype=np.float64, copy=True)
     if mode == "parity":
         C = C.astype(F32).astype(np.float64)
     hist = []
+    prev = None
     for _ in range(iters):
         lab = assign(R, C, mode)
+        if labels_history is not None:
+            labels_history.append(lab)
+        if converge and prev is not None and int((lab != prev).sum()) < converge:
+            break
         C, _ = update(R, lab, C, mode)
         hist.append(float(((np.asarray(R, np.float64) - C[lab]) ** 2).sum()))
+        prev = lab
     lab = assign(R, C, mode)
     return C, lab, hist
 
@@ -212,6 +232,7 @@ class Encoded:
     cache: np.ndarray        # [T][H][K][d] float32 (unrounded, for the next chunk)
     residuals: Optional[List[np.ndarray]] = None   # R(0..T), each [H][N][d]
     sse: Optional[List[List[List[float]]]] = None  # [t][h] -> per-iteration SSE
+    rounds: Optional[np.ndarray] = None            # [T][H] Lloyd updates run
 
 
 def _store(C: np.ndarray, dtype: str) -> np.ndarray:
@@ -242,6 +263,7 @@ def encode_chunk(X: np.ndarray, cfg: CodecConfig, cache: Optional[np.ndarray] = 
     new_cache = np.zeros((T, H, K, d), cdt)
     residuals = [X.astype(np.float64)] if keep_residuals else None
     sse = [[None] * H for _ in range(T)]
+    rounds = np.zeros((T, H), np.int32)
     Rall = X.astype(np.float64)
     for h in range(H):
         R = Rall[h]
@@ -250,8 +272,9 @@ def encode_chunk(X: np.ndarray, cfg: CodecConfig, cache: Optional[np.ndarray] = 
                 C0 = np.asarray(start[t - 1, h], np.float64)
             else:
                 C0 = R[forgy_indices(N, K, cfg.seed, head_offset + h, t)]
-            C, lab, hist = lloyd(R, C0, n_it, mode)
+            C, lab, hist = lloyd(R, C0, n_it, mode, converge=cfg.converge)
             sse[t - 1][h] = hist
+            rounds[t - 1, h] = len(hist)
             Cs = _store(C, cfg.dtype) if mode == "parity" else C
             asg[t - 1, h] = lab.astype(np.uint8)
             cent[t - 1, h] = Cs
@@ -266,7 +289,7 @@ def encode_chunk(X: np.ndarray, cfg: CodecConfig, cache: Optional[np.ndarray] = 
         _, packed, s_code = group_quant(R.astype(F32), G)
         codes[h] = packed
         scales[h] = s_code
-    return Encoded(codes, scales, asg, cent, new_cache, residuals, sse)
+    return Encoded(codes, scales, asg, cent, new_cache, residuals, sse, rounds)
 
 
 def rope_rotate(y: np.ndarray, table: np.ndarray) -> np.ndarray:

@@ -94,7 +94,7 @@ def test_workspace_sizes(q):
 @pytest.mark.parametrize("field,value,status", [
     ("n_centroids", 0, -1), ("n_centroids", 257, -1), ("n_stages", -1, -1), ("n_stages", 9, -1),
     ("group_size", 48, -1), ("group_size", 0, -1), ("iters_cold", -1, -1), ("dtype", 7, -1),
-    ("reserved", 1, -1), ("d", 192, -2), ("d", 256, -2), ("group_size", 8, -2)])
+    ("converge", -1, -1), ("d", 192, -2), ("d", 256, -2), ("group_size", 8, -2)])
 def test_config_validation(q, field, value, status):
     g, _ = _cfg(q, synthkv.PRESETS[2])
     setattr(g, field, value)
