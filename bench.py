@@ -53,8 +53,10 @@ def parse():
     ap.add_argument("--share-reps", type=int, default=5,
                     help="timed steps of one GPU's share of the layer when its heads are split over 8 GPUs "
                          "(5 key + 5 value heads; 0 skips)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the per-stage error, convergence, FP8-table and latency reports")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=3, help="heads in the oracle's timed sample")
+    ap.add_argument("--cpu-heads", type=int, default=2, help="heads of K and of V in the oracle's warm-chunk leg")
     return ap.parse_args()
 
 
@@ -267,6 +269,13 @@ def main():
     if args.stress_reps > 0:
         stress = run_stress(q, synthkv, torch, dev, stream, args.stress_reps)
 
+    extras = {}
+    if not args.no_extras:
+        extras["stage_errors"] = run_stage_errors(q, synthkv, torch, dev, stream)
+        extras["convergence"] = run_convergence(q, synthkv, torch, dev, stream, X, p, HK)
+        extras["fp8_tables"] = run_fp8_tables(q, synthkv, torch, dev, stream, X, p, HK, out)
+        extras["latency_single_head_chunk"] = run_latency(q, synthkv, torch, dev, stream)
+
     cpu = None if args.no_cpu_baseline else cpu_baseline(p, args.cpu_heads, ms_per_step, vec_step)
 
     line = {
@@ -281,6 +290,7 @@ def main():
                                "then full-cache fused decode",
                    "heads": HK, "tokens": Ntot, "d": d, "centroids": K, "stages": T, "group_size": G,
                    "chunk_tokens": p.chunk_tokens, "iters_cold": p.iters_cold, "iters_warm": p.iters_warm},
+        "tokens_per_s": round(Ntot / (ms_per_step * 1e-3), 1),
         "roofline": roof,
         "rooflines": roofs,
         "cpu_baseline": cpu,
@@ -297,6 +307,7 @@ def main():
         "aggressive": aggressive,
         "head_share_of_8": share,
         "decode_stress": stress,
+        **extras,
         "kernels": kernels,
         "profiled_ms_per_step": None if prof_ms_step is None else round(prof_ms_step, 4),
     }
@@ -488,48 +499,249 @@ def run_stress(q, synthkv, torch, dev, stream, reps):
             "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "reps": reps, "setup_s": round(prep_s, 1)}
 
 
+def run_stage_errors(q, synthkv, torch, dev, stream):
+    """The aggressive setting's error per stage on the HIP path: the whole
+    48-head tensor (K and V of 24 heads, 9,360 tokens in 2 chunks) encoded with
+    T = 0..4 stages (T = 0 is single-shot round-to-nearest 2-bit with the same
+    E4M3 group-16 scales), decoded in fp32; MSE over all elements in fp64, for
+    K and V separately, and each stage's ratio MSE(t-1) / MSE(t)."""
+    p = synthkv.PRESETS[4]
+    H, Ntot, d, K, G = p.heads, p.n_tokens, p.d, p.n_centroids, p.group_size
+    HK = 2 * H
+    log(f"per-stage error: aggressive setting, T = 0..{p.n_stages}")
+    X = torch.empty((2, H, Ntot, d), dtype=torch.bfloat16, device=dev)
+    for i, t in enumerate(("K", "V")):
+        X[i] = torch.cat(list(synthkv.gen_torch(p, t, dev, frames_per_call=p.chunk_frames)), dim=1)
+    X = X.view(HK, Ntot, d)
+    Xd = X.double()
+    mse = {"K": [], "V": []}
+    for T in range(0, p.n_stages + 1):
+        cfg = q.config(d, K, T, G, p.iters_cold, p.iters_warm, p.codec_seed("K"), p.dtype)
+        dst = q.CompressedKV(cfg, HK, Ntot, p.chunk_tokens, dev)
+        cache = q.CentroidCache(cfg, HK) if T else None
+        enc = q.Encoder(cfg, HK, p.chunk_tokens, dev)
+        for c in range(p.n_chunks):
+            b, e = p.chunk_range(c)
+            enc.encode(X[:, b:e], dst, c, cache=cache, stream=stream)
+        y = q.decode(cfg, dst, 0, Ntot, out_dtype="f32", stream=stream)
+        err = (y.double() - Xd).pow(2)
+        mse["K"].append(float(err[:H].mean()))
+        mse["V"].append(float(err[H:].mean()))
+        del dst, cache, enc, y, err
+    out = {}
+    for t in ("K", "V"):
+        m = mse[t]
+        out[t] = {"mse": [float(f"{v:.6g}") for v in m],
+                  "ratio_per_stage": [round(m[i - 1] / m[i], 3) for i in range(1, len(m))],
+                  "total_vs_rtn": round(m[0] / m[-1], 2)}
+    return {"workload": "aggressive setting: K and V of 24 heads x 128, 9,360 tokens in 2 chunks (cold, warm), "
+                        "256 centroids, G=16, E4M3 scales; T = 0 is single-shot round-to-nearest 2-bit",
+            "stages": list(range(0, p.n_stages + 1)), **out,
+            "pages_context": "real-model KV: 5.83x, 1.39x, 1.15x for stages 1-3 (not this data)"}
+
+
+def run_convergence(q, synthkv, torch, dev, stream, X, p, HK):
+    """Rounds to convergence, cold vs warm, on the HIP path: the 13B layer's
+    chunks encoded with the device-side stop (converge = 1: labels unchanged,
+    exact; converge = 5: fewer than 0.1% of 4,680 tokens moved), at most 30
+    rounds; per chunk the mean / max rounds over heads and stages, and the
+    chunk time next to the fixed counts (10 cold, 3 warm)."""
+    d, K, T, G = p.d, p.n_centroids, p.n_stages, p.group_size
+    res = {}
+    for conv in (1, 5):
+        cfg = q.config(d, K, T, G, 30, 30, p.codec_seed("K"), p.dtype, conv)
+        dst = q.CompressedKV(cfg, HK, p.n_tokens, p.chunk_tokens, dev)
+        cache = q.CentroidCache(cfg, HK)
+        enc = q.Encoder(cfg, HK, p.chunk_tokens, dev)
+        log(f"convergence: converge={conv}, at most 30 rounds")
+        chunks = []
+        for c in range(p.n_chunks - 1):   # the full chunks
+            b, e = p.chunk_range(c)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            enc.encode(X[:, b:e], dst, c, cache=cache, stream=stream)
+            e1.record(stream)
+            r = enc.rounds(stream).float()
+            torch.cuda.synchronize()
+            chunks.append({"chunk": c, "start": "cold" if c == 0 else "warm",
+                           "rounds_mean": round(float(r.mean()), 2), "rounds_max": int(r.max()),
+                           "rounds_mean_K": round(float(r[:, :HK // 2].mean()), 2),
+                           "rounds_mean_V": round(float(r[:, HK // 2:].mean()), 2),
+                           "ms": round(e0.elapsed_time(e1), 3)})
+        warm = [c["rounds_mean"] for c in chunks[1:]]
+        res[f"converge_{conv}"] = {"chunks": chunks, "cold_rounds_mean": chunks[0]["rounds_mean"],
+                                   "warm_rounds_mean": round(sum(warm) / len(warm), 2),
+                                   "cold_over_warm": round(chunks[0]["rounds_mean"] / (sum(warm) / len(warm)), 2)}
+    return res
+
+
+def run_fp8_tables(q, synthkv, torch, dev, stream, X, p, HK, ref_out):
+    """The bench step's encode and decode with the centroid tables stored in
+    FP8 (E4M3 times a power of two per table): step time, decode bandwidth,
+    reconstruction error next to bf16 tables, and the bytes."""
+    d, K, T, G = p.d, p.n_centroids, p.n_stages, p.group_size
+    cfg = q.config(d, K, T, G, p.iters_cold, p.iters_warm, p.codec_seed("K"), p.dtype, 0, "e4m3")
+    dst = q.CompressedKV(cfg, HK, p.n_tokens, p.chunk_tokens, dev)
+    cache = q.CentroidCache(cfg, HK)
+    enc = q.Encoder(cfg, HK, p.chunk_tokens, dev)
+    out = torch.empty_like(ref_out)
+    log("FP8 centroid tables: encode + decode of the layer")
+
+    def step():
+        cache.reset()
+        for c in range(p.n_chunks):
+            b, e = p.chunk_range(c)
+            enc.encode(X[:, b:e], dst, c, cache=cache, stream=stream)
+
+    step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(3):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    enc_ms = e0.elapsed_time(e1) / 3
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    t = 0.0
+    for _ in range(5):
+        flush.sum()
+        a = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        q.decode(cfg, dst, 0, p.n_tokens, out=out, stream=stream)
+        b_.record(stream)
+        torch.cuda.synchronize()
+        t += a.elapsed_time(b_)
+    dec_ms = t / 5
+    del flush
+    dec_b = HK * p.n_tokens * (d // 4 + d // G + T + 2 * d) + p.n_chunks * T * HK * (K * d + 16)
+    H = HK // 2
+    Xd = X.double()
+    m8 = [float((out[s].double() - Xd[s]).pow(2).mean()) for s in (slice(0, H), slice(H, HK))]
+    mb = [float((ref_out[s].double() - Xd[s]).pow(2).mean()) for s in (slice(0, H), slice(H, HK))]
+    total = sum(q.qvg_cache_view_bytes(cfg, HK, p.n_tokens, p.chunk_tokens))
+    cfg_n = q.config(d, K, T, G, p.iters_cold, p.iters_warm, p.codec_seed("K"), p.dtype)
+    total_n = sum(q.qvg_cache_view_bytes(cfg_n, HK, p.n_tokens, p.chunk_tokens))
+    raw = HK * p.n_tokens * d * 2
+    return {"encode_ms_per_step": round(enc_ms, 4), "decode_us": round(dec_ms * 1e3, 2),
+            "decode_algorithmic_bytes": int(dec_b), "decode_gbs": round(dec_b / (dec_ms * 1e-3) / 1e9, 1),
+            "mse_K": float(f"{m8[0]:.6g}"), "mse_V": float(f"{m8[1]:.6g}"),
+            "mse_K_bf16_tables": float(f"{mb[0]:.6g}"), "mse_V_bf16_tables": float(f"{mb[1]:.6g}"),
+            "compressed_bytes": int(total), "compressed_bytes_bf16_tables": int(total_n),
+            "ratio": round(raw / total, 3), "ratio_bf16_tables": round(raw / total_n, 3)}
+
+
+def run_latency(q, synthkv, torch, dev, stream):
+    """One chunk of one head's K and V (the single-head workload, 4,680 tokens,
+    cold, 10 rounds, 2 stages): encode and decode latency."""
+    p = synthkv.PRESETS[2]
+    X = torch.cat([torch.from_numpy(synthkv.gen_numpy(p, t)) for t in ("K", "V")]).to(torch.bfloat16).to(dev)
+    cfg = q.config(p.d, p.n_centroids, p.n_stages, p.group_size, p.iters_cold, p.iters_warm, p.codec_seed("K"),
+                   p.dtype)
+    dst = q.CompressedKV(cfg, 2, p.n_tokens, p.chunk_tokens, dev)
+    enc = q.Encoder(cfg, 2, p.chunk_tokens, dev)
+    out = torch.empty((2, p.n_tokens, p.d), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        enc.encode(X, dst, 0, stream=stream)
+    torch.cuda.synchronize()
+    te, td = [], []
+    for _ in range(10):
+        a, b_, c_ = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a.record(stream)
+        enc.encode(X, dst, 0, stream=stream)
+        b_.record(stream)
+        q.decode(cfg, dst, 0, p.n_tokens, out=out, stream=stream)
+        c_.record(stream)
+        torch.cuda.synchronize()
+        te.append(a.elapsed_time(b_))
+        td.append(b_.elapsed_time(c_))
+    te.sort()
+    td.sort()
+    return {"workload": "one head's K and V, one chunk of 4,680 tokens, cold (10 rounds), 2 stages",
+            "encode_ms_median": round(te[5], 4), "decode_us_median": round(td[5] * 1e3, 2)}
+
+
 def cpu_baseline(p, heads, gpu_ms_step, vec_step):
-    """The oracle (NumPy, fp64) on heads 0..heads-1 of the same layer: chunk 0
-    cold, chunk 1 warm, and the decode of both, for K and V; extrapolated to
-    the step's mix of 1 cold + 7 warm + 1 ragged chunk and the full decode."""
+    """The oracle (NumPy, fp64) on the host cores, three legs, each the median of
+    3 runs: a cold single-head chunk of K and V (the single-head workload:
+    4,680 tokens, 10 rounds, 2 stages), a warm chunk of the 13B layer on
+    `heads` key and `heads` value heads (3 rounds, from the previous chunk's
+    centroids), and the decode of 10 chunks of the long-horizon cache on two
+    heads.  Their per-vector times give the headline workload's step on the
+    host (1 cold + 7 warm + 1 ragged chunk x 80 head-tensors + the full
+    decode): a baseline, extrapolated and labeled so."""
+    import platform
+
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
     import synthkv
 
-    log(f"cpu baseline: oracle on {heads} heads x 2 chunks x K,V")
-    cold = warm = dec = 0.0
-    for t in ("K", "V"):
-        X = synthkv.gen_numpy(p, t, heads=heads, n_tokens=2 * p.chunk_tokens)
-        oc = oracle.CodecConfig(d=p.d, n_centroids=p.n_centroids, n_stages=p.n_stages, group_size=p.group_size,
-                                iters_cold=p.iters_cold, iters_warm=p.iters_warm, seed=p.codec_seed(t),
-                                dtype=p.dtype)
-        t0 = time.perf_counter()
-        e0 = oracle.encode_chunk(X[:, :p.chunk_tokens], oc)
-        t1 = time.perf_counter()
-        e1 = oracle.encode_chunk(X[:, p.chunk_tokens:], oc, cache=e0.cache)
-        t2 = time.perf_counter()
-        oracle.decode(e0, p.group_size, "bf16")
-        oracle.decode(e1, p.group_size, "bf16")
-        t3 = time.perf_counter()
-        cold += t1 - t0
-        warm += t2 - t1
-        dec += t3 - t2
-    per_head_tensor = lambda s: s / (2 * heads)
+    def ocfg(pr, t):
+        return oracle.CodecConfig(d=pr.d, n_centroids=pr.n_centroids, n_stages=pr.n_stages,
+                                  group_size=pr.group_size, iters_cold=pr.iters_cold, iters_warm=pr.iters_warm,
+                                  seed=pr.codec_seed(t), dtype=pr.dtype)
+
+    def median3(f):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            f()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[1]
+
+    log("cpu baseline: oracle legs (median of 3 each)")
+    p2 = synthkv.PRESETS[2]
+    x2 = {t: synthkv.gen_numpy(p2, t) for t in ("K", "V")}
+    cold_s = median3(lambda: [oracle.encode_chunk(x2[t], ocfg(p2, t)) for t in ("K", "V")])
+    cold_vec = cold_s / (2 * p2.n_tokens)
+    xs = {t: synthkv.gen_numpy(p, t, heads=heads, n_tokens=2 * p.chunk_tokens) for t in ("K", "V")}
+    prev = {t: oracle.encode_chunk(xs[t][:, :p.chunk_tokens], ocfg(p, t)).cache for t in ("K", "V")}
+    warm_s = median3(lambda: [oracle.encode_chunk(xs[t][:, p.chunk_tokens:], ocfg(p, t), cache=prev[t])
+                              for t in ("K", "V")])
+    warm_vec = warm_s / (2 * heads * p.chunk_tokens)
+    p5 = synthkv.PRESETS[5]
+    n10 = 10 * p5.chunk_tokens
+    x5 = synthkv.gen_numpy(p5, "K", heads=2, n_tokens=n10)
+    # the decode's time does not depend on how well k-means converged: one round
+    oc5 = oracle.CodecConfig(**{**ocfg(p5, "K").__dict__, "iters_cold": 1})
+    encs = [oracle.encode_chunk(x5[:, c * p5.chunk_tokens:(c + 1) * p5.chunk_tokens], oc5) for c in range(10)]
+    dec_s = median3(lambda: [oracle.decode(e, p5.group_size, "bf16") for e in encs])
+    dec_vec = dec_s / (2 * n10)
     rag = (p.n_tokens - (p.n_chunks - 1) * p.chunk_tokens) / p.chunk_tokens
     n_warm = p.n_chunks - 2
-    est = 2 * p.heads * (per_head_tensor(cold) + (n_warm + rag) * per_head_tensor(warm)
-                         + (p.n_chunks - 1 + rag) / 2 * per_head_tensor(dec))
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    hk = 2 * p.heads
+    est = hk * p.chunk_tokens * (cold_vec + (n_warm + rag) * warm_vec) + hk * p.n_tokens * dec_vec
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info if i.get("user_api") == "blas"})
+    cpu_model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    dec_b_vec = (p5.d // 4 + p5.d // p5.group_size + p5.n_stages + 2 * p5.d
+                 + p5.n_stages * p5.n_centroids * p5.d * 2 / p5.chunk_tokens)
     return {"value": round(vec_step / est, 1), "unit": "KV vectors/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"heads 0..{heads - 1} of K and V: chunk 0 cold + chunk 1 warm encode + their decode "
-                      f"({cold + warm + dec:.1f} s measured), extrapolated to one step "
-                      f"(1 cold + {n_warm} warm + 1 ragged chunk x 40 heads x 2 tensors + full decode)",
-            "measured_s": round(cold + warm + dec, 2), "est_step_s": round(est, 2),
-            "gpu_speedup": round(est / (gpu_ms_step * 1e-3), 1),
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "sample": "three legs, median of 3 each: cold single-head chunk of K and V (4,680 tokens); warm "
+                      f"13B-layer chunk on {heads} K + {heads} V heads; decode of 10 long-horizon chunks on 2 "
+                      "heads; per-vector times extrapolated to one step of the headline workload",
+            "legs": {"cold_chunk_KV_s": round(cold_s, 3), "cold_vectors_per_s": round(1 / cold_vec, 1),
+                     "warm_chunk_s": round(warm_s, 3), "warm_vectors_per_s": round(1 / warm_vec, 1),
+                     "decode_10_chunks_s": round(dec_s, 3), "decode_vectors_per_s": round(1 / dec_vec, 1),
+                     "decode_gbs": round(dec_b_vec / dec_vec / 1e9, 3)},
+            "est_step_s": round(est, 2), "gpu_speedup": round(est / (gpu_ms_step * 1e-3), 1),
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model, "blas": blas,
+            "blas_threads": threads}
 
 
 if __name__ == "__main__":

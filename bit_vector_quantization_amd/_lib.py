@@ -27,6 +27,9 @@ QVG_ERR_OOM = -6
 QVG_F32 = 0
 QVG_BF16 = 1
 
+QVG_CENT_NATIVE = 0
+QVG_CENT_E4M3 = 1
+
 
 class QvgError(RuntimeError):
     def __init__(self, status: int, what: str):
@@ -37,7 +40,8 @@ class QvgError(RuntimeError):
 class qvg_config(ctypes.Structure):
     _fields_ = [("d", c_int32), ("n_centroids", c_int32), ("n_stages", c_int32),
                 ("group_size", c_int32), ("iters_cold", c_int32), ("iters_warm", c_int32),
-                ("seed", c_uint64), ("dtype", c_int32), ("converge", c_int32)]
+                ("seed", c_uint64), ("dtype", c_int32), ("converge", c_int32),
+                ("centroid_format", c_int32), ("reserved", c_int32)]
 
 
 class qvg_cache_view(ctypes.Structure):
@@ -133,8 +137,10 @@ def _stream(s) -> int | None:
 
 
 def make_config(d: int, n_centroids: int, n_stages: int, group_size: int, iters_cold: int,
-                iters_warm: int, seed: int, dtype: int, converge: int = 0) -> qvg_config:
-    return qvg_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dtype, converge)
+                iters_warm: int, seed: int, dtype: int, converge: int = 0,
+                centroid_format: int = QVG_CENT_NATIVE) -> qvg_config:
+    return qvg_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dtype, converge,
+                      centroid_format, 0)
 
 
 # ---- entry points (same names as the C ABI) --------------------------------

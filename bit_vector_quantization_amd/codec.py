@@ -8,9 +8,11 @@ from . import _lib as L
 
 
 def config(d: int, n_centroids: int, n_stages: int, group_size: int, iters_cold: int,
-           iters_warm: int, seed: int, dtype: str, converge: int = 0) -> L.qvg_config:
+           iters_warm: int, seed: int, dtype: str, converge: int = 0,
+           centroid_format: str = "native") -> L.qvg_config:
     dt = {"bf16": L.QVG_BF16, "f32": L.QVG_F32}[dtype]
-    return L.make_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dt, converge)
+    cf = {"native": L.QVG_CENT_NATIVE, "e4m3": L.QVG_CENT_E4M3}[centroid_format]
+    return L.make_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dt, converge, cf)
 
 
 def _dtype_of(cfg: L.qvg_config) -> torch.dtype:
@@ -44,8 +46,12 @@ class CompressedKV:
         self.codes = torch.empty((heads, cap_tokens, d // 4), dtype=torch.uint8, device=device)
         self.scales = torch.empty((heads, cap_tokens, d // G), dtype=torch.uint8, device=device)
         self.assign = torch.empty((max(T, 1), heads, cap_tokens), dtype=torch.uint8, device=device)
-        self.centroids = torch.empty((self.n_chunks, max(T, 1), heads, K, d), dtype=_dtype_of(cfg),
-                                     device=device)
+        if cfg.centroid_format == L.QVG_CENT_E4M3:   # per table: 16-byte exponent header + K*d codes
+            self.centroids = torch.empty((self.n_chunks, max(T, 1), heads, 16 + K * d), dtype=torch.uint8,
+                                         device=device)
+        else:
+            self.centroids = torch.empty((self.n_chunks, max(T, 1), heads, K, d), dtype=_dtype_of(cfg),
+                                         device=device)
         assert self.codes.numel() == nb[0] and self.scales.numel() == nb[1]
         assert T == 0 or (self.assign.numel() == nb[2]
                           and self.centroids.numel() * self.centroids.element_size() == nb[3])

@@ -40,10 +40,16 @@ using namespace qvg;
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 size_t dtype_size(int dt) { return dt == QVG_BF16 ? 2 : 4; }
+// Bytes of one stored centroid table (one chunk, stage and head).
+size_t table_bytes(const qvg_config &c) {
+    const size_t kd = (size_t)c.n_centroids * c.d;
+    return c.centroid_format == QVG_CENT_E4M3 ? kd + 16 : kd * dtype_size(c.dtype);
+}
 
 qvg_status check_config(const qvg_config *c) {
     if (!c) return QVG_ERR_INVALID_ARG;
-    if (c->converge < 0) return QVG_ERR_INVALID_ARG;
+    if (c->converge < 0 || c->reserved != 0) return QVG_ERR_INVALID_ARG;
+    if (c->centroid_format != QVG_CENT_NATIVE && c->centroid_format != QVG_CENT_E4M3) return QVG_ERR_INVALID_ARG;
     if (c->d <= 0 || c->group_size <= 0) return QVG_ERR_INVALID_ARG;
     if (c->n_centroids < 1 || c->n_centroids > QVG_MAX_CENTROIDS) return QVG_ERR_INVALID_ARG;
     if (c->n_stages < 0 || c->n_stages > QVG_MAX_STAGES) return QVG_ERR_INVALID_ARG;
@@ -135,7 +141,7 @@ size_t conv_words(int H, int T) { return (size_t)3 * H + 1 + (size_t)T * H; }
 // and the earlier stages' stored centroids and assignments.
 struct EncodeWorkspace {
     size_t C = 0, Cb = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, vstats = 0, tstats = 0, r1 = 0,
-           conv = 0, total = 0;
+           conv = 0, mirror = 0, total = 0;
 
     EncodeWorkspace(const qvg_config &c, int H, int N) {
         const size_t D = c.d, K = c.n_centroids, Kp = padded_k(c.n_centroids);
@@ -154,6 +160,8 @@ struct EncodeWorkspace {
         tstats = take((size_t)T * H * TSTAT_BLOCKS * 2 * 4);
         if (c.dtype == QVG_BF16 && T >= 2) r1 = take((size_t)H * N * D * 2);   // R(1) as the stage-2 operand
         conv = take(conv_words(H, T) * 4);
+        // FP8 tables: their values in the tensor dtype, which later residuals read
+        if (c.centroid_format == QVG_CENT_E4M3) mirror = take((size_t)T * H * K * D * dtype_size(c.dtype));
         total = off;
     }
 };
@@ -214,7 +222,7 @@ qvg_status qvg_chunk_bytes(const qvg_config *cfg, int32_t heads, int32_t n_token
     out[0] = H * N * D / 4;
     out[1] = H * N * D / cfg->group_size;
     out[2] = (uint64_t)cfg->n_stages * H * N;
-    out[3] = (uint64_t)cfg->n_stages * H * cfg->n_centroids * D * dtype_size(cfg->dtype);
+    out[3] = (uint64_t)cfg->n_stages * H * table_bytes(*cfg);
     return QVG_OK;
 }
 
@@ -228,7 +236,7 @@ qvg_status qvg_cache_view_bytes(const qvg_config *cfg, int32_t heads, int64_t ca
     out[0] = H * N * D / 4;
     out[1] = H * N * D / cfg->group_size;
     out[2] = (uint64_t)cfg->n_stages * H * N;
-    out[3] = chunks * cfg->n_stages * H * cfg->n_centroids * D * dtype_size(cfg->dtype);
+    out[3] = chunks * cfg->n_stages * H * table_bytes(*cfg);
     return QVG_OK;
 }
 
@@ -371,6 +379,7 @@ static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_he
     int32_t *chg[2] = {conv, conv + H};
     int32_t *done = conv + 2 * H, *ndone = conv + 3 * H, *rounds = conv + 3 * H + 1;
     const bool cvg = cfg->converge > 0;
+    const bool fp8 = cfg->centroid_format == QVG_CENT_E4M3;
     if (need_draw) QVG_LAUNCH("forgy", 0, (double)T * H * K * 4, launch_forgy(T, H, N, K, cfg->seed, idx, s));
 
     // the exactness certificate of the update needs the input's value statistics:
@@ -435,24 +444,36 @@ static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_he
                                          fill[c ^ 1], cv, s));
             }
         }
+        // the stage's centroids as stored; with FP8 tables the store also puts
+        // their values into the operand table, so the final assignment below is
+        // nearest under the stored centroids in every format
+        const size_t tbytes = table_bytes(*cfg);
+        void *cslot = static_cast<char *>(dst->centroids) + ((size_t)chunk_index * T + (t - 1)) * H * tbytes;
+        void *mslot = fp8 ? static_cast<void *>(at<char>(workspace, ws.mirror) + (size_t)(t - 1) * H * K * D * esz)
+                          : nullptr;
+        if (fp8) {
+            QVG_LAUNCH("store_centroids", 0, (double)H * K * D * (4 + 1 + esz + 2 + (cache ? 4 : 0)),
+                       launch_store_e4m3(D, cfg->dtype, H, K, C, static_cast<uint8_t *>(cslot), (int64_t)tbytes, mslot,
+                                         Cb, cache ? cache->data + slice : nullptr,
+                                         tstats + (size_t)(t - 1) * H * TSTAT_BLOCKS * 2, s));
+        } else {
+            QVG_LAUNCH("store_centroids", 0, (double)H * K * D * (4 + esz + (cache ? 4 : 0)),
+                       launch_store_centroids(D, H, K, C, cfg->dtype, cslot, cache ? cache->data + slice : nullptr,
+                                              tstats + (size_t)(t - 1) * H * TSTAT_BLOCKS * 2, s));
+        }
         uint16_t *rout = r1 && t == 1 ? r1 : nullptr;
         QVG_LAUNCH("assign", assign_flops, assign_bytes + (rout ? HND * 2 : 0.0),
                    launch_assign(D, cfg->dtype, H, N, K, asrc, Cb, pi, cap, nullptr, nullptr, rout, nullptr, nullptr,
                                  nullptr, s));
-        void *cslot = static_cast<char *>(dst->centroids) +
-                      (((size_t)chunk_index * T + (t - 1)) * H * K * D) * esz;
-        QVG_LAUNCH("store_centroids", 0, (double)H * K * D * (4 + esz + (cache ? 4 : 0)),
-                   launch_store_centroids(D, H, K, C, cfg->dtype, cslot, cache ? cache->data + slice : nullptr,
-                                          tstats + (size_t)(t - 1) * H * TSTAT_BLOCKS * 2, s));
         if (t < T) {
-            src.cent[t - 1] = cslot;
+            src.cent[t - 1] = fp8 ? mslot : cslot;
             src.pi[t - 1] = pi;
             src.P = t;
         } else {
             // the residual uses the stored centroids: the bf16 operand table for bf16
             // tensors (identical values), the fp32 table otherwise
-            const void *cent = cfg->dtype == QVG_BF16 ? (const void *)Cb : (const void *)C;
-            const int cent_rows = cfg->dtype == QVG_BF16 ? Kp : K;
+            const void *cent = fp8 ? mslot : cfg->dtype == QVG_BF16 ? (const void *)Cb : (const void *)C;
+            const int cent_rows = !fp8 && cfg->dtype == QVG_BF16 ? Kp : K;
             QVG_LAUNCH("residual_quant", HND * T, row_bytes + H * N + (double)H * K * D * esz + HND / 4 + HND / G,
                        launch_quant(D, cfg->dtype, H, N, src, cent, cent_rows, pi, cap, dst->codes + tok0 * (D / 4),
                                     dst->scales + tok0 * (D / G), cap, G, s));
@@ -518,7 +539,7 @@ static qvg_status decode_impl(const qvg_config *cfg, const qvg_cache_view *src, 
     a.scales = src->scales;
     a.assign = src->assign;
     a.cent = src->centroids;
-    a.cent_dtype = cfg->dtype;
+    a.cent_dtype = cfg->centroid_format == QVG_CENT_E4M3 ? DT_E4M3 : cfg->dtype;
     a.cap = src->cap_tokens;
     a.chunk_tokens = src->chunk_tokens;
     a.H = src->heads;
@@ -536,7 +557,7 @@ static qvg_status decode_impl(const qvg_config *cfg, const qvg_cache_view *src, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t chunks = (tok_end - 1) / a.chunk_tokens - tok_begin / a.chunk_tokens + 1;
     double bytes = (double)a.H * ntok * (a.D / 4 + a.D / a.G + a.T + a.D * dtype_size(out_dtype)) +
-                   (double)chunks * a.T * a.H * a.K * a.D * dtype_size(cfg->dtype);
+                   (double)chunks * a.T * a.H * table_bytes(*cfg);
     double flops = (double)a.H * ntok * a.D * (a.T + 1);
     if (rope && rope_heads > 0) {
         bytes += (double)ntok * a.D * 4;             // the rotation table, read once

@@ -345,7 +345,7 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
 // value with its low mantissa byte replaced by the centroid's number
 // (v_perm_b32).  Among negative floats a larger low byte is a smaller value,
 // so equal truncated values go to the lower number; v_med3_f32 keeps the two
-// best and four lanes merge.
+// best, and the four lanes of a token merge their pairs into its three best.
 //
 // Exactness.  The bf16 products are exact in fp32; the instruction adds them
 // and C with fp32 roundings along a shallow tree (an in-kernel probe shows the
@@ -355,12 +355,17 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
 // which keeps every value negative (the 2^-12 |x|^2 margin is far larger)
 // and misorders two centroids only if they lie within
 // 2^-17.4 (|x|^2 + max |c|^2) of each other; a key is within 2^-15 of its
-// value.  A token whose two best keys are further apart than
-//   2^-16 (|x|^2 + max |c|^2) + 2^-14 (|k1| + |k2|)
-// keeps the fp32 winner.  The others (a few in a thousand) are re-decided on
-// fp64 distances, 16 lanes per token: every bf16 x bf16 product is exact in
+// value.  A candidate whose key is further below the best key k1 than
+//   2^-16 (|x|^2 + max |c|^2) + 2^-14 (|k1| + |k|)
+// cannot be the nearest; a token with no such second or third candidate keeps
+// the fp32 winner.  The others are re-decided on fp64 distances of the two or
+// three candidates, 16 lanes per token: every bf16 x bf16 product is exact in
 // fp64 and the sums are exact for the value ranges met in practice, so the
-// decision is that of |c|^2 - 2 <x, c>, lowest index on ties.
+// decision is that of |c|^2 - 2 <x, c>, lowest index on ties.  Every centroid
+// that could be the nearest is a candidate unless four or more lie within
+// the band, or three within one lane's quarter of the centroids (the lane
+// keeps two); then a candidate within the band is chosen, whose distance is
+// within the band of the nearest one's.
 //
 // A workgroup is 16 waves, each taking 32-token tiles; the bf16 tables of up
 // to two heads (rows of D / 8 + 1 16-byte chunks, the last unused, so that the
@@ -563,7 +568,8 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) xx[b] = __int_as_float(list[16 * b + r16]);
     __builtin_amdgcn_wave_barrier();
-    // merge the four lanes of each token, settle the clear cases, list the near ties
+    // merge the four lanes of each token into its three best keys, settle the
+    // clear cases, list the near ties
     int n_list = 0;
     int nchg = 0;   // labels this lane changed (counted when `changed` is set)
 #pragma unroll
@@ -571,17 +577,22 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
         uint32_t u1 = __float_as_uint(q1[b]), u2 = __float_as_uint(q2[b]);
         u1 = (u1 & 0xFFFFFF03u) | ((u1 & 0xFCu) << 2) | (uint32_t)(4 * g);
         u2 = (u2 & 0xFFFFFF03u) | ((u2 & 0xFCu) << 2) | (uint32_t)(4 * g);
-        float k1 = __uint_as_float(u1), k2 = __uint_as_float(u2);
+        float k1 = __uint_as_float(u1), k2 = __uint_as_float(u2), k3 = -__FLT_MAX__;
+        // the three largest of two sorted triples a, w: the j-th largest of the
+        // union is the maximum over i of min(a_i, w_(j-i)) with a_0 = w_0 = +inf
 #pragma unroll
         for (int o = 16; o <= 32; o <<= 1) {
-            const float w1 = __shfl_xor(k1, o), w2 = __shfl_xor(k2, o);
+            const float w1 = __shfl_xor(k1, o), w2 = __shfl_xor(k2, o), w3 = __shfl_xor(k3, o);
+            k3 = fmax_key(fmax_key(k3, w3), fmax_key(fmin_key(k1, w2), fmin_key(k2, w1)));
             k2 = fmax_key(fmin_key(k1, w1), fmax_key(k2, w2));
             k1 = fmax_key(k1, w1);
         }
         const int c1 = (int)(__float_as_uint(k1) & 0xFFu), c2 = (int)(__float_as_uint(k2) & 0xFFu);
-        const float cnmax = -2.0f * fminf(lhcn[c1], lhcn[c2]);
-        const float tol = 0x1p-16f * (xx[b] + cnmax) + 0x1p-14f * (fabsf(k1) + fabsf(k2));
-        const bool tie = (k1 - k2) <= tol;
+        const int c3 = (int)(__float_as_uint(k3) & 0xFFu);
+        const float tol2 = 0x1p-16f * (xx[b] - 2.0f * fminf(lhcn[c1], lhcn[c2])) + 0x1p-14f * (fabsf(k1) + fabsf(k2));
+        const float tol3 = 0x1p-16f * (xx[b] - 2.0f * fminf(lhcn[c1], lhcn[c3])) + 0x1p-14f * (fabsf(k1) + fabsf(k3));
+        const bool third = (k1 - k3) <= tol3;   // c3 might be the nearest too
+        const bool tie = third || (k1 - k2) <= tol2;
         const int n = tok0 + 16 * b + r16;
         const bool mine = g == 0 && n < N;
         if (mine && !tie) {
@@ -594,26 +605,30 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
         const uint64_t m = __ballot(mine && tie);
         if (mine && tie) {
             const int pos = n_list + __popcll(m & ((1ull << lane) - 1ull));
-            list[pos] = ((16 * b + r16) << 16) | (c1 << 8) | c2;
+            list[pos] = ((16 * b + r16) << 24) | (c1 << 16) | (c2 << 8) | (third ? c3 : c2);
         }
         n_list += __popcll(m);
     }
     __builtin_amdgcn_wave_barrier();
-    // near ties: 16 lanes per token, 8 channels each, fp64 distances
+    // near ties: 16 lanes per token, 8 channels each, fp64 distances of the two
+    // (or three) candidates
     const int sub = lane & 15, grp = lane >> 4;
     for (int j0 = 0; j0 < n_list; j0 += 4) {
         const int j = j0 + grp;
         const int e = list[j < n_list ? j : 0];
-        const int nl = e >> 16, c1 = (e >> 8) & 0xFF, c2 = e & 0xFF;
+        const int nl = (e >> 24) & 0xFF, c1 = (e >> 16) & 0xFF, c2 = (e >> 8) & 0xFF, c3 = e & 0xFF;
         const int n = tok0 + nl;
-        double p1 = 0.0, p2 = 0.0;   // <x, c1>, <x, c2>
+        const bool any3 = __ballot(j < n_list && c3 != c2) != 0;   // a third candidate in this batch
+        double p1 = 0.0, p2 = 0.0, p3 = 0.0;   // <x, c1>, <x, c2>, <x, c3>
         if (j < n_list && sub < CH) {
             const uint4 xv = src_row8_bf16<D, KVT>(src, h, n, 8 * sub);
             const uint4 a1 = lds[c1 * (CH + 1) + sub];
             const uint4 a2 = lds[c2 * (CH + 1) + sub];
+            const uint4 a3 = lds[c3 * (CH + 1) + sub];
             const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
             const uint32_t aw[4] = {a1.x, a1.y, a1.z, a1.w};
             const uint32_t bw[4] = {a2.x, a2.y, a2.z, a2.w};
+            const uint32_t cw[4] = {a3.x, a3.y, a3.z, a3.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const double xl = (double)__uint_as_float(xw[i] << 16);
@@ -622,13 +637,22 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
                 p1 = fma(xh, (double)__uint_as_float(aw[i] & 0xFFFF0000u), p1);
                 p2 = fma(xl, (double)__uint_as_float(bw[i] << 16), p2);
                 p2 = fma(xh, (double)__uint_as_float(bw[i] & 0xFFFF0000u), p2);
+                if (any3) {
+                    p3 = fma(xl, (double)__uint_as_float(cw[i] << 16), p3);
+                    p3 = fma(xh, (double)__uint_as_float(cw[i] & 0xFFFF0000u), p3);
+                }
             }
         }
         p1 = group_sum<16>(p1);
         p2 = group_sum<16>(p2);
+        if (any3) p3 = group_sum<16>(p3);
         if (j < n_list && sub == 0) {
             const double e1 = lcn64[c1] - 2.0 * p1, e2 = lcn64[c2] - 2.0 * p2;
-            const int best = (e2 < e1 || (e2 == e1 && c2 < c1)) ? c2 : c1;
+            int best = (e2 < e1 || (e2 == e1 && c2 < c1)) ? c2 : c1;
+            if (c3 != c2) {
+                const double eb = best == c1 ? e1 : e2, e3 = lcn64[c3] - 2.0 * p3;
+                if (e3 < eb || (e3 == eb && c3 < best)) best = c3;
+            }
             uint8_t *pp = pi + (size_t)h * pi_hs + n;
             if (changed) nchg += (int)*pp != best;
             *pp = (uint8_t)best;
@@ -1672,6 +1696,123 @@ __global__ __launch_bounds__(256) void k_store_centroids(int64_t per_head8, cons
     }
 }
 
+// FP8 storage: one workgroup per head.  The table's exponent e is the smallest
+// with max|C| <= 448 * 2^e; every value is stored as the E4M3FN code of
+// C / 2^e (nearest, ties to even; the sign kept unless the code is zero), and
+// its decoded value (code value times 2^e, exact in bf16 and fp32) goes to the
+// mirror table [K][D] of the tensor dtype and to the operand table Cb [Kp][D],
+// so that the stage's final assignment and the later residuals use the
+// centroids as stored.  The table in dst: a 16-byte header (e as int32, then
+// zeros) and K D code bytes.  tstats as for k_store_centroids, from the mirror.
+template <typename KVT>
+__global__ __launch_bounds__(1024) void k_store_e4m3(int K, int D, int Kp, const float *C, uint8_t *dst,
+                                                     int64_t tbytes, KVT *mirror, uint16_t *Cb, float *cache,
+                                                     uint32_t *tstats) {
+    const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t nv = (int64_t)K * D;   // a multiple of 8
+    const float *c = C + h * nv;
+    __shared__ uint32_t red[2][16];
+    uint32_t mx = 0u;
+    for (int64_t i = (int64_t)tid * 4; i < nv; i += 4096) {
+        const float4 v = *reinterpret_cast<const float4 *>(c + i);
+        mx = max(max(mx, __float_as_uint(v.x) & 0x7FFFFFFFu), __float_as_uint(v.y) & 0x7FFFFFFFu);
+        mx = max(max(mx, __float_as_uint(v.z) & 0x7FFFFFFFu), __float_as_uint(v.w) & 0x7FFFFFFFu);
+    }
+    mx = wave_max_u(mx);
+    if (lane == 0) red[0][wave] = mx;
+    __syncthreads();
+    mx = 0u;
+    for (int w = 0; w < 16; ++w) mx = max(mx, red[0][w]);
+    const float amax = __uint_as_float(mx);
+    int e = 0;
+    if (amax > 0.f) {
+        int q;
+        (void)frexpf(amax, &q);                      // amax = m 2^q, 0.5 <= m < 1
+        e = q - 9;
+        while (amax > ldexpf(448.f, e)) ++e;         // exact comparisons with 448 2^e
+        while (amax <= ldexpf(448.f, e - 1)) --e;
+    }
+    uint8_t *tb = dst + h * tbytes;
+    if (tid < 4) reinterpret_cast<int32_t *>(tb)[tid] = tid == 0 ? e : 0;
+    uint8_t *codes = tb + 16;
+    uint32_t mn = 0xFFFFFFFFu, tmx = 0u;
+    for (int64_t i = (int64_t)tid * 8; i < nv; i += 8192) {
+        const float4 a = *reinterpret_cast<const float4 *>(c + i), b = *reinterpret_cast<const float4 *>(c + i + 4);
+        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        uint32_t cb[8];
+        float dv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            uint32_t code = e4m3_encode_nonneg(ldexpf(fabsf(v[j]), -e));
+            if (code && (__float_as_uint(v[j]) >> 31)) code |= 0x80u;
+            cb[j] = code;
+            dv[j] = ldexpf(e4m3_decode(code), e);
+        }
+        *reinterpret_cast<uint2 *>(codes + i) = make_uint2(cb[0] | (cb[1] << 8) | (cb[2] << 16) | (cb[3] << 24),
+                                                           cb[4] | (cb[5] << 8) | (cb[6] << 16) | (cb[7] << 24));
+        const int64_t row = i / D, col = i - row * D;
+        uint32_t bb[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) bb[j] = __float_as_uint(dv[j]) >> 16;   // exact: at most 4 significant bits
+        *reinterpret_cast<uint4 *>(Cb + ((size_t)h * Kp + row) * D + col) =
+            make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16), bb[6] | (bb[7] << 16));
+        KVT *mr = mirror + h * nv + i;
+        if constexpr (sizeof(KVT) == 2) {
+            *reinterpret_cast<uint4 *>(mr) =
+                make_uint4(bb[0] | (bb[1] << 16), bb[2] | (bb[3] << 16), bb[4] | (bb[5] << 16), bb[6] | (bb[7] << 16));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t m = bb[j] & 0x7FFFu;
+                tmx = max(tmx, m);
+                mn = min(mn, m - 1u);
+            }
+        } else {
+            reinterpret_cast<float4 *>(mr)[0] = make_float4(dv[0], dv[1], dv[2], dv[3]);
+            reinterpret_cast<float4 *>(mr)[1] = make_float4(dv[4], dv[5], dv[6], dv[7]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t m = __float_as_uint(dv[j]) & 0x7FFFFFFFu;
+                tmx = max(tmx, m);
+                mn = min(mn, m - 1u);
+            }
+        }
+        if (cache) {
+            reinterpret_cast<float4 *>(cache + h * nv + i)[0] = a;
+            reinterpret_cast<float4 *>(cache + h * nv + i)[1] = b;
+        }
+    }
+    if (!tstats) return;
+    mn = (uint32_t)wave_min_i((int)(mn ^ 0x80000000u)) ^ 0x80000000u;   // unsigned minimum
+    tmx = wave_max_u(tmx);
+    __syncthreads();
+    if (lane == 0) {
+        red[0][wave] = mn;
+        red[1][wave] = tmx;
+    }
+    __syncthreads();
+    if (tid < TSTAT_BLOCKS) {   // the head's pair, repeated in every partial slot
+        uint32_t a = 0xFFFFFFFFu, b = 0u;
+        for (int w = 0; w < 16; ++w) {
+            a = min(a, red[0][w]);
+            b = max(b, red[1][w]);
+        }
+        tstats[((size_t)h * TSTAT_BLOCKS + tid) * 2] = a;
+        tstats[((size_t)h * TSTAT_BLOCKS + tid) * 2 + 1] = b;
+    }
+}
+
+hipError_t launch_store_e4m3(int D, int dtype, int H, int K, const float *C, uint8_t *dst, int64_t table_bytes,
+                             void *mirror, uint16_t *Cb, float *cache, uint32_t *tstats, hipStream_t s) {
+    if (table_bytes != (int64_t)K * D + 16 || H >= 65536) return hipErrorInvalidValue;
+    if (dtype == DT_BF16)
+        QVG_KERNEL(k_store_e4m3<uint16_t>, dim3(H), dim3(1024), 0, s, K, D, padded_k(K), C, dst, table_bytes,
+                   static_cast<uint16_t *>(mirror), Cb, cache, tstats);
+    else
+        QVG_KERNEL(k_store_e4m3<float>, dim3(H), dim3(1024), 0, s, K, D, padded_k(K), C, dst, table_bytes,
+                   static_cast<float *>(mirror), Cb, cache, tstats);
+    return hipGetLastError();
+}
+
 hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype, void *dst, float *cache,
                                   uint32_t *tstats, hipStream_t s) {
     const int64_t per_head8 = (int64_t)K * D / 8;   // D is a multiple of 8
@@ -1904,9 +2045,9 @@ __device__ __forceinline__ void decode_slice(int T, uint32_t w0, uint32_t w1, ui
 // before the first is used; TT = -1 takes T at run time.
 constexpr int DEC_U = 2;
 
-template <int D, typename CentT, typename OutT, int TT>
+template <int D, typename CentT, typename OutT, int TT, bool FP8>
 __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
-                                                const uint8_t *__restrict__ assign, const CentT *__restrict__ cent,
+                                                const uint8_t *__restrict__ assign, const void *__restrict__ cent_v,
                                                 int64_t cap, int chunk_tokens, int H, int K, int T_rt, int G,
                                                 int64_t tok_begin, int64_t ntok, const float *__restrict__ rope,
                                                 int rope_heads, OutT *__restrict__ out, int64_t out_hs,
@@ -1951,10 +2092,24 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ code
                 kk = assign[((size_t)t * H + h) * cap + n[u]];
                 kk = kk < K ? kk : K - 1;
             }
-            const uint4 *src = reinterpret_cast<const uint4 *>(
-                cent + ((((size_t)c * T + t) * H + h) * K + kk) * D + hf * (D / 2) + 8 * j);
-            cv[0] = src[0];
-            if constexpr (sizeof(CentT) == 4) cv[1] = src[1];
+            if constexpr (FP8) {   // 8 codes, widened to bf16 exactly: code value x 2^e
+                const uint8_t *tbl = static_cast<const uint8_t *>(cent_v) + (((size_t)c * T + t) * H + h) * (K * D + 16);
+                const float sc = ldexpf(1.f, *reinterpret_cast<const int32_t *>(tbl));
+                const uint2 v = *reinterpret_cast<const uint2 *>(tbl + 16 + (size_t)kk * D + hf * (D / 2) + 8 * j);
+                uint32_t o[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t w = q < 2 ? v.x : v.y, sh = 16 * (q & 1);
+                    o[q] = (__float_as_uint(e4m3_decode((w >> sh) & 0xFFu) * sc) >> 16) |
+                           (__float_as_uint(e4m3_decode((w >> (sh + 8)) & 0xFFu) * sc) & 0xFFFF0000u);
+                }
+                cv[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            } else {
+                const uint4 *src = reinterpret_cast<const uint4 *>(
+                    static_cast<const CentT *>(cent_v) + ((((size_t)c * T + t) * H + h) * K + kk) * D + hf * (D / 2) + 8 * j);
+                cv[0] = src[0];
+                if constexpr (sizeof(CentT) == 4) cv[1] = src[1];
+            }
         });
     }
 }
@@ -1987,11 +2142,13 @@ __device__ __forceinline__ uint32_t load_scales(const uint8_t *p) {
     else return *p;
 }
 
-template <int D, int G, typename CentT, typename OutT, int TT, bool ROPE>
+// FP8: the stored tables are E4M3 codes behind a 16-byte exponent header (CentT
+// is then the bf16 form they take in LDS, exactly).
+template <int D, int G, typename CentT, typename OutT, int TT, bool ROPE, bool FP8>
 __global__ __launch_bounds__(DEC_LDS_THREADS, 8) void k_decode_lds(const uint8_t *__restrict__ codes,
                                                                    const uint8_t *__restrict__ scales,
                                                                    const uint8_t *__restrict__ assign,
-                                                                   const CentT *__restrict__ cent, int64_t cap,
+                                                                   const void *__restrict__ cent_v, int64_t cap,
                                                                    int chunk_tokens, int H, int K,
                                                                    int64_t tok_begin, int64_t tok_end,
                                                                    int64_t c_first, int64_t n_units,
@@ -2021,11 +2178,34 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, 8) void k_decode_lds(const uint8_t
     const int64_t c = c_first + uu / H;
     const int tid = threadIdx.x;
     for (int t = 0; t < TT; ++t) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(cent + (((size_t)c * TT + t) * H + h) * K * D);
-        for (int i = tid; i < K * CHH; i += DEC_LDS_THREADS) {
-            const int row = i / CHH, q = i - row * CHH;
-            const int r = t * K + row;
-            tab[r * CHH + (q ^ (r & (CHH - 1)))] = src[(size_t)row * PARTS * CHH + hf * CHH + q];
+        if constexpr (FP8) {
+            // 16 codes per load become two bf16 chunks: value = code value x 2^e
+            const uint8_t *tbl = static_cast<const uint8_t *>(cent_v) + (((size_t)c * TT + t) * H + h) * (K * D + 16);
+            const float sc = ldexpf(1.f, *reinterpret_cast<const int32_t *>(tbl));
+            const uint4 *src = reinterpret_cast<const uint4 *>(tbl + 16);
+            constexpr int SCH = DP / 16;   // 16-byte code chunks per part of a row
+            for (int i = tid; i < K * SCH; i += DEC_LDS_THREADS) {
+                const int row = i / SCH, q = i - row * SCH;
+                const int r = t * K + row;
+                const uint4 v = src[(size_t)row * (D / 16) + hf * SCH + q];
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                uint32_t o[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const uint32_t b0 = (w[k / 2] >> (16 * (k & 1))) & 0xFFu, b1 = (w[k / 2] >> (16 * (k & 1) + 8)) & 0xFFu;
+                    o[k] = (__float_as_uint(e4m3_decode(b0) * sc) >> 16) | (__float_as_uint(e4m3_decode(b1) * sc) & 0xFFFF0000u);
+                }
+                tab[r * CHH + ((2 * q) ^ (r & (CHH - 1)))] = make_uint4(o[0], o[1], o[2], o[3]);
+                tab[r * CHH + ((2 * q + 1) ^ (r & (CHH - 1)))] = make_uint4(o[4], o[5], o[6], o[7]);
+            }
+        } else {
+            const CentT *cent = static_cast<const CentT *>(cent_v);
+            const uint4 *src = reinterpret_cast<const uint4 *>(cent + (((size_t)c * TT + t) * H + h) * K * D);
+            for (int i = tid; i < K * CHH; i += DEC_LDS_THREADS) {
+                const int row = i / CHH, q = i - row * CHH;
+                const int r = t * K + row;
+                tab[r * CHH + (q ^ (r & (CHH - 1)))] = src[(size_t)row * PARTS * CHH + hf * CHH + q];
+            }
         }
     }
     const int64_t tb = max(tok_begin, c * chunk_tokens), te = min(tok_end, (c + 1) * chunk_tokens);
@@ -2107,7 +2287,8 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, 8) void k_decode_lds(const uint8_t
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
-    const size_t tab_bytes = (size_t)a.T * a.K * (a.D / DEC_PARTS) * (a.cent_dtype == DT_BF16 ? 2 : 4);
+    // tables in LDS: bf16 (FP8 tables are widened to bf16 there) or fp32
+    const size_t tab_bytes = (size_t)a.T * a.K * (a.D / DEC_PARTS) * (a.cent_dtype == DT_F32 ? 4 : 2);
     const size_t lds = tab_bytes + dec_meta_bytes(a.D, a.G, a.T);
     // the staged loads need the scale bytes of a part aligned to their size
     const bool scales_aligned = (reinterpret_cast<uintptr_t>(a.scales) & 3u) == 0;
@@ -2119,11 +2300,19 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
             dim3 g((unsigned)nb), b(DEC_LDS_THREADS);
 #define QVG_DECL_R(DD, GG, CT, OT, TT, RO)                                                                        \
     do {                                                                                                          \
-        (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, GG, CT, OT, TT, RO>,                             \
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                          \
-        QVG_KERNEL((k_decode_lds<DD, GG, CT, OT, TT, RO>), g, b, lds, s, a.codes, a.scales, a.assign,             \
-                   (const CT *)a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.tok_begin, a.tok_begin + a.ntok, c0,    \
-                   units, a.rope, a.rope_heads, (OT *)a.out, a.out_hs);                                           \
+        if (a.cent_dtype == DT_E4M3) {                                                                            \
+            (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, GG, uint16_t, OT, TT, RO, true>,             \
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
+            QVG_KERNEL((k_decode_lds<DD, GG, uint16_t, OT, TT, RO, true>), g, b, lds, s, a.codes, a.scales,       \
+                       a.assign, a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.tok_begin, a.tok_begin + a.ntok, c0,  \
+                       units, a.rope, a.rope_heads, (OT *)a.out, a.out_hs);                                       \
+        } else {                                                                                                  \
+            (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, GG, CT, OT, TT, RO, false>,                  \
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
+            QVG_KERNEL((k_decode_lds<DD, GG, CT, OT, TT, RO, false>), g, b, lds, s, a.codes, a.scales, a.assign,  \
+                       a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.tok_begin, a.tok_begin + a.ntok, c0, units,     \
+                       a.rope, a.rope_heads, (OT *)a.out, a.out_hs);                                              \
+        }                                                                                                         \
     } while (0)
 #define QVG_DECL(DD, GG, CT, OT, TT)                               \
     do {                                                           \
@@ -2146,7 +2335,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     } while (0)
 #define QVG_DECL_C(DD, GG)                                 \
     do {                                                   \
-        if (a.cent_dtype == DT_BF16) QVG_DECL_O(DD, GG, uint16_t); \
+        if (a.cent_dtype != DT_F32) QVG_DECL_O(DD, GG, uint16_t); \
         else QVG_DECL_O(DD, GG, float);                    \
     } while (0)
 #define QVG_DECL_G(DD)                                     \
@@ -2172,9 +2361,16 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     const uint32_t bph = (uint32_t)((a.ntok + TPB - 1) / TPB);
     dim3 g(bph * a.H), b(256);
 #define QVG_DEC(DD, CT, OT, TT)                                                                                   \
-    QVG_KERNEL((k_decode<DD, CT, OT, TT>), g, b, 0, s, a.codes, a.scales, a.assign, (const CT *)a.cent,    \
+    do {                                                                                                          \
+        if (a.cent_dtype == DT_E4M3)                                                                              \
+            QVG_KERNEL((k_decode<DD, uint16_t, OT, TT, true>), g, b, 0, s, a.codes, a.scales, a.assign, a.cent,   \
                        a.cap, a.chunk_tokens, a.H, a.K, a.T, a.G, a.tok_begin, a.ntok, a.rope, a.rope_heads,     \
-                       (OT *)a.out, a.out_hs, bph)
+                       (OT *)a.out, a.out_hs, bph);                                                               \
+        else                                                                                                      \
+            QVG_KERNEL((k_decode<DD, CT, OT, TT, false>), g, b, 0, s, a.codes, a.scales, a.assign, a.cent,        \
+                       a.cap, a.chunk_tokens, a.H, a.K, a.T, a.G, a.tok_begin, a.ntok, a.rope, a.rope_heads,     \
+                       (OT *)a.out, a.out_hs, bph);                                                               \
+    } while (0)
 #define QVG_DEC_T(DD, CT, OT)                              \
     do {                                                   \
         switch (a.T) {                                     \
@@ -2193,7 +2389,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     } while (0)
 #define QVG_DEC_C(DD)                                      \
     do {                                                   \
-        if (a.cent_dtype == DT_BF16) QVG_DEC_O(DD, uint16_t); \
+        if (a.cent_dtype != DT_F32) QVG_DEC_O(DD, uint16_t); \
         else QVG_DEC_O(DD, float);                         \
     } while (0)
     if (a.D == 128) QVG_DEC_C(128); else QVG_DEC_C(64);

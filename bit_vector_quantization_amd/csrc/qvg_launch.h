@@ -8,7 +8,7 @@
 
 namespace qvg {
 
-enum { DT_F32 = 0, DT_BF16 = 1 };
+enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };   // DT_E4M3: stored centroid tables only
 
 constexpr int MAX_PREV = 7;   // earlier stages a residual can be rebuilt from
 
@@ -115,6 +115,13 @@ constexpr int TSTAT_BLOCKS = 4;
 hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype, void *dst_slice,
                                   float *cache_slice, uint32_t *tstats, hipStream_t s);
 
+// FP8 storage of one stage's tables (see k_store_e4m3): dst [H] tables of
+// table_bytes = 16 + K D bytes (exponent header, E4M3 codes); mirror [H][K][D]
+// of the tensor dtype and Cb [H][Kp][D] bf16 receive the stored values; cache
+// and tstats as for launch_store_centroids.
+hipError_t launch_store_e4m3(int D, int dtype, int H, int K, const float *C, uint8_t *dst, int64_t table_bytes,
+                             void *mirror, uint16_t *Cb, float *cache, uint32_t *tstats, hipStream_t s);
+
 // r = R(t-1) - cent[pi] (cent non-null; cent [H][cent_rows][D] of the tensor
 // dtype) or r = R(t-1); then 2-bit codes and E4M3 scales of r, head stride
 // q_cap tokens.
@@ -127,7 +134,7 @@ hipError_t launch_quant(int D, int dtype, int H, int N, const Src &src, const vo
 struct DecodeArgs {
     const uint8_t *codes, *scales, *assign;
     const void *cent;
-    int cent_dtype;
+    int cent_dtype;   // DT_BF16, DT_F32, or DT_E4M3: tables of 16 + K D bytes
     int64_t cap;
     int chunk_tokens, H, K, T, G, D;
     int64_t tok_begin, ntok;

@@ -55,6 +55,13 @@ enum {
 
 enum { QVG_F32 = 0, QVG_BF16 = 1 };
 
+/* How the centroid tables are stored (qvg_config.centroid_format). */
+enum {
+    QVG_CENT_NATIVE = 0, /* in the tensor dtype (bf16 or fp32)                          */
+    QVG_CENT_E4M3 = 1    /* FP8: per table a 16-byte header with an exponent e (int32,
+                            then zeros) and K*d E4M3FN codes; value = code value * 2^e */
+};
+
 #define QVG_MAX_CENTROIDS 256 /* assignments are stored as uint8 (163.com, section 7) */
 #define QVG_MAX_STAGES 8
 
@@ -81,7 +88,17 @@ enum { QVG_F32 = 0, QVG_BF16 = 1 };
  *                reports the rounds run.
  *   seed         codec seed; the cold draw of (head h, stage t) is keyed by
  *                ((seed * 65536 + h) * 64 + t) mod 2^64
- *   dtype        QVG_BF16 or QVG_F32: the input X and the stored centroids       */
+ *   dtype        QVG_BF16 or QVG_F32: the input X (and the stored centroids with
+ *                QVG_CENT_NATIVE)
+ *   centroid_format  QVG_CENT_NATIVE, or QVG_CENT_E4M3: every stored table
+ *                (chunk, stage, head) in the FP8 format the pages use for the
+ *                scales (163.com article, sections 5-7, where the centroids are
+ *                a small share of the compressed bytes): e is the smallest
+ *                exponent with max|C| <= 448 * 2^e, each value the E4M3FN code
+ *                of C / 2^e (nearest, ties to even).  A stage's labels and the
+ *                later residuals use the stored values; the streaming cache
+ *                keeps the unrounded fp32 centroids.  Halves the table bytes.
+ *   reserved     must be 0                                                       */
 typedef struct {
     int32_t d;
     int32_t n_centroids;
@@ -92,13 +109,16 @@ typedef struct {
     uint64_t seed;
     int32_t dtype;
     int32_t converge; /* >= 0 */
+    int32_t centroid_format;
+    int32_t reserved;
 } qvg_config;
 
 /* The compressed cache of one tensor (K or V) of one layer, caller-allocated.
  *   codes      [H][cap_tokens][d/4]       uint8, four 2-bit codes per byte, lowest channel in bits 0-1
  *   scales     [H][cap_tokens][d/G]       uint8, FP8 E4M3FN (OCP) per-group scales
  *   assign     [T][H][cap_tokens]         uint8 centroid index per token and stage
- *   centroids  [n_chunks][T][H][K][d]     dtype (bf16 or fp32) stored centroids,
+ *   centroids  [n_chunks][T][H] tables of K x d stored centroids: dtype values
+ *              (QVG_CENT_NATIVE) or 16 + K*d bytes each (QVG_CENT_E4M3),
  *              n_chunks = ceil(cap_tokens / chunk_tokens)
  * Chunk c holds tokens [c * chunk_tokens, min((c + 1) * chunk_tokens, cap_tokens)).
  * Buffer sizes: qvg_cache_view_bytes.                                           */
@@ -129,7 +149,8 @@ qvg_status qvg_config_validate(const qvg_config *cfg);
  * 2-bit codes with FP8 E4M3 per-group scales; section 7: uint8 assignments of
  * 256 centroids, group sizes 16 / 64; the stored centroids of every stage):
  * out[0] codes = H*N*d/4, out[1] scales = H*N*d/G, out[2] assignments = T*H*N,
- * out[3] centroids = T*H*K*d*sizeof(dtype).  Host only. */
+ * out[3] centroids = T*H*K*d*sizeof(dtype) (QVG_CENT_E4M3: T*H*(16 + K*d)).
+ * Host only. */
 qvg_status qvg_chunk_bytes(const qvg_config *cfg, int32_t heads, int32_t n_tokens, uint64_t out[4]);
 
 /* Sizes of the four buffers of a qvg_cache_view holding `cap_tokens` tokens per
@@ -292,7 +313,8 @@ qvg_status qvg_group_quant(const float *r, int64_t r_head_stride, int32_t heads,
  * quantised residual, adding back each stage's stored centroids in reverse;
  * section 5: the fused dequantisation kernel; storage format of sections 5 and 7):
  *   codes [H][N][d/4], scales [H][N][d/G], assign [T][H][N] uint8,
- *   centroids [T][H][K][d] (cfg->dtype)  ->  out [H][N][d] (out_dtype), contiguous. */
+ *   centroids [T][H] tables in cfg's centroid format  ->  out [H][N][d] (out_dtype),
+ *   contiguous. */
 qvg_status qvg_dequant_reconstruct(const qvg_config *cfg, int32_t heads, int32_t n_tokens,
                                    const uint8_t *codes, const uint8_t *scales,
                                    const uint8_t *assign, const void *centroids, void *out,

@@ -73,6 +73,7 @@ class CodecConfig:
     seed: int
     dtype: str = "bf16"        # "bf16" or "f32": input values and centroid storage
     converge: int = 0          # 0: fixed round counts; c >= 1: stop once a round moves fewer than c tokens
+    centroid_format: str = "native"   # "native": stored in dtype; "e4m3": FP8 E4M3 times 2^e per table
 
 
 # --------------------------------------------------------------------------
@@ -174,6 +175,44 @@ def lloyd(R: np.ndarray, C0: np.ndarray, iters: int, mode: str = "parity", conve
 
 
 # --------------------------------------------------------------------------
+# centroid storage in FP8
+# --------------------------------------------------------------------------
+#
+# A variant of the storage format: the pages count the centroids as a minor
+# share of the compressed cache next to the 2-bit values (163.com article,
+# section 6) and store the scales in FP8 E4M3 (section 5); storing the
+# centroid tables in the same FP8 format halves their bytes.  Reading: one
+# power-of-two factor 2^e per stored table (chunk, stage, head), the smallest
+# that keeps the table's largest magnitude within E4M3's 448, and every value
+# rounded to the nearest E4M3 value of v / 2^e (ties to even).  A power of two
+# keeps the scaling exact, so every stored value is an E4M3 value times 2^e,
+# which bf16 and fp32 hold exactly.
+
+E4M3_TABLE_HEADER = 16   # bytes in front of each stored FP8 table: its exponent e (int32) and padding
+
+
+def e4m3_table_exponent(C: np.ndarray) -> int:
+    """Smallest integer e with max|C| <= 448 * 2^e (0 for an all-zero table)."""
+    amax = float(np.max(np.abs(np.asarray(C, np.float64))))
+    if amax == 0.0:
+        return 0
+    e = math.frexp(amax)[1] - 9                  # a first guess, then exact comparisons
+    while amax > math.ldexp(448.0, e):
+        e += 1
+    while amax <= math.ldexp(448.0, e - 1):
+        e -= 1
+    return e
+
+
+def store_e4m3(C: np.ndarray):
+    """(e, codes, values) of one centroid table stored in FP8: codes are the
+    E4M3FN bytes of C / 2^e, values their decoded magnitudes times 2^e."""
+    e = e4m3_table_exponent(C)
+    codes = e4m3_encode(np.ldexp(np.asarray(C, np.float64), -e))
+    return e, codes, np.ldexp(e4m3_decode(codes), e)
+
+
+# --------------------------------------------------------------------------
 # 2-bit group quantisation and its inverse
 # --------------------------------------------------------------------------
 
@@ -233,9 +272,12 @@ class Encoded:
     residuals: Optional[List[np.ndarray]] = None   # R(0..T), each [H][N][d]
     sse: Optional[List[List[List[float]]]] = None  # [t][h] -> per-iteration SSE
     rounds: Optional[np.ndarray] = None            # [T][H] Lloyd updates run
+    cent_exp: Optional[np.ndarray] = None          # [T][H] table exponents (FP8 centroid storage)
 
 
-def _store(C: np.ndarray, dtype: str) -> np.ndarray:
+def _store(C: np.ndarray, dtype: str, fmt: str = "native") -> np.ndarray:
+    if fmt == "e4m3":
+        return store_e4m3(C)[2].astype(F32)
     return (bf16_round(C) if dtype == "bf16" else np.asarray(C, np.float64)).astype(F32)
 
 
@@ -264,6 +306,8 @@ def encode_chunk(X: np.ndarray, cfg: CodecConfig, cache: Optional[np.ndarray] = 
     residuals = [X.astype(np.float64)] if keep_residuals else None
     sse = [[None] * H for _ in range(T)]
     rounds = np.zeros((T, H), np.int32)
+    fp8 = cfg.centroid_format == "e4m3"
+    cexp = np.zeros((T, H), np.int32) if fp8 else None
     Rall = X.astype(np.float64)
     for h in range(H):
         R = Rall[h]
@@ -275,7 +319,11 @@ def encode_chunk(X: np.ndarray, cfg: CodecConfig, cache: Optional[np.ndarray] = 
             C, lab, hist = lloyd(R, C0, n_it, mode, converge=cfg.converge)
             sse[t - 1][h] = hist
             rounds[t - 1, h] = len(hist)
-            Cs = _store(C, cfg.dtype) if mode == "parity" else C
+            Cs = _store(C, cfg.dtype, cfg.centroid_format) if mode == "parity" else C
+            if fp8:
+                # the stage's labels are nearest under the centroids as stored
+                cexp[t - 1, h] = e4m3_table_exponent(C)
+                lab = assign(R, Cs.astype(np.float64), mode)
             asg[t - 1, h] = lab.astype(np.uint8)
             cent[t - 1, h] = Cs
             new_cache[t - 1, h] = C.astype(F32) if mode == "parity" else C
@@ -289,7 +337,7 @@ def encode_chunk(X: np.ndarray, cfg: CodecConfig, cache: Optional[np.ndarray] = 
         _, packed, s_code = group_quant(R.astype(F32), G)
         codes[h] = packed
         scales[h] = s_code
-    return Encoded(codes, scales, asg, cent, new_cache, residuals, sse, rounds)
+    return Encoded(codes, scales, asg, cent, new_cache, residuals, sse, rounds, cexp)
 
 
 def rope_rotate(y: np.ndarray, table: np.ndarray) -> np.ndarray:
@@ -373,11 +421,12 @@ def chunk_bytes(cfg: CodecConfig, heads: int, n_tokens: int) -> Dict[str, int]:
     """Bytes one encoded chunk occupies, by component."""
     d, K, T, G = cfg.d, cfg.n_centroids, cfg.n_stages, cfg.group_size
     bc = 2 if cfg.dtype == "bf16" else 4
+    table = K * d + E4M3_TABLE_HEADER if cfg.centroid_format == "e4m3" else K * d * bc
     return {
         "codes": heads * n_tokens * d // 4,
         "scales": heads * n_tokens * d // G,
         "assign": T * heads * n_tokens,
-        "centroids": T * heads * K * d * bc,
+        "centroids": T * heads * table,
     }
 
 

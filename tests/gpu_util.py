@@ -35,7 +35,14 @@ def ocfg(p: synthkv.Preset, tensor: str, **kw) -> oracle.CodecConfig:
 def gcfg(oc: oracle.CodecConfig):
     q = lib()
     return q.config(oc.d, oc.n_centroids, oc.n_stages, oc.group_size, oc.iters_cold, oc.iters_warm,
-                    oc.seed, oc.dtype)
+                    oc.seed, oc.dtype, oc.converge, oc.centroid_format)
+
+
+def fp8_tables(raw: np.ndarray, K: int, d: int):
+    """Stored FP8 tables [..][16 + K d] bytes -> (values [..][K][d] fp32, exponents [..])."""
+    e = raw[..., :4].copy().view(np.int32)[..., 0]
+    vals = oracle.e4m3_decode(raw[..., 16:]).reshape(raw.shape[:-1] + (K, d))
+    return np.ldexp(vals, e[..., None, None]).astype(np.float32), e
 
 
 def to_dev(X: np.ndarray, dtype: str) -> torch.Tensor:
@@ -71,8 +78,11 @@ def fetch(dst, chunk: int, oc: oracle.CodecConfig):
     """Chunk `chunk` of a CompressedKV as oracle-shaped arrays."""
     b, e = chunk * dst.chunk_tokens, min((chunk + 1) * dst.chunk_tokens, dst.cap)
     T = oc.n_stages
+    cent = to_np(dst.centroids[chunk, :T])
+    if oc.centroid_format == "e4m3":
+        cent, _ = fp8_tables(cent, oc.n_centroids, oc.d)
     return dict(codes=to_np(dst.codes[:, b:e]), scales=to_np(dst.scales[:, b:e]),
-                assign=to_np(dst.assign[:T, :, b:e]), centroids=to_np(dst.centroids[chunk, :T]))
+                assign=to_np(dst.assign[:T, :, b:e]), centroids=cent)
 
 
 def distance_table(Xop: np.ndarray, C: np.ndarray) -> np.ndarray:
