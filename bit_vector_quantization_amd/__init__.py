@@ -8,4 +8,4 @@ name; ``codec`` allocates device buffers with torch around it.
 """
 from . import _lib
 from ._lib import *  # noqa: F401,F403  (the C entry points, same names)
-from .codec import CentroidCache, CompressedKV, Encoder, config, decode  # noqa: F401
+from .codec import CentroidCache, CompressedKV, Encoder, attention, config, decode  # noqa: F401

@@ -74,6 +74,10 @@ _SIGNATURES = {
     "qvg_centroid_cache_import": (c_int32, [c_void_p, c_void_p, c_void_p]),
     "qvg_encode_chunk": (c_int32, [_CFG, c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p,
                                    _VIEW, c_int32, c_void_p, c_uint64, c_void_p]),
+    "qvg_attention_workspace_bytes": (c_int32, [_CFG, c_int32, c_int32, c_int64, POINTER(c_uint64)]),
+    "qvg_attention": (c_int32, [_CFG, _VIEW, c_int32, _VIEW, c_int32, c_int64, c_int64, c_void_p, c_void_p,
+                                c_int64, c_int32, c_int32, ctypes.c_float, c_void_p, c_int64, c_void_p, c_void_p,
+                                c_uint64, c_void_p]),
     "qvg_encode_rounds": (c_int32, [_CFG, c_int32, c_int32, c_void_p, c_uint64, c_void_p, c_void_p]),
     "qvg_encode_chunk_static": (c_int32, [_CFG, c_void_p, c_int64, c_int32, c_int32, c_void_p, c_void_p,
                                           _VIEW, c_int32, c_void_p]),
@@ -219,6 +223,22 @@ def qvg_encode_rounds(cfg: qvg_config, heads: int, n_tokens: int, workspace, wor
                       stream=None) -> None:
     _check(LIB.qvg_encode_rounds(ctypes.byref(cfg), heads, n_tokens, _ptr(workspace), workspace_bytes,
                                  _ptr(rounds_out), _stream(stream)), "qvg_encode_rounds")
+
+
+def qvg_attention_workspace_bytes(cfg: qvg_config, heads: int, n_queries: int, n_keys: int) -> int:
+    out = c_uint64()
+    _check(LIB.qvg_attention_workspace_bytes(ctypes.byref(cfg), heads, n_queries, n_keys, ctypes.byref(out)),
+           "qvg_attention_workspace_bytes")
+    return out.value
+
+
+def qvg_attention(cfg: qvg_config, k_src: qvg_cache_view, k_head0: int, v_src: qvg_cache_view, v_head0: int,
+                  tok_begin: int, tok_end: int, rope, q, q_head_stride: int, heads: int, n_queries: int,
+                  scale: float, out, out_head_stride: int, lse, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(LIB.qvg_attention(ctypes.byref(cfg), ctypes.byref(k_src), k_head0, ctypes.byref(v_src), v_head0,
+                             tok_begin, tok_end, _ptr(rope), _ptr(q), q_head_stride, heads, n_queries, scale,
+                             _ptr(out), out_head_stride, _ptr(lse), _ptr(workspace), workspace_bytes,
+                             _stream(stream)), "qvg_attention")
 
 
 QVG_STATIC_SCRATCH_BYTES = 64 << 20   # the fixed scratch array of qvg_encode_chunk_static

@@ -143,3 +143,24 @@ def decode(cfg: L.qvg_config, src: CompressedKV, tok_begin: int, tok_end: int,
         L.qvg_decode_rope(cfg, src.view, tok_begin, tok_end, rope, src.heads if rope_heads is None else rope_heads,
                           out, out.stride(0), odt, stream or torch.cuda.current_stream())
     return out
+
+
+def attention(cfg: L.qvg_config, k_src: CompressedKV, v_src: CompressedKV, q: torch.Tensor, tok_begin: int,
+              tok_end: int, k_head0: int = 0, v_head0: int = 0, rope: torch.Tensor | None = None,
+              scale: float | None = None, stream=None, want_lse: bool = False):
+    """softmax(scale q k^T) v over the compressed keys and values of tokens
+    [tok_begin, tok_end), rebuilt inside the kernel (q: bf16 [H][Nq][d] with
+    contiguous rows).  Returns fp32 [H][Nq][d] (and the lse [H][Nq])."""
+    H, Nq, d = q.shape
+    assert q.dtype == torch.bfloat16 and q.stride(2) == 1 and q.stride(1) == d
+    if rope is not None:
+        assert rope.dtype == torch.float32 and rope.is_contiguous()
+        assert tuple(rope.shape) == (tok_end - tok_begin, d // 2, 2)
+    out = torch.empty((H, Nq, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((H, Nq), dtype=torch.float32, device=q.device) if want_lse else None
+    ws_bytes = L.qvg_attention_workspace_bytes(cfg, H, Nq, tok_end - tok_begin)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    L.qvg_attention(cfg, k_src.view, k_head0, v_src.view, v_head0, tok_begin, tok_end, rope, q, q.stride(0), H,
+                    Nq, d ** -0.5 if scale is None else scale, out, out.stride(0), lse, ws, ws_bytes,
+                    stream or torch.cuda.current_stream())
+    return (out, lse) if want_lse else out

@@ -13,6 +13,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <vector>
@@ -579,6 +580,95 @@ qvg_status qvg_decode_rope(const qvg_config *cfg, const qvg_cache_view *src, int
                            int32_t out_dtype, void *stream) {
     if (!rope || !aligned16(rope) || !src || rope_heads < 0 || rope_heads > src->heads) return QVG_ERR_INVALID_ARG;
     return decode_impl(cfg, src, tok_begin, tok_end, rope, rope_heads, out, out_head_stride, out_dtype, stream);
+}
+
+// Splits of the key range of an attention call: enough workgroups to fill the
+// chip twice over, at least 4 tiles of 64 keys per split, at most 64 splits.
+static int attention_splits(int H, int Nq, int64_t Nk) {
+    const int64_t qblocks = (Nq + 255) / 256;
+    int64_t sp = (512 + qblocks * H - 1) / (qblocks * H);
+    sp = std::min<int64_t>(sp, std::max<int64_t>(1, Nk / 256));
+    return (int)std::max<int64_t>(1, std::min<int64_t>(sp, 64));
+}
+
+qvg_status qvg_attention_workspace_bytes(const qvg_config *cfg, int32_t heads, int32_t n_queries, int64_t n_keys,
+                                         uint64_t *bytes) {
+    qvg_status st = check_config(cfg);
+    if (st != QVG_OK) return st;
+    if (heads < 1 || n_queries < 1 || n_keys < 1 || !bytes) return QVG_ERR_INVALID_ARG;
+    const int sp = attention_splits(heads, n_queries, n_keys);
+    *bytes = round_up((size_t)sp * heads * n_queries * cfg->d * 4, 256) + (size_t)sp * heads * n_queries * 2 * 4;
+    return QVG_OK;
+}
+
+static bool view_ok(const qvg_cache_view *v, int64_t tok_end) {
+    return v && v->heads >= 1 && v->chunk_tokens >= 1 && tok_end <= v->cap_tokens && v->codes && v->scales &&
+           v->assign && v->centroids && aligned16(v->codes) && aligned16(v->centroids);
+}
+
+qvg_status qvg_attention(const qvg_config *cfg, const qvg_cache_view *k_src, int32_t k_head0,
+                         const qvg_cache_view *v_src, int32_t v_head0, int64_t tok_begin, int64_t tok_end,
+                         const float *rope, const void *q, int64_t q_head_stride, int32_t heads, int32_t n_queries,
+                         float scale, float *out, int64_t out_head_stride, float *lse, void *workspace,
+                         uint64_t workspace_bytes, void *stream) {
+    qvg_status st = check_config(cfg);
+    if (st != QVG_OK) return st;
+    if (cfg->d != 128 || cfg->dtype != QVG_BF16 || cfg->n_stages < 1 || cfg->n_stages > 4) return QVG_ERR_UNSUPPORTED;
+    if (heads < 1 || n_queries < 1 || tok_begin < 0 || tok_end <= tok_begin) return QVG_ERR_INVALID_ARG;
+    if (!view_ok(k_src, tok_end) || !view_ok(v_src, tok_end)) return QVG_ERR_INVALID_ARG;
+    if (k_head0 < 0 || v_head0 < 0 || k_head0 + heads > k_src->heads || v_head0 + heads > v_src->heads)
+        return QVG_ERR_INVALID_ARG;
+    if (!q || !aligned16(q) || q_head_stride < (int64_t)n_queries * cfg->d || (q_head_stride * 2) % 16 != 0)
+        return QVG_ERR_INVALID_ARG;
+    if (!out || out_head_stride < (int64_t)n_queries * cfg->d) return QVG_ERR_INVALID_ARG;
+    if (rope && !aligned16(rope)) return QVG_ERR_INVALID_ARG;
+    if (!(scale > 0.f) || !(scale < 1e30f)) return QVG_ERR_INVALID_ARG;
+    const int64_t nk = tok_end - tok_begin;
+    uint64_t need = 0;
+    st = qvg_attention_workspace_bytes(cfg, heads, n_queries, nk, &need);
+    if (st != QVG_OK) return st;
+    if (!workspace || !aligned16(workspace)) return QVG_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return QVG_ERR_WORKSPACE;
+    if ((int64_t)(n_queries + 255) / 256 >= 65536 || heads >= 65536) return QVG_ERR_UNSUPPORTED;
+    AttnArgs a{};
+    auto src_of = [&](const qvg_cache_view *v) {
+        AttnSrc r{};
+        r.codes = v->codes;
+        r.scales = v->scales;
+        r.assign = v->assign;
+        r.cent = v->centroids;
+        r.cap = v->cap_tokens;
+        r.chunk_tokens = v->chunk_tokens;
+        r.heads = v->heads;
+        r.K = cfg->n_centroids;
+        r.G = cfg->group_size;
+        return r;
+    };
+    a.k = src_of(k_src);
+    a.v = src_of(v_src);
+    a.khead0 = k_head0;
+    a.vhead0 = v_head0;
+    a.T = cfg->n_stages;
+    a.fp8 = cfg->centroid_format == QVG_CENT_E4M3;
+    a.splits = attention_splits(heads, n_queries, nk);
+    a.tok_begin = tok_begin;
+    a.tok_end = tok_end;
+    a.keys_per_split = (nk + a.splits - 1) / a.splits;
+    a.splits = (int)((nk + a.keys_per_split - 1) / a.keys_per_split);   // no empty split
+    a.rope = rope;
+    a.q = static_cast<const uint16_t *>(q);
+    a.q_hs = q_head_stride;
+    a.H = heads;
+    a.Nq = n_queries;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                          round_up((size_t)a.splits * heads * n_queries * cfg->d * 4, 256));
+    const double flops = 4.0 * heads * n_queries * nk * cfg->d;
+    const double bytes = (double)heads * nk * 2 * (cfg->d / 4 + cfg->d / cfg->group_size + cfg->n_stages) +
+                         (double)heads * n_queries * cfg->d * (2 + 4);
+    QVG_LAUNCH("attention", flops, bytes, launch_attention(a, out, out_head_stride, lse, static_cast<hipStream_t>(stream)));
+    return QVG_OK;
 }
 
 qvg_status qvg_kmeans_assign(const void *x, int32_t x_dtype, int64_t x_head_stride, const float *centroids,

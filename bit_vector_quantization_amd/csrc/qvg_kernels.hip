@@ -2401,6 +2401,257 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
+// attention over the compressed cache
+// ---------------------------------------------------------------------------
+//
+// softmax(scale Q K^T) V with K and V rebuilt inside the kernel, tile by tile,
+// from the compressed cache (codes, scales, assignments, centroid tables): no
+// decoded K or V ever goes to memory.  A workgroup of 16 waves takes 256
+// queries of one head (16 per wave, their bf16 rows held as MFMA operands) and
+// a range of keys (a split), 64 keys per tile:
+//   1. every thread rebuilds 8 channels of one key of K and of V with the
+//      decode's arithmetic (dequantise, add the stages' centroid rows in
+//      reverse order in fp32, rotate the key if a table is given, round to
+//      bf16), so the tiles equal qvg_decode's output bit for bit; K goes to
+//      LDS row by row, V transposed;
+//   2. S = Q K^T on v_mfma_f32_16x16x32_bf16 (lane l: key l % 16, queries
+//      4 (l / 16) .. + 3), online softmax in base 2 with the row statistics
+//      shared by the 16 lanes of a row group;
+//   3. P (bf16) through the wave's LDS rows, then O += P V on the same
+//      instruction, O[query 4 (l / 16) + r][channel 16 b + l % 16].
+// Each split writes its unnormalised O and (max, sum); k_attn_merge combines
+// the splits by their log-sum-exp.
+constexpr int ATT_WAVES = 16;
+constexpr int ATT_BQ = 16 * ATT_WAVES;   // queries per workgroup
+constexpr int ATT_BK = 64;               // keys per tile
+constexpr int ATT_D = 128;
+constexpr int ATT_KROW = ATT_D + 8;      // bf16 per K row in LDS (padded against bank conflicts)
+constexpr int ATT_VROW = ATT_BK + 8;     // bf16 per transposed V row
+constexpr int ATT_PROW = ATT_BK + 8;     // bf16 per P row
+constexpr size_t ATT_LDS = (size_t)2 * (ATT_BK * ATT_KROW + ATT_D * ATT_VROW + ATT_WAVES * 16 * ATT_PROW);
+
+// 8 channels [8 j, 8 j + 8) of key n of one head of a compressed tensor, in fp32:
+// dequantised, then the stages' centroid rows added from T - 1 down to 0.
+template <int TT, bool FP8>
+__device__ __forceinline__ void attn_row8(const AttnSrc &a, int head, int64_t n, int j, float *y) {
+    constexpr int D = ATT_D;
+    const size_t row = (size_t)head * a.cap + n;
+    const uint32_t w = reinterpret_cast<const uint16_t *>(a.codes)[row * (D / 8) + j];
+    const uint32_t sc = a.scales[row * (D / a.G) + (8 * j) / a.G];
+    dequant8(w, e4m3_decode(sc), y);
+    const int64_t c = n / a.chunk_tokens;
+#pragma unroll
+    for (int t = TT - 1; t >= 0; --t) {
+        int k = a.assign[((size_t)t * a.heads + head) * a.cap + n];
+        k = k < a.K ? k : a.K - 1;
+        uint4 cv;
+        if constexpr (FP8) {
+            const uint8_t *tbl = static_cast<const uint8_t *>(a.cent) + (((size_t)c * TT + t) * a.heads + head) *
+                                                                            (a.K * D + 16);
+            const float sf = ldexpf(1.f, *reinterpret_cast<const int32_t *>(tbl));
+            const uint2 v = *reinterpret_cast<const uint2 *>(tbl + 16 + (size_t)k * D + 8 * j);
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t ww = q < 2 ? v.x : v.y, sh = 16 * (q & 1);
+                o[q] = (__float_as_uint(e4m3_decode((ww >> sh) & 0xFFu) * sf) >> 16) |
+                       (__float_as_uint(e4m3_decode((ww >> (sh + 8)) & 0xFFu) * sf) & 0xFFFF0000u);
+            }
+            cv = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+            cv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.cent) +
+                                                  ((((size_t)c * TT + t) * a.heads + head) * a.K + k) * D + 8 * j);
+        }
+        add8<uint16_t>(&cv, y);
+    }
+}
+
+template <int TT, bool FP8>
+__global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
+    constexpr int D = ATT_D;
+    extern __shared__ uint16_t att_lds[];
+    uint16_t *lk = att_lds;                              // [ATT_BK][ATT_KROW]
+    uint16_t *lvt = lk + ATT_BK * ATT_KROW;              // [D][ATT_VROW]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint16_t *lp = lvt + D * ATT_VROW + wave * 16 * ATT_PROW;   // this wave's [16][ATT_PROW]
+    const int h = blockIdx.y, split = blockIdx.z;
+    const int64_t kb0 = a.tok_begin + (int64_t)split * a.keys_per_split;
+    const int64_t kb1 = min(a.tok_end, kb0 + a.keys_per_split);
+    const int g = lane >> 4, c16 = lane & 15;
+    const int q0 = blockIdx.x * ATT_BQ + wave * 16;
+    // this wave's queries as A operands: row c16, channels 32 s + 8 g .. + 7
+    bf16x8_t qa[D / 32];
+    {
+        const int qr = min(q0 + c16, a.Nq - 1);
+        const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (size_t)h * a.q_hs + (size_t)qr * D + 8 * g);
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) qa[s] = __builtin_bit_cast(bf16x8_t, qp[4 * s]);
+    }
+    f32x4_t o[D / 16];
+#pragma unroll
+    for (int b = 0; b < D / 16; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m[4], l[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        m[r] = -__builtin_inff();
+        l[r] = 0.f;
+    }
+    const int kk = tid >> 4, j = tid & 15;   // the key and 8-channel slice this thread rebuilds
+    for (int64_t t0 = kb0; t0 < kb1; t0 += ATT_BK) {
+        __syncthreads();   // the previous tile's readers are done
+        {
+            const int64_t n = t0 + kk;
+            float yk[8], yv[8];
+            if (n < kb1) {
+                attn_row8<TT, FP8>(a.k, a.khead0 + h, n, j, yk);
+                if (a.rope) {
+                    float cs[8];
+                    load8_f32(a.rope + (size_t)(n - a.tok_begin) * D + 8 * j, cs);
+                    rope8(cs, yk);
+                }
+                attn_row8<TT, FP8>(a.v, a.vhead0 + h, n, j, yv);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) yk[i] = yv[i] = 0.f;
+            }
+            *reinterpret_cast<uint4 *>(lk + kk * ATT_KROW + 8 * j) =
+                make_uint4(pack_bf16x2(yk[0], yk[1]), pack_bf16x2(yk[2], yk[3]), pack_bf16x2(yk[4], yk[5]),
+                           pack_bf16x2(yk[6], yk[7]));
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                const uint32_t pv = pack_bf16x2(yv[i], yv[i + 1]);
+                lvt[(8 * j + i) * ATT_VROW + kk] = (uint16_t)pv;
+                lvt[(8 * j + i + 1) * ATT_VROW + kk] = (uint16_t)(pv >> 16);
+            }
+        }
+        __syncthreads();
+        // S = Q K^T for 4 blocks of 16 keys
+        f32x4_t sacc[ATT_BK / 16];
+#pragma unroll
+        for (int kb = 0; kb < ATT_BK / 16; ++kb) {
+            sacc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const uint16_t *kr = lk + (16 * kb + c16) * ATT_KROW + 8 * g;
+#pragma unroll
+            for (int s = 0; s < D / 32; ++s)
+                sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    qa[s], __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(kr + 32 * s)), sacc[kb], 0, 0,
+                    0);
+        }
+        // online softmax, base 2, rows 4 g + r
+        float mx[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+#pragma unroll
+        for (int kb = 0; kb < ATT_BK / 16; ++kb) {
+            const bool valid = t0 + 16 * kb + c16 < kb1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = valid ? sacc[kb][r] * a.scale_log2 : -__builtin_inff();
+                sacc[kb][r] = v;
+                mx[r] = fmaxf(mx[r], v);
+            }
+        }
+        float corr[4], rs[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int o2 = 1; o2 < 16; o2 <<= 1) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], o2));
+            const float mn = fmaxf(m[r], mx[r]);
+            corr[r] = exp2f(m[r] - mn);
+            m[r] = mn;
+            rs[r] = 0.f;
+        }
+#pragma unroll
+        for (int kb = 0; kb < ATT_BK / 16; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pexp = exp2f(sacc[kb][r] - m[r]);
+                rs[r] += pexp;
+                lp[(4 * g + r) * ATT_PROW + 16 * kb + c16] = (uint16_t)f32_to_bf16(pexp);
+            }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+            for (int o2 = 1; o2 < 16; o2 <<= 1) rs[r] += __shfl_xor(rs[r], o2);
+            l[r] = l[r] * corr[r] + rs[r];
+        }
+#pragma unroll
+        for (int b = 0; b < D / 16; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[b][r] *= corr[r];
+        __builtin_amdgcn_wave_barrier();
+        // O += P V: P rows c16 from the wave's LDS rows, V^T rows from the tile
+#pragma unroll
+        for (int s = 0; s < ATT_BK / 32; ++s) {
+            const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(lp + c16 * ATT_PROW + 32 * s + 8 * g));
+#pragma unroll
+            for (int b = 0; b < D / 16; ++b) {
+                const bf16x8_t vb = __builtin_bit_cast(
+                    bf16x8_t, *reinterpret_cast<const uint4 *>(lvt + (16 * b + c16) * ATT_VROW + 32 * s + 8 * g));
+                o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[b], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    // this split's unnormalised output and row statistics
+    const size_t base = ((size_t)split * a.H + h) * a.Nq;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int qi = q0 + 4 * g + r;
+        if (qi >= a.Nq) continue;
+#pragma unroll
+        for (int b = 0; b < D / 16; ++b) a.part_o[(base + qi) * D + 16 * b + c16] = o[b][r];
+        if (c16 == 0) {
+            a.part_ml[(base + qi) * 2] = m[r];
+            a.part_ml[(base + qi) * 2 + 1] = l[r];
+        }
+    }
+}
+
+// Combines the splits of every (head, query): O = sum_s 2^(m_s - M) O_s /
+// sum_s 2^(m_s - M) l_s and lse = (M + log2 sum_s 2^(m_s - M) l_s) ln 2.
+__global__ __launch_bounds__(128) void k_attn_merge(const float *part_o, const float *part_ml, int splits, int H,
+                                                    int Nq, float *out, int64_t out_hs, float *lse) {
+    const int qi = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+    float M = -__builtin_inff();
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[(((size_t)s * H + h) * Nq + qi) * 2]);
+    float den = 0.f, num = 0.f;
+    for (int s = 0; s < splits; ++s) {
+        const size_t i = ((size_t)s * H + h) * Nq + qi;
+        const float w = exp2f(part_ml[i * 2] - M);
+        den += w * part_ml[i * 2 + 1];
+        num += w * part_o[i * ATT_D + d];
+    }
+    out[(size_t)h * out_hs + (size_t)qi * ATT_D + d] = num / den;
+    if (lse && d == 0) lse[(size_t)h * Nq + qi] = (M + log2f(den)) * 0.69314718055994530942f;
+}
+
+hipError_t launch_attention(const AttnArgs &a, float *out, int64_t out_hs, float *lse, hipStream_t s) {
+    const dim3 g((unsigned)((a.Nq + ATT_BQ - 1) / ATT_BQ), (unsigned)a.H, (unsigned)a.splits), b(64 * ATT_WAVES);
+#define QVG_ATT(TT, F8)                                                                                         \
+    do {                                                                                                        \
+        (void)hipFuncSetAttribute((const void *)k_attention<TT, F8>, hipFuncAttributeMaxDynamicSharedMemorySize, \
+                                  (int)ATT_LDS);                                                                \
+        QVG_KERNEL((k_attention<TT, F8>), g, b, ATT_LDS, s, a);                                                 \
+    } while (0)
+#define QVG_ATT_T(F8)                                                                                           \
+    do {                                                                                                        \
+        switch (a.T) {                                                                                          \
+            case 1: QVG_ATT(1, F8); break;                                                                      \
+            case 2: QVG_ATT(2, F8); break;                                                                      \
+            case 3: QVG_ATT(3, F8); break;                                                                      \
+            default: QVG_ATT(4, F8); break;                                                                     \
+        }                                                                                                       \
+    } while (0)
+    if (a.fp8) QVG_ATT_T(true); else QVG_ATT_T(false);
+#undef QVG_ATT_T
+#undef QVG_ATT
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    QVG_KERNEL(k_attn_merge, dim3((unsigned)a.Nq, (unsigned)a.H), dim3(ATT_D), 0, s, a.part_o, a.part_ml, a.splits,
+               a.H, a.Nq, out, out_hs, lse);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // fixed device scratch of the entry point that allocates nothing
 // ---------------------------------------------------------------------------
 

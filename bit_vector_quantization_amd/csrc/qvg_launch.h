@@ -148,6 +148,30 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 
+// Attention over the compressed cache (k_attention + k_attn_merge): one
+// compressed tensor as the kernel reads it (bf16 tables, or FP8 tables of
+// 16 + K D bytes), d = 128.
+struct AttnSrc {
+    const uint8_t *codes, *scales, *assign;
+    const void *cent;
+    int64_t cap;
+    int chunk_tokens, heads, K, G;
+};
+struct AttnArgs {
+    AttnSrc k, v;
+    int khead0, vhead0;   // attention head h reads K head khead0 + h and V head vhead0 + h
+    int T, fp8;
+    int64_t tok_begin, tok_end, keys_per_split;
+    const float *rope;    // [tok_end - tok_begin][D/2] (cos, sin) for the keys, or null
+    const uint16_t *q;    // bf16 [H][Nq][D], head stride q_hs
+    int64_t q_hs;
+    int H, Nq, splits;
+    float scale_log2;     // the score scale times log2(e)
+    float *part_o;        // [splits][H][Nq][D] fp32
+    float *part_ml;       // [splits][H][Nq][2] fp32
+};
+hipError_t launch_attention(const AttnArgs &a, float *out, int64_t out_hs, float *lse, hipStream_t s);
+
 // Events the next kernel launch records at its own start and end
 // (hipExtLaunchKernelGGL); the library's profiler sets them around one launcher
 // call, and the launch clears them.  Thread-local; null when profiling is off.

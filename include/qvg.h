@@ -269,6 +269,37 @@ qvg_status qvg_decode_rope(const qvg_config *cfg, const qvg_cache_view *src, int
                            int64_t tok_end, const float *rope, int32_t rope_heads, void *out,
                            int64_t out_head_stride, int32_t out_dtype, void *stream);
 
+/* Attention that reads the compressed cache directly (163.com article, section 5:
+ * the fused dequantisation kernel keeps the rebuilt keys and values out of
+ * memory; gist.science summaries, section 2C): for attention head h and query i,
+ *   O[h][i] = sum_j softmax_j(scale <q_i, k_j>) v_j,  lse[h][i] = ln sum_j exp(scale <q_i, k_j>),
+ * over the keys j in [tok_begin, tok_end), with k_j and v_j the rows qvg_decode
+ * (keys: qvg_decode_rope when `rope` is given) would write in bf16, rebuilt in
+ * the kernel tile by tile and never stored.  Scores and sums in fp32 on the
+ * matrix cores; the softmax weights enter the sum with V as bf16.
+ *   k_src, k_head0   keys: attention head h reads head k_head0 + h of k_src
+ *   v_src, v_head0   values: head v_head0 + h of v_src (one K-then-V cache of
+ *                    2H heads: the same view, k_head0 = 0, v_head0 = H)
+ *   rope             NULL, or fp32 [tok_end - tok_begin][d/2][2] (cos, sin) that
+ *                    rotates the keys as qvg_decode_rope does; 16-byte aligned
+ *   q                bf16 [heads][n_queries][d] (rotated by the caller), head
+ *                    stride q_head_stride elements, 16-byte aligned
+ *   scale            the score scale (> 0), e.g. 1 / sqrt(d)
+ *   out              fp32 [heads][n_queries][d], head stride out_head_stride
+ *   lse              NULL or fp32 [heads][n_queries]
+ *   workspace        device scratch of qvg_attention_workspace_bytes(cfg, heads,
+ *                    n_queries, tok_end - tok_begin) bytes (the key range is
+ *                    split over workgroups; the splits merge by their lse)
+ * Requires d = 128, a bf16 cache with 1-4 stages (QVG_ERR_UNSUPPORTED otherwise)
+ * and both views holding the tokens; other conventions as qvg_decode. */
+qvg_status qvg_attention_workspace_bytes(const qvg_config *cfg, int32_t heads, int32_t n_queries, int64_t n_keys,
+                                         uint64_t *bytes);
+qvg_status qvg_attention(const qvg_config *cfg, const qvg_cache_view *k_src, int32_t k_head0,
+                         const qvg_cache_view *v_src, int32_t v_head0, int64_t tok_begin, int64_t tok_end,
+                         const float *rope, const void *q, int64_t q_head_stride, int32_t heads, int32_t n_queries,
+                         float scale, float *out, int64_t out_head_stride, float *lse, void *workspace,
+                         uint64_t workspace_bytes, void *stream);
+
 /* ---- stage-level entry points (same conventions), for parity checks and profiling ---- */
 
 /* Workspace the stage-level k-means calls need for (heads, n_tokens, d, K). Host only. */

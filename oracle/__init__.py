@@ -14,4 +14,5 @@ from .rng import forgy_indices, forgy_key, shuffle_prefix, splitmix64_next
 from .qvg import (CodecConfig, Encoded, assign, update, lloyd, group_quant, pack2, unpack2,
                   dequant, encode_chunk, decode_chunk, decode, rope_rotate, rtn_reconstruct, mse,
                   kv_cache_bytes, chunk_bytes, compression_ratio, bits_per_value_ratio,
-                  E4M3_TABLE_HEADER, e4m3_table_exponent, store_e4m3)
+                  E4M3_TABLE_HEADER, e4m3_table_exponent, store_e4m3, attention,
+                  attention_tolerance)

@@ -392,6 +392,31 @@ def decode(enc: Encoded, G: int, out: str = "f32") -> np.ndarray:
     return decode_chunk(enc.codes, enc.scales, enc.assign, enc.centroids, G, out)
 
 
+def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """softmax(scale Q K^T) V per head, in float64, and the natural log of each
+    query's softmax denominator.  Q [H][Nq][d], K and V [H][Nk][d] -> (O
+    [H][Nq][d], lse [H][Nq]).  The scores are shifted by their row maximum
+    before exponentiation, which leaves the result unchanged."""
+    Q, K, V = (np.asarray(a, np.float64) for a in (Q, K, V))
+    S = scale * np.einsum("hqd,hkd->hqk", Q, K)
+    m = S.max(axis=2, keepdims=True)
+    E = np.exp(S - m)
+    den = E.sum(axis=2, keepdims=True)
+    return np.einsum("hqk,hkd->hqd", E / den, V), (m + np.log(den))[..., 0]
+
+
+def attention_tolerance(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Elementwise error allowed to an attention that rounds its softmax weights
+    to bf16 before the weighted sum of V (each weight within 2^-8 of itself
+    relative, the exponentials and fp32 sums within far less):
+    2^-7 sum_j p_j |v_j| + 2^-20 max|v| per output element."""
+    Q, K, V = (np.asarray(a, np.float64) for a in (Q, K, V))
+    S = scale * np.einsum("hqd,hkd->hqk", Q, K)
+    E = np.exp(S - S.max(axis=2, keepdims=True))
+    P = E / E.sum(axis=2, keepdims=True)
+    return 2.0 ** -7 * np.einsum("hqk,hkd->hqd", P, np.abs(V)) + 2.0 ** -20 * np.abs(V).max()
+
+
 def rtn_reconstruct(X: np.ndarray, G: int) -> np.ndarray:
     """Round-to-nearest baseline: the same quantiser applied to X directly."""
     X = np.asarray(X, dtype=F32)
