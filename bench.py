@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--share-reps", type=int, default=5,
                     help="timed steps of one GPU's share of the layer when its heads are split over 8 GPUs "
                          "(5 key + 5 value heads; 0 skips)")
+    ap.add_argument("--attn-reps", type=int, default=3,
+                    help="timed attention calls over the long-horizon cache (0 skips)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the per-stage error, convergence, FP8-table and latency reports")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -265,9 +267,9 @@ def main():
         aggressive = run_aggressive(q, synthkv, torch, dev, stream, args.aggressive_reps)
 
     # long-horizon decode stress: 12 heads x 128, 700 frames (1,092,000 tokens)
-    stress = None
+    stress = attention = None
     if args.stress_reps > 0:
-        stress = run_stress(q, synthkv, torch, dev, stream, args.stress_reps)
+        stress, attention = run_stress(q, synthkv, torch, dev, stream, args.stress_reps, args.attn_reps)
 
     extras = {}
     if not args.no_extras:
@@ -307,6 +309,7 @@ def main():
         "aggressive": aggressive,
         "head_share_of_8": share,
         "decode_stress": stress,
+        "attention": attention,
         **extras,
         "kernels": kernels,
         "profiled_ms_per_step": None if prof_ms_step is None else round(prof_ms_step, 4),
@@ -457,7 +460,7 @@ def run_aggressive(q, synthkv, torch, dev, stream, reps):
             "decode_us": round(seg[-1] * 1e3, 2), "reps": reps}
 
 
-def run_stress(q, synthkv, torch, dev, stream, reps):
+def run_stress(q, synthkv, torch, dev, stream, reps, attn_reps=0):
     p = synthkv.PRESETS[5]
     H, Ntot, d, K, T, G = p.heads, p.n_tokens, p.d, p.n_centroids, p.n_stages, p.group_size
     HK = 2 * H
@@ -493,10 +496,90 @@ def run_stress(q, synthkv, torch, dev, stream, reps):
     torch.cuda.synchronize()
     ms = sum(a.elapsed_time(b) for a, b in times) / reps
     gbs = total_b / (ms * 1e-3) / 1e9
-    return {"workload": "K and V as one 24-head tensor, 128 dims, 700 frames of 30x52 (1,092,000 tokens, "
-                        "234 chunks), 2 stages, 256 centroids, G=64; fused decode of the whole cache",
-            "kv_decode_ms": round(ms, 4), "algorithmic_bytes": int(total_b), "gbs": round(gbs, 1),
-            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "reps": reps, "setup_s": round(prep_s, 1)}
+    rec = {"workload": "K and V as one 24-head tensor, 128 dims, 700 frames of 30x52 (1,092,000 tokens, "
+                       "234 chunks), 2 stages, 256 centroids, G=64; fused decode of the whole cache",
+           "kv_decode_ms": round(ms, 4), "algorithmic_bytes": int(total_b), "gbs": round(gbs, 1),
+           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "reps": reps, "setup_s": round(prep_s, 1)}
+    attn = None
+    if attn_reps > 0:
+        attn = run_attention(q, torch, p, cfg, dst, out, stream, attn_reps)
+    return rec, attn
+
+
+def run_attention(q, torch, p, cfg, dst, out, stream, reps):
+    """Attention of one chunk's queries (4,680 per head, 12 heads) over the whole
+    long-horizon cache (1,092,000 keys), keys rotated by a rotary table, read
+    straight from the compressed cache (qvg_attention), next to the unfused
+    path: the rotated decode of K and decode of V to bf16, then PyTorch's
+    scaled_dot_product_attention."""
+    H, Ntot, d = p.heads, p.n_tokens, p.d
+    Nq = p.chunk_tokens
+    dev = out.device
+    log(f"attention: {H} heads, {Nq} queries over {Ntot} compressed keys")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    qd = (torch.randn((H, Nq, d), generator=g, device=dev) * 0.1).to(torch.bfloat16)
+    pos = torch.arange(Ntot, device=dev, dtype=torch.float32)[:, None]
+    inv = torch.pow(10000.0, -torch.arange(d // 2, device=dev, dtype=torch.float32) / (d // 2))[None, :]
+    ang = pos * inv
+    rope = torch.stack((torch.cos(ang), torch.sin(ang)), dim=-1).contiguous()
+    del pos, ang
+    flops = 4.0 * H * Nq * Ntot * d
+
+    def fused():
+        return q.attention(cfg, dst, dst, qd, 0, Ntot, k_head0=0, v_head0=H, rope=rope, stream=stream)
+
+    fused()
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        o_f = fused()
+        b.record(stream)
+        torch.cuda.synchronize()
+        t.append(a.elapsed_time(b))
+    ms = sorted(t)[len(t) // 2]
+    tf = flops / (ms * 1e-3) / 1e12
+    rec = {"workload": f"{H} heads, {Nq} queries (one chunk) over {Ntot} keys of the long-horizon cache, keys "
+                       "rotated by a rotary table, K/V rebuilt in the kernel from the compressed cache",
+           "fused_ms": round(ms, 3), "tflops": round(tf, 1), "reps": reps,
+           "roofline": dict(kernel="attention", bound="mfma", achieved=round(tf, 1), peak=MFMA_BF16_PEAK_TFLOPS,
+                            unit="TFLOP/s", frac=round(tf / MFMA_BF16_PEAK_TFLOPS, 4), traffic=None,
+                            avg_launch_ms=round(ms, 3), algorithmic_per_launch=flops,
+                            timed="HIP events around each call (attention + split merge), on its stream")}
+    # unfused: decode to bf16 (keys rotated), then scaled_dot_product_attention
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        import torch.nn.functional as F
+
+        def unfused():
+            q.decode(cfg, dst, 0, Ntot, out=out, stream=stream, rope=rope, rope_heads=H)
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+                return F.scaled_dot_product_attention(qd[None], out[None, :H], out[None, H:])
+
+        o_u = unfused()
+        torch.cuda.synchronize()
+        tu, td = [], []
+        for _ in range(reps):
+            a, m_, b = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            a.record(stream)
+            q.decode(cfg, dst, 0, Ntot, out=out, stream=stream, rope=rope, rope_heads=H)
+            m_.record(stream)
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+                o_u = F.scaled_dot_product_attention(qd[None], out[None, :H], out[None, H:])
+            b.record(stream)
+            torch.cuda.synchronize()
+            tu.append(a.elapsed_time(b))
+            td.append(a.elapsed_time(m_))
+        rec.update(unfused_ms=round(sorted(tu)[len(tu) // 2], 3), unfused_decode_ms=round(sorted(td)[len(td) // 2], 3),
+                   unfused_bf16_kv_bytes=int(2 * H * Ntot * d * 2),
+                   max_abs_diff_vs_unfused=float((o_f - o_u[0].float()).abs().max()))
+    except Exception as ex:   # no fused SDPA backend: report the fused path alone
+        rec.update(unfused_ms=None, unfused_error=str(ex)[:200])
+    del rope
+    return rec
 
 
 def run_stage_errors(q, synthkv, torch, dev, stream):

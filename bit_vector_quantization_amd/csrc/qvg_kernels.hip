@@ -2414,11 +2414,12 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
 //      reverse order in fp32, rotate the key if a table is given, round to
 //      bf16), so the tiles equal qvg_decode's output bit for bit; K goes to
 //      LDS row by row, V transposed;
-//   2. S = Q K^T on v_mfma_f32_16x16x32_bf16 (lane l: key l % 16, queries
-//      4 (l / 16) .. + 3), online softmax in base 2 with the row statistics
-//      shared by the 16 lanes of a row group;
-//   3. P (bf16) through the wave's LDS rows, then O += P V on the same
-//      instruction, O[query 4 (l / 16) + r][channel 16 b + l % 16].
+//   2. S^T = K Q^T on v_mfma_f32_16x16x32_bf16: lane l holds the scores of
+//      query l % 16 against keys 16 b + 4 (l / 16) + r, so every lane owns one
+//      query's softmax statistics (online, base 2, merged over 4 lanes);
+//   3. O^T += V^T P^T on the same instruction with the softmax weights (bf16)
+//      taken from the lane's own registers: the instruction's k order is
+//      permuted to the keys the lane holds, and V^T is read in that order.
 // Each split writes its unnormalised O and (max, sum); k_attn_merge combines
 // the splits by their log-sum-exp.
 constexpr int ATT_WAVES = 16;
@@ -2427,8 +2428,7 @@ constexpr int ATT_BK = 64;               // keys per tile
 constexpr int ATT_D = 128;
 constexpr int ATT_KROW = ATT_D + 8;      // bf16 per K row in LDS (padded against bank conflicts)
 constexpr int ATT_VROW = ATT_BK + 8;     // bf16 per transposed V row
-constexpr int ATT_PROW = ATT_BK + 8;     // bf16 per P row
-constexpr size_t ATT_LDS = (size_t)2 * (ATT_BK * ATT_KROW + ATT_D * ATT_VROW + ATT_WAVES * 16 * ATT_PROW);
+constexpr size_t ATT_LDS = (size_t)2 * (ATT_BK * ATT_KROW + ATT_D * ATT_VROW);
 
 // 8 channels [8 j, 8 j + 8) of key n of one head of a compressed tensor, in fp32:
 // dequantised, then the stages' centroid rows added from T - 1 down to 0.
@@ -2473,30 +2473,25 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
     uint16_t *lk = att_lds;                              // [ATT_BK][ATT_KROW]
     uint16_t *lvt = lk + ATT_BK * ATT_KROW;              // [D][ATT_VROW]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    uint16_t *lp = lvt + D * ATT_VROW + wave * 16 * ATT_PROW;   // this wave's [16][ATT_PROW]
     const int h = blockIdx.y, split = blockIdx.z;
     const int64_t kb0 = a.tok_begin + (int64_t)split * a.keys_per_split;
     const int64_t kb1 = min(a.tok_end, kb0 + a.keys_per_split);
     const int g = lane >> 4, c16 = lane & 15;
     const int q0 = blockIdx.x * ATT_BQ + wave * 16;
-    // this wave's queries as A operands: row c16, channels 32 s + 8 g .. + 7
-    bf16x8_t qa[D / 32];
+    // this wave's queries as B operands of S^T = K Q^T: column c16, channels 32 s + 8 g .. + 7
+    bf16x8_t qb[D / 32];
     {
         const int qr = min(q0 + c16, a.Nq - 1);
         const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (size_t)h * a.q_hs + (size_t)qr * D + 8 * g);
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) qa[s] = __builtin_bit_cast(bf16x8_t, qp[4 * s]);
+        for (int s = 0; s < D / 32; ++s) qb[s] = __builtin_bit_cast(bf16x8_t, qp[4 * s]);
     }
+    // O^T = V^T P^T: lane holds channels 16 b + 4 g + r of query c16
     f32x4_t o[D / 16];
 #pragma unroll
     for (int b = 0; b < D / 16; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m[4], l[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        m[r] = -__builtin_inff();
-        l[r] = 0.f;
-    }
-    const int kk = tid >> 4, j = tid & 15;   // the key and 8-channel slice this thread rebuilds
+    float m = -__builtin_inff(), l = 0.f;   // the lane's query: running maximum (base 2) and sum
+    const int kk = tid >> 4, j = tid & 15;  // the key and 8-channel slice this thread rebuilds
     for (int64_t t0 = kb0; t0 < kb1; t0 += ATT_BK) {
         __syncthreads();   // the previous tile's readers are done
         {
@@ -2525,7 +2520,8 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
             }
         }
         __syncthreads();
-        // S = Q K^T for 4 blocks of 16 keys
+        // S^T = K Q^T for 4 blocks of 16 keys: sacc[kb][r] = score of key
+        // 16 kb + 4 g + r for the lane's query c16
         f32x4_t sacc[ATT_BK / 16];
 #pragma unroll
         for (int kb = 0; kb < ATT_BK / 16; ++kb) {
@@ -2534,74 +2530,72 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
 #pragma unroll
             for (int s = 0; s < D / 32; ++s)
                 sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    qa[s], __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(kr + 32 * s)), sacc[kb], 0, 0,
-                    0);
+                    __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(kr + 32 * s)), qb[s], sacc[kb], 0,
+                    0, 0);
         }
-        // online softmax, base 2, rows 4 g + r
-        float mx[4] = {-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-#pragma unroll
-        for (int kb = 0; kb < ATT_BK / 16; ++kb) {
-            const bool valid = t0 + 16 * kb + c16 < kb1;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float v = valid ? sacc[kb][r] * a.scale_log2 : -__builtin_inff();
-                sacc[kb][r] = v;
-                mx[r] = fmaxf(mx[r], v);
-            }
-        }
-        float corr[4], rs[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-#pragma unroll
-            for (int o2 = 1; o2 < 16; o2 <<= 1) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], o2));
-            const float mn = fmaxf(m[r], mx[r]);
-            corr[r] = exp2f(m[r] - mn);
-            m[r] = mn;
-            rs[r] = 0.f;
-        }
+        // online softmax in base 2 for the lane's query; its 64 scores sit in
+        // the 4 lanes c16, c16 + 16, c16 + 32, c16 + 48
+        float mx = -__builtin_inff();
 #pragma unroll
         for (int kb = 0; kb < ATT_BK / 16; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float pexp = exp2f(sacc[kb][r] - m[r]);
-                rs[r] += pexp;
-                lp[(4 * g + r) * ATT_PROW + 16 * kb + c16] = (uint16_t)f32_to_bf16(pexp);
+                const bool valid = t0 + 16 * kb + 4 * g + r < kb1;
+                const float v = valid ? sacc[kb][r] * a.scale_log2 : -__builtin_inff();
+                sacc[kb][r] = v;
+                mx = fmaxf(mx, v);
             }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx);
+        const float corr = __builtin_amdgcn_exp2f(m - mn);
+        m = mn;
+        float rs = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int kb = 0; kb < ATT_BK / 16; ++kb)
 #pragma unroll
-            for (int o2 = 1; o2 < 16; o2 <<= 1) rs[r] += __shfl_xor(rs[r], o2);
-            l[r] = l[r] * corr[r] + rs[r];
-        }
+            for (int r = 0; r < 4; ++r) {
+                const float pe = __builtin_amdgcn_exp2f(sacc[kb][r] - mn);
+                sacc[kb][r] = pe;
+                rs += pe;
+            }
+        rs += __shfl_xor(rs, 16);
+        rs += __shfl_xor(rs, 32);
+        l = l * corr + rs;
 #pragma unroll
         for (int b = 0; b < D / 16; ++b)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[b][r] *= corr[r];
-        __builtin_amdgcn_wave_barrier();
-        // O += P V: P rows c16 from the wave's LDS rows, V^T rows from the tile
+            for (int r = 0; r < 4; ++r) o[b][r] *= corr;
+        // O^T += V^T P^T over 32-key steps.  The step's k index 8 g + i stands
+        // for key 4 g + i (i < 4) or 16 + 4 g + i - 4 (i >= 4) of the step, the
+        // keys this lane holds P of, so P^T comes straight from registers; V^T
+        // reads the same keys from the transposed tile.
 #pragma unroll
         for (int s = 0; s < ATT_BK / 32; ++s) {
-            const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4 *>(lp + c16 * ATT_PROW + 32 * s + 8 * g));
+            const uint4 pw = make_uint4(pack_bf16x2(sacc[2 * s][0], sacc[2 * s][1]),
+                                        pack_bf16x2(sacc[2 * s][2], sacc[2 * s][3]),
+                                        pack_bf16x2(sacc[2 * s + 1][0], sacc[2 * s + 1][1]),
+                                        pack_bf16x2(sacc[2 * s + 1][2], sacc[2 * s + 1][3]));
+            const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
             for (int b = 0; b < D / 16; ++b) {
-                const bf16x8_t vb = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const uint4 *>(lvt + (16 * b + c16) * ATT_VROW + 32 * s + 8 * g));
-                o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[b], 0, 0, 0);
+                const uint16_t *vr = lvt + (16 * b + c16) * ATT_VROW + 32 * s + 4 * g;
+                const uint2 lo = *reinterpret_cast<const uint2 *>(vr), hi = *reinterpret_cast<const uint2 *>(vr + 16);
+                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[b], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_wave_barrier();
     }
     // this split's unnormalised output and row statistics
-    const size_t base = ((size_t)split * a.H + h) * a.Nq;
+    const int qi = q0 + c16;
+    if (qi < a.Nq) {
+        const size_t base = ((size_t)split * a.H + h) * a.Nq + qi;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int qi = q0 + 4 * g + r;
-        if (qi >= a.Nq) continue;
-#pragma unroll
-        for (int b = 0; b < D / 16; ++b) a.part_o[(base + qi) * D + 16 * b + c16] = o[b][r];
-        if (c16 == 0) {
-            a.part_ml[(base + qi) * 2] = m[r];
-            a.part_ml[(base + qi) * 2 + 1] = l[r];
+        for (int b = 0; b < D / 16; ++b)
+            *reinterpret_cast<float4 *>(a.part_o + base * D + 16 * b + 4 * g) = make_float4(o[b][0], o[b][1], o[b][2], o[b][3]);
+        if (g == 0) {
+            a.part_ml[base * 2] = m;
+            a.part_ml[base * 2 + 1] = l;
         }
     }
 }
