@@ -30,6 +30,9 @@ QVG_BF16 = 1
 QVG_CENT_NATIVE = 0
 QVG_CENT_E4M3 = 1
 
+QVG_SCALE_E4M3 = 0
+QVG_SCALE_TWO_LEVEL = 1
+
 
 class QvgError(RuntimeError):
     def __init__(self, status: int, what: str):
@@ -41,13 +44,13 @@ class qvg_config(ctypes.Structure):
     _fields_ = [("d", c_int32), ("n_centroids", c_int32), ("n_stages", c_int32),
                 ("group_size", c_int32), ("iters_cold", c_int32), ("iters_warm", c_int32),
                 ("seed", c_uint64), ("dtype", c_int32), ("converge", c_int32),
-                ("centroid_format", c_int32), ("reserved", c_int32)]
+                ("centroid_format", c_int32), ("scale_mode", c_int32)]
 
 
 class qvg_cache_view(ctypes.Structure):
     _fields_ = [("codes", c_void_p), ("scales", c_void_p), ("assign", c_void_p),
                 ("centroids", c_void_p), ("cap_tokens", c_int64), ("chunk_tokens", c_int32),
-                ("heads", c_int32)]
+                ("heads", c_int32), ("scale_exp", c_void_p)]
 
 
 class qvg_kernel_stat(ctypes.Structure):
@@ -142,9 +145,9 @@ def _stream(s) -> int | None:
 
 def make_config(d: int, n_centroids: int, n_stages: int, group_size: int, iters_cold: int,
                 iters_warm: int, seed: int, dtype: int, converge: int = 0,
-                centroid_format: int = QVG_CENT_NATIVE) -> qvg_config:
+                centroid_format: int = QVG_CENT_NATIVE, scale_mode: int = QVG_SCALE_E4M3) -> qvg_config:
     return qvg_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dtype, converge,
-                      centroid_format, 0)
+                      centroid_format, scale_mode)
 
 
 # ---- entry points (same names as the C ABI) --------------------------------

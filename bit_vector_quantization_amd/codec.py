@@ -9,10 +9,11 @@ from . import _lib as L
 
 def config(d: int, n_centroids: int, n_stages: int, group_size: int, iters_cold: int,
            iters_warm: int, seed: int, dtype: str, converge: int = 0,
-           centroid_format: str = "native") -> L.qvg_config:
+           centroid_format: str = "native", scale_mode: str = "e4m3") -> L.qvg_config:
     dt = {"bf16": L.QVG_BF16, "f32": L.QVG_F32}[dtype]
     cf = {"native": L.QVG_CENT_NATIVE, "e4m3": L.QVG_CENT_E4M3}[centroid_format]
-    return L.make_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dt, converge, cf)
+    sm = {"e4m3": L.QVG_SCALE_E4M3, "two_level": L.QVG_SCALE_TWO_LEVEL}[scale_mode]
+    return L.make_config(d, n_centroids, n_stages, group_size, iters_cold, iters_warm, seed, dt, converge, cf, sm)
 
 
 def _dtype_of(cfg: L.qvg_config) -> torch.dtype:
@@ -55,9 +56,13 @@ class CompressedKV:
         assert self.codes.numel() == nb[0] and self.scales.numel() == nb[1]
         assert T == 0 or (self.assign.numel() == nb[2]
                           and self.centroids.numel() * self.centroids.element_size() == nb[3])
+        # second-level scale exponents, [n_chunks][H] (two-level scales only)
+        self.scale_exp = (torch.zeros((self.n_chunks, heads), dtype=torch.int8, device=device)
+                          if cfg.scale_mode == L.QVG_SCALE_TWO_LEVEL else None)
         self.view = L.qvg_cache_view(self.codes.data_ptr(), self.scales.data_ptr(),
                                      self.assign.data_ptr(), self.centroids.data_ptr(),
-                                     cap_tokens, chunk_tokens, heads)
+                                     cap_tokens, chunk_tokens, heads,
+                                     None if self.scale_exp is None else self.scale_exp.data_ptr())
 
     def bytes(self) -> int:
         return sum(L.qvg_cache_view_bytes(self.cfg, self.heads, self.cap, self.chunk_tokens))

@@ -49,7 +49,8 @@ size_t table_bytes(const qvg_config &c) {
 
 qvg_status check_config(const qvg_config *c) {
     if (!c) return QVG_ERR_INVALID_ARG;
-    if (c->converge < 0 || c->reserved != 0) return QVG_ERR_INVALID_ARG;
+    if (c->converge < 0) return QVG_ERR_INVALID_ARG;
+    if (c->scale_mode != QVG_SCALE_E4M3 && c->scale_mode != QVG_SCALE_TWO_LEVEL) return QVG_ERR_INVALID_ARG;
     if (c->centroid_format != QVG_CENT_NATIVE && c->centroid_format != QVG_CENT_E4M3) return QVG_ERR_INVALID_ARG;
     if (c->d <= 0 || c->group_size <= 0) return QVG_ERR_INVALID_ARG;
     if (c->n_centroids < 1 || c->n_centroids > QVG_MAX_CENTROIDS) return QVG_ERR_INVALID_ARG;
@@ -142,14 +143,18 @@ size_t conv_words(int H, int T) { return (size_t)3 * H + 1 + (size_t)T * H; }
 // and the earlier stages' stored centroids and assignments.
 struct EncodeWorkspace {
     size_t C = 0, Cb = 0, cnt = 0, fill = 0, offsets = 0, order = 0, idx = 0, vstats = 0, tstats = 0, r1 = 0,
-           conv = 0, mirror = 0, total = 0;
+           conv = 0, mirror = 0, qmax = 0, total = 0;
 
     EncodeWorkspace(const qvg_config &c, int H, int N) {
         const size_t D = c.d, K = c.n_centroids, Kp = padded_k(c.n_centroids);
         const int T = c.n_stages;
-        if (T == 0) { total = 256; return; }
         size_t off = 0;
         auto take = [&](size_t bytes) { size_t o = off; off += round_up(bytes, 256); return o; };
+        qmax = take((size_t)H * 4);   // the quantiser's per-head maxima (two-level scales)
+        if (T == 0) {
+            total = off;
+            return;
+        }
         C = take((size_t)H * K * D * 4);
         Cb = take((size_t)H * Kp * D * 2);
         cnt = take((size_t)2 * H * Kp * 4);
@@ -339,6 +344,8 @@ static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_he
     const int64_t tok0 = (int64_t)chunk_index * dst->chunk_tokens;
     if (tok0 + N > dst->cap_tokens) return QVG_ERR_INVALID_ARG;
     if (!dst->codes || !dst->scales || !aligned16(dst->codes)) return QVG_ERR_INVALID_ARG;
+    const bool two = cfg->scale_mode == QVG_SCALE_TWO_LEVEL;
+    if (two && !dst->scale_exp) return QVG_ERR_INVALID_ARG;
     if (T > 0 && (!dst->assign || !dst->centroids || !aligned16(dst->centroids))) return QVG_ERR_INVALID_ARG;
     if (init_centroids && !aligned16(init_centroids)) return QVG_ERR_INVALID_ARG;
     if (cache && (cache->heads != H || cache->d != D || cache->n_centroids != K || cache->n_stages != T))
@@ -352,10 +359,24 @@ static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_he
     const double HND = (double)H * N * D;
 
     const Src src0 = plain_src(x, x_head_stride);
+    // two-level scales: a first quantiser launch gathers each head's max|r|
+    uint32_t *qmax = at<uint32_t>(workspace, ws.qmax);
+    int8_t *sexp = two ? dst->scale_exp + (size_t)chunk_index * H : nullptr;
+    auto quant = [&](const Src &qs, const void *cent, int cent_rows, const uint8_t *pi, double flops,
+                     double bytes) -> qvg_status {
+        if (two) {
+            QVG_LAUNCH("zero", 0, H * 4.0, launch_zero(reinterpret_cast<int32_t *>(qmax), H, s));
+            QVG_LAUNCH("quant_max", 0, bytes, launch_quant(D, cfg->dtype, H, N, qs, cent, cent_rows, pi, cap,
+                                                           nullptr, nullptr, cap, G, qmax, nullptr, nullptr, s));
+        }
+        QVG_LAUNCH(T == 0 ? "group_quant" : "residual_quant", flops, bytes,
+                   launch_quant(D, cfg->dtype, H, N, qs, cent, cent_rows, pi, cap, dst->codes + tok0 * (D / 4),
+                                dst->scales + tok0 * (D / G), cap, G, nullptr, two ? qmax : nullptr, sexp, s));
+        return QVG_OK;
+    };
     if (T == 0) {
-        QVG_LAUNCH("group_quant", 0, HND * esz + HND / 4 + HND / G,
-                   launch_quant(D, cfg->dtype, H, N, src0, nullptr, 0, nullptr, 0, dst->codes + tok0 * (D / 4),
-                                dst->scales + tok0 * (D / G), cap, G, s));
+        st = quant(src0, nullptr, 0, nullptr, 0, HND * esz + HND / 4 + HND / G);
+        if (st != QVG_OK) return st;
         if (cache) cache->valid = 1;
         return QVG_OK;
     }
@@ -475,9 +496,9 @@ static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_he
             // tensors (identical values), the fp32 table otherwise
             const void *cent = fp8 ? mslot : cfg->dtype == QVG_BF16 ? (const void *)Cb : (const void *)C;
             const int cent_rows = !fp8 && cfg->dtype == QVG_BF16 ? Kp : K;
-            QVG_LAUNCH("residual_quant", HND * T, row_bytes + H * N + (double)H * K * D * esz + HND / 4 + HND / G,
-                       launch_quant(D, cfg->dtype, H, N, src, cent, cent_rows, pi, cap, dst->codes + tok0 * (D / 4),
-                                    dst->scales + tok0 * (D / G), cap, G, s));
+            st = quant(src, cent, cent_rows, pi, HND * T,
+                       row_bytes + H * N + (double)H * K * D * esz + HND / 4 + HND / G);
+            if (st != QVG_OK) return st;
         }
     }
     if (cache) cache->valid = 1;
@@ -555,6 +576,10 @@ static qvg_status decode_impl(const qvg_config *cfg, const qvg_cache_view *src, 
     a.out_hs = out_head_stride;
     a.rope = rope;
     a.rope_heads = rope ? rope_heads : 0;
+    if (cfg->scale_mode == QVG_SCALE_TWO_LEVEL) {
+        if (!src->scale_exp) return QVG_ERR_INVALID_ARG;
+        a.scale_exp = src->scale_exp;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int64_t chunks = (tok_end - 1) / a.chunk_tokens - tok_begin / a.chunk_tokens + 1;
     double bytes = (double)a.H * ntok * (a.D / 4 + a.D / a.G + a.T + a.D * dtype_size(out_dtype)) +
@@ -642,8 +667,10 @@ qvg_status qvg_attention(const qvg_config *cfg, const qvg_cache_view *k_src, int
         r.heads = v->heads;
         r.K = cfg->n_centroids;
         r.G = cfg->group_size;
+        r.scale_exp = cfg->scale_mode == QVG_SCALE_TWO_LEVEL ? v->scale_exp : nullptr;
         return r;
     };
+    if (cfg->scale_mode == QVG_SCALE_TWO_LEVEL && (!k_src->scale_exp || !v_src->scale_exp)) return QVG_ERR_INVALID_ARG;
     a.k = src_of(k_src);
     a.v = src_of(v_src);
     a.khead0 = k_head0;
@@ -761,7 +788,7 @@ qvg_status qvg_group_quant(const float *r, int64_t r_head_stride, int32_t heads,
     const double HND = (double)heads * n_tokens * d;
     QVG_LAUNCH("group_quant", 0, HND * 4 + HND / 4 + HND / group_size,
                launch_quant(d, QVG_F32, heads, n_tokens, plain_src(r, r_head_stride), nullptr, 0, nullptr, 0, codes,
-                            scales, n_tokens, group_size, s));
+                            scales, n_tokens, group_size, nullptr, nullptr, nullptr, s));
     return QVG_OK;
 }
 
@@ -811,6 +838,7 @@ qvg_status qvg_dequant_reconstruct(const qvg_config *cfg, int32_t heads, int32_t
     qvg_status st = check_config(cfg);
     if (st != QVG_OK) return st;
     if (heads < 1 || n_tokens < 1) return QVG_ERR_INVALID_ARG;
+    if (cfg->scale_mode != QVG_SCALE_E4M3) return QVG_ERR_UNSUPPORTED;
     qvg_cache_view v;
     v.codes = const_cast<uint8_t *>(codes);
     v.scales = const_cast<uint8_t *>(scales);
@@ -819,6 +847,7 @@ qvg_status qvg_dequant_reconstruct(const qvg_config *cfg, int32_t heads, int32_t
     v.cap_tokens = n_tokens;
     v.chunk_tokens = n_tokens;
     v.heads = heads;
+    v.scale_exp = nullptr;
     return qvg_decode(cfg, &v, 0, n_tokens, out, (int64_t)n_tokens * cfg->d, out_dtype, stream);
 }
 

@@ -1829,9 +1829,15 @@ hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype
 // group are adjacent lanes and combine their maxima with lane shuffles.
 
 // PM: the number of earlier stages when it is 0 or 1, else 2 (any number).
+// Two-level scales take two launches: with amax_out the kernel only folds the
+// head's largest |r| (fp32 bits) into amax_out[h]; with amax_in it quantises
+// with the second-level exponent f, the smallest f >= 0 with
+// fp32(max|r| / 1.5) <= 448 * 2^f (scale code = E4M3 of fp32(a / 1.5) / 2^f,
+// worth its value times 2^f), and writes f to exp_out[h].
 template <int D, typename KVT, bool CENT, int PM>
 __global__ __launch_bounds__(256) void k_quant(Src src, int N, const KVT *cent, int cent_rows, const uint8_t *pi,
-                                               int64_t pi_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap, int G) {
+                                               int64_t pi_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap, int G,
+                                               uint32_t *amax_out, const uint32_t *amax_in, int8_t *exp_out) {
     constexpr int SL = D / 16;
     constexpr int TPB = 256 / SL;
     const int h = blockIdx.y;
@@ -1873,10 +1879,20 @@ __global__ __launch_bounds__(256) void k_quant(Src src, int N, const KVT *cent, 
     float a = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(r[i]));
+    if (amax_out) {   // first launch of a two-level quantisation
+        atomicMax(&amax_out[h], __float_as_uint(a));
+        return;
+    }
     const int lanes = G >> 4;
     for (int o = 1; o < lanes; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
-    const uint32_t sc = e4m3_encode_nonneg(a / 1.5f);
-    const float s = e4m3_decode(sc);
+    int f = 0;
+    if (amax_in) {
+        const float a15 = __uint_as_float(amax_in[h]) / 1.5f;
+        while (a15 > ldexpf(448.f, f)) ++f;
+        if (n == 0 && j == 0) exp_out[h] = (int8_t)f;
+    }
+    const uint32_t sc = e4m3_encode_nonneg(ldexpf(a / 1.5f, -f));
+    const float s = ldexpf(e4m3_decode(sc), f);
     uint32_t w = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -1890,12 +1906,12 @@ __global__ __launch_bounds__(256) void k_quant(Src src, int N, const KVT *cent, 
 
 hipError_t launch_quant(int D, int dtype, int H, int N, const Src &src, const void *cent, int cent_rows,
                         const uint8_t *pi, int64_t pi_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap, int G,
-                        hipStream_t s) {
+                        uint32_t *amax_out, const uint32_t *amax_in, int8_t *exp_out, hipStream_t s) {
     const int TPB = 256 / (D / 16);
     dim3 g((N + TPB - 1) / TPB, H), b(256);
 #define QVG_QUANT_LAUNCH(CE, PMV)                                                                            \
     QVG_KERNEL((k_quant<DD, KVT, CE, PMV>), g, b, 0, s, src, N, (const KVT *)cent, cent_rows, pi, pi_hs, codes, \
-               scales, q_cap, G)
+               scales, q_cap, G, amax_out, amax_in, exp_out)
     QVG_DISPATCH_DT(D, dtype, {
         if (cent) {
             if (src.P == 0) QVG_QUANT_LAUNCH(true, 0);
@@ -2015,11 +2031,11 @@ __device__ __forceinline__ void slice_inputs(const uint8_t *codes, const uint8_t
 // for t = T-1 .. 0, rotate by the token's cos/sin row rp when it is not null,
 // and store the two half rows of rb.
 template <int D, typename CentT, typename OutT, typename Fetch>
-__device__ __forceinline__ void decode_slice(int T, uint32_t w0, uint32_t w1, uint32_t sc0, uint32_t sc1, int j,
-                                             const float *rp, OutT *rb, Fetch fetch) {
+__device__ __forceinline__ void decode_slice(int T, uint32_t w0, uint32_t w1, uint32_t sc0, uint32_t sc1, float sx,
+                                             int j, const float *rp, OutT *rb, Fetch fetch) {
     float y[16];
-    dequant8(w0, e4m3_decode(sc0), y);
-    dequant8(w1, e4m3_decode(sc1), y + 8);
+    dequant8(w0, e4m3_decode(sc0) * sx, y);
+    dequant8(w1, e4m3_decode(sc1) * sx, y + 8);
     for (int t = T - 1; t >= 0; --t) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -2050,8 +2066,8 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ code
                                                 const uint8_t *__restrict__ assign, const void *__restrict__ cent_v,
                                                 int64_t cap, int chunk_tokens, int H, int K, int T_rt, int G,
                                                 int64_t tok_begin, int64_t ntok, const float *__restrict__ rope,
-                                                int rope_heads, OutT *__restrict__ out, int64_t out_hs,
-                                                uint32_t blocks_per_head) {
+                                                int rope_heads, const int8_t *__restrict__ scale_exp,
+                                                OutT *__restrict__ out, int64_t out_hs, uint32_t blocks_per_head) {
     constexpr int SL = D / 16;
     constexpr int TPB = 256 / SL;
     constexpr int TS = TT > 0 ? TT : 1;
@@ -2084,7 +2100,8 @@ __global__ __launch_bounds__(256) void k_decode(const uint8_t *__restrict__ code
         const int64_t c = n[u] / chunk_tokens;
         OutT *rb = out + (size_t)h * out_hs + (size_t)(n[u] - tok_begin) * D;
         const float *rp = rope && h < rope_heads ? rope + (size_t)(n[u] - tok_begin) * D : nullptr;
-        decode_slice<D, CentT, OutT>(T, w0[u], w1[u], sc0[u], sc1[u], j, rp, rb, [&](int t, int hf, uint4 *cv) {
+        const float sx = scale_exp ? ldexpf(1.f, scale_exp[c * H + h]) : 1.f;
+        decode_slice<D, CentT, OutT>(T, w0[u], w1[u], sc0[u], sc1[u], sx, j, rp, rb, [&](int t, int hf, uint4 *cv) {
             int kk;
             if constexpr (TT > 0) {
                 kk = k[u][t];
@@ -2153,6 +2170,7 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, 8) void k_decode_lds(const uint8_t
                                                                    int64_t tok_begin, int64_t tok_end,
                                                                    int64_t c_first, int64_t n_units,
                                                                    const float *__restrict__ rope, int rope_heads,
+                                                                   const int8_t *__restrict__ scale_exp,
                                                                    OutT *__restrict__ out, int64_t out_hs) {
     constexpr int PARTS = DEC_PARTS;
     constexpr int DP = D / PARTS;                             // channels of a part
@@ -2211,6 +2229,8 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, 8) void k_decode_lds(const uint8_t
     const int64_t tb = max(tok_begin, c * chunk_tokens), te = min(tok_end, (c + 1) * chunk_tokens);
     const size_t hrow = (size_t)h * cap;
     const size_t a_stage = (size_t)H * cap;
+    // second level of two-level scales: 2^f for this (chunk, head), else 1
+    const float sx = scale_exp ? ldexpf(1.f, scale_exp[c * H + h]) : 1.f;
     const int jj = tid % LPT, slot = tid / LPT;
     const int c0 = hf * DP + 8 * jj;   // first channel of the lane
     const int sofs = DP >= G ? (8 * jj) / G : 0;   // the lane's scale byte among its token's SPT
@@ -2263,7 +2283,7 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, 8) void k_decode_lds(const uint8_t
             if (i >= nt) break;
             const uint32_t w = reinterpret_cast<const uint16_t *>(mcodes)[i * (CB / 2) + jj];
             float y[8];
-            dequant8(w, e4m3_decode(msc[i * SPT + sofs]), y);
+            dequant8(w, e4m3_decode(msc[i * SPT + sofs]) * sx, y);
 #pragma unroll
             for (int t = TT - 1; t >= 0; --t) {
                 const int kk = mlab[t * DEC_TRIP + i];
@@ -2305,13 +2325,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
             QVG_KERNEL((k_decode_lds<DD, GG, uint16_t, OT, TT, RO, true>), g, b, lds, s, a.codes, a.scales,       \
                        a.assign, a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.tok_begin, a.tok_begin + a.ntok, c0,  \
-                       units, a.rope, a.rope_heads, (OT *)a.out, a.out_hs);                                       \
+                       units, a.rope, a.rope_heads, a.scale_exp, (OT *)a.out, a.out_hs);                          \
         } else {                                                                                                  \
             (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, GG, CT, OT, TT, RO, false>,                  \
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
             QVG_KERNEL((k_decode_lds<DD, GG, CT, OT, TT, RO, false>), g, b, lds, s, a.codes, a.scales, a.assign,  \
                        a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.tok_begin, a.tok_begin + a.ntok, c0, units,     \
-                       a.rope, a.rope_heads, (OT *)a.out, a.out_hs);                                              \
+                       a.rope, a.rope_heads, a.scale_exp, (OT *)a.out, a.out_hs);                                 \
         }                                                                                                         \
     } while (0)
 #define QVG_DECL(DD, GG, CT, OT, TT)                               \
@@ -2365,11 +2385,11 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
         if (a.cent_dtype == DT_E4M3)                                                                              \
             QVG_KERNEL((k_decode<DD, uint16_t, OT, TT, true>), g, b, 0, s, a.codes, a.scales, a.assign, a.cent,   \
                        a.cap, a.chunk_tokens, a.H, a.K, a.T, a.G, a.tok_begin, a.ntok, a.rope, a.rope_heads,     \
-                       (OT *)a.out, a.out_hs, bph);                                                               \
+                       a.scale_exp, (OT *)a.out, a.out_hs, bph);                                                  \
         else                                                                                                      \
             QVG_KERNEL((k_decode<DD, CT, OT, TT, false>), g, b, 0, s, a.codes, a.scales, a.assign, a.cent,        \
                        a.cap, a.chunk_tokens, a.H, a.K, a.T, a.G, a.tok_begin, a.ntok, a.rope, a.rope_heads,     \
-                       (OT *)a.out, a.out_hs, bph);                                                               \
+                       a.scale_exp, (OT *)a.out, a.out_hs, bph);                                                  \
     } while (0)
 #define QVG_DEC_T(DD, CT, OT)                              \
     do {                                                   \
@@ -2438,8 +2458,9 @@ __device__ __forceinline__ void attn_row8(const AttnSrc &a, int head, int64_t n,
     const size_t row = (size_t)head * a.cap + n;
     const uint32_t w = reinterpret_cast<const uint16_t *>(a.codes)[row * (D / 8) + j];
     const uint32_t sc = a.scales[row * (D / a.G) + (8 * j) / a.G];
-    dequant8(w, e4m3_decode(sc), y);
     const int64_t c = n / a.chunk_tokens;
+    const float sx = a.scale_exp ? ldexpf(1.f, a.scale_exp[c * a.heads + head]) : 1.f;
+    dequant8(w, e4m3_decode(sc) * sx, y);
 #pragma unroll
     for (int t = TT - 1; t >= 0; --t) {
         int k = a.assign[((size_t)t * a.heads + head) * a.cap + n];

@@ -125,9 +125,12 @@ hipError_t launch_store_e4m3(int D, int dtype, int H, int K, const float *C, uin
 // r = R(t-1) - cent[pi] (cent non-null; cent [H][cent_rows][D] of the tensor
 // dtype) or r = R(t-1); then 2-bit codes and E4M3 scales of r, head stride
 // q_cap tokens.
+// Two-level scales: amax_out (non-null, [H] zeroed beforehand) makes this
+// launch only gather max|r| per head; amax_in (non-null) quantises with the
+// second-level exponent it implies and writes it to exp_out [H].
 hipError_t launch_quant(int D, int dtype, int H, int N, const Src &src, const void *cent, int cent_rows,
                         const uint8_t *pi, int64_t pi_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap,
-                        int G, hipStream_t s);
+                        int G, uint32_t *amax_out, const uint32_t *amax_in, int8_t *exp_out, hipStream_t s);
 
 // Fused dequantise + reconstruct of tokens [tok_begin, tok_begin + ntok), with an
 // optional rotary position embedding of the first rope_heads heads.
@@ -142,6 +145,8 @@ struct DecodeArgs {
     // or null
     const float *rope = nullptr;
     int rope_heads = 0;
+    // second-level exponents of two-level scales, [n_chunks][H] of the view, or null
+    const int8_t *scale_exp = nullptr;
     void *out;
     int out_dtype;
     int64_t out_hs;
@@ -154,6 +159,7 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 struct AttnSrc {
     const uint8_t *codes, *scales, *assign;
     const void *cent;
+    const int8_t *scale_exp;   // [n_chunks][heads] two-level exponents, or null
     int64_t cap;
     int chunk_tokens, heads, K, G;
 };

@@ -55,6 +55,13 @@ enum {
 
 enum { QVG_F32 = 0, QVG_BF16 = 1 };
 
+/* How the per-group scales are formed (qvg_config.scale_mode). */
+enum {
+    QVG_SCALE_E4M3 = 0,     /* E4M3FN(max|r| / 1.5), saturating at 448                         */
+    QVG_SCALE_TWO_LEVEL = 1 /* E4M3FN(max|r| / 1.5 / 2^f) worth its value * 2^f, with one f >= 0
+                               per (chunk, head), the smallest that saturates no group          */
+};
+
 /* How the centroid tables are stored (qvg_config.centroid_format). */
 enum {
     QVG_CENT_NATIVE = 0, /* in the tensor dtype (bf16 or fp32)                          */
@@ -98,7 +105,13 @@ enum {
  *                of C / 2^e (nearest, ties to even).  A stage's labels and the
  *                later residuals use the stored values; the streaming cache
  *                keeps the unrounded fp32 centroids.  Halves the table bytes.
- *   reserved     must be 0                                                       */
+ *   scale_mode   QVG_SCALE_E4M3, or QVG_SCALE_TWO_LEVEL: value residuals with
+ *                outliers near 1e3 (163.com article, section 2) can exceed what an
+ *                E4M3 scale holds (448 * 1.5 = 672); a second-level power of two
+ *                per (chunk, head) in the view's scale_exp extends the range
+ *                exactly.  It lowers the worst error of saturating groups; the
+ *                larger step also applies to the rest of their group.  A chunk
+ *                with no saturating group keeps f = 0 and the plain result.    */
 typedef struct {
     int32_t d;
     int32_t n_centroids;
@@ -110,7 +123,7 @@ typedef struct {
     int32_t dtype;
     int32_t converge; /* >= 0 */
     int32_t centroid_format;
-    int32_t reserved;
+    int32_t scale_mode;
 } qvg_config;
 
 /* The compressed cache of one tensor (K or V) of one layer, caller-allocated.
@@ -120,6 +133,8 @@ typedef struct {
  *   centroids  [n_chunks][T][H] tables of K x d stored centroids: dtype values
  *              (QVG_CENT_NATIVE) or 16 + K*d bytes each (QVG_CENT_E4M3),
  *              n_chunks = ceil(cap_tokens / chunk_tokens)
+ *   scale_exp  [n_chunks][H] int8 second-level scale exponents
+ *              (QVG_SCALE_TWO_LEVEL; may be NULL otherwise)
  * Chunk c holds tokens [c * chunk_tokens, min((c + 1) * chunk_tokens, cap_tokens)).
  * Buffer sizes: qvg_cache_view_bytes.                                           */
 typedef struct {
@@ -130,6 +145,7 @@ typedef struct {
     int64_t cap_tokens;
     int32_t chunk_tokens;
     int32_t heads;
+    int8_t *scale_exp;
 } qvg_cache_view;
 
 /* Streaming centroid cache (163.com article, section 5; gist.science summaries,
@@ -345,7 +361,7 @@ qvg_status qvg_group_quant(const float *r, int64_t r_head_stride, int32_t heads,
  * section 5: the fused dequantisation kernel; storage format of sections 5 and 7):
  *   codes [H][N][d/4], scales [H][N][d/G], assign [T][H][N] uint8,
  *   centroids [T][H] tables in cfg's centroid format  ->  out [H][N][d] (out_dtype),
- *   contiguous. */
+ *   contiguous.  QVG_ERR_UNSUPPORTED with two-level scales (use qvg_decode). */
 qvg_status qvg_dequant_reconstruct(const qvg_config *cfg, int32_t heads, int32_t n_tokens,
                                    const uint8_t *codes, const uint8_t *scales,
                                    const uint8_t *assign, const void *centroids, void *out,

@@ -15,4 +15,4 @@ from .qvg import (CodecConfig, Encoded, assign, update, lloyd, group_quant, pack
                   dequant, encode_chunk, decode_chunk, decode, rope_rotate, rtn_reconstruct, mse,
                   kv_cache_bytes, chunk_bytes, compression_ratio, bits_per_value_ratio,
                   E4M3_TABLE_HEADER, e4m3_table_exponent, store_e4m3, attention,
-                  attention_tolerance)
+                  attention_tolerance, two_level_exponent)

@@ -74,6 +74,7 @@ class CodecConfig:
     dtype: str = "bf16"        # "bf16" or "f32": input values and centroid storage
     converge: int = 0          # 0: fixed round counts; c >= 1: stop once a round moves fewer than c tokens
     centroid_format: str = "native"   # "native": stored in dtype; "e4m3": FP8 E4M3 times 2^e per table
+    scale_mode: str = "e4m3"   # "e4m3": group scales saturate at 448; "two_level": 2^f per (chunk, head) x E4M3
 
 
 # --------------------------------------------------------------------------
@@ -216,17 +217,20 @@ def store_e4m3(C: np.ndarray):
 # 2-bit group quantisation and its inverse
 # --------------------------------------------------------------------------
 
-def group_quant(R32: np.ndarray, G: int):
+def group_quant(R32: np.ndarray, G: int, f: int = 0):
     """Quantise rows of fp32 values in groups of G channels.
 
+    f >= 0 is the second-level exponent of the two-level scale: the group's
+    scale is stored as the E4M3FN code of fp32(a / 1.5) / 2^f and worth its
+    value times 2^f (f = 0: the plain E4M3 scale).
     Returns (q [N][d] in {0..3}, packed [N][d/4] uint8, scale codes [N][d/G]
     uint8 E4M3FN)."""
     R32 = np.asarray(R32, dtype=F32)
     N, d = R32.shape
     g = R32.reshape(N, d // G, G)
     a = np.abs(g).max(axis=2)                         # float32
-    s_code = e4m3_encode(a / F32(1.5))                # fp32 division, then E4M3
-    s = e4m3_decode(s_code).astype(F32)[:, :, None]
+    s_code = e4m3_encode(np.ldexp((a / F32(1.5)).astype(np.float64), -f))   # fp32 division, exact 2^-f, E4M3
+    s = np.ldexp(e4m3_decode(s_code), f).astype(F32)[:, :, None]
     q = (g >= -s).astype(np.uint8) + (g >= 0) + (g >= s)
     q = q.reshape(N, d).astype(np.uint8)
     packed = pack2(q)
@@ -250,11 +254,24 @@ def unpack2(packed: np.ndarray) -> np.ndarray:
     return out.reshape(N, nb * 4)
 
 
-def dequant(packed: np.ndarray, s_code: np.ndarray, G: int) -> np.ndarray:
-    """(q - 1.5) * s in float32 (the product is exact)."""
+def two_level_exponent(R32: np.ndarray) -> int:
+    """Second-level exponent f of one chunk of one head: the smallest f >= 0
+    with fp32(max|r| / 1.5) <= 448 * 2^f, so that no group's scale saturates.
+    The pages store the group scales in E4M3, whose largest value (448) is
+    below what value outliers near 1e3 need (163.com article, sections 2 and
+    5); a power of two per chunk and head extends the range exactly."""
+    amax15 = float(np.float32(np.abs(np.asarray(R32, F32)).max()) / F32(1.5))
+    f = 0
+    while amax15 > math.ldexp(448.0, f):
+        f += 1
+    return f
+
+
+def dequant(packed: np.ndarray, s_code: np.ndarray, G: int, f: int = 0) -> np.ndarray:
+    """(q - 1.5) * s in float32 (the product is exact); s = E4M3 value x 2^f."""
     q = unpack2(packed).astype(F32)
     N, d = q.shape
-    s = e4m3_decode(s_code).astype(F32)
+    s = np.ldexp(e4m3_decode(s_code), f).astype(F32)
     return ((q.reshape(N, d // G, G) - F32(1.5)) * s[:, :, None]).reshape(N, d)
 
 
@@ -273,6 +290,7 @@ class Encoded:
     sse: Optional[List[List[List[float]]]] = None  # [t][h] -> per-iteration SSE
     rounds: Optional[np.ndarray] = None            # [T][H] Lloyd updates run
     cent_exp: Optional[np.ndarray] = None          # [T][H] table exponents (FP8 centroid storage)
+    scale_exp: Optional[np.ndarray] = None         # [H] second-level scale exponents (two-level scales)
 
 
 def _store(C: np.ndarray, dtype: str, fmt: str = "native") -> np.ndarray:
@@ -308,6 +326,8 @@ def encode_chunk(X: np.ndarray, cfg: CodecConfig, cache: Optional[np.ndarray] = 
     rounds = np.zeros((T, H), np.int32)
     fp8 = cfg.centroid_format == "e4m3"
     cexp = np.zeros((T, H), np.int32) if fp8 else None
+    two = cfg.scale_mode == "two_level"
+    sexp = np.zeros(H, np.int32) if two else None
     Rall = X.astype(np.float64)
     for h in range(H):
         R = Rall[h]
@@ -334,10 +354,13 @@ def encode_chunk(X: np.ndarray, cfg: CodecConfig, cache: Optional[np.ndarray] = 
                 if len(residuals) <= t:
                     residuals.append(np.zeros_like(Rall))
                 residuals[t][h] = R
-        _, packed, s_code = group_quant(R.astype(F32), G)
+        f = two_level_exponent(R) if two else 0
+        if two:
+            sexp[h] = f
+        _, packed, s_code = group_quant(R.astype(F32), G, f)
         codes[h] = packed
         scales[h] = s_code
-    return Encoded(codes, scales, asg, cent, new_cache, residuals, sse, rounds, cexp)
+    return Encoded(codes, scales, asg, cent, new_cache, residuals, sse, rounds, cexp, sexp)
 
 
 def rope_rotate(y: np.ndarray, table: np.ndarray) -> np.ndarray:
@@ -357,7 +380,8 @@ def rope_rotate(y: np.ndarray, table: np.ndarray) -> np.ndarray:
 
 def decode_chunk(codes: np.ndarray, scales: np.ndarray, asg: np.ndarray,
                  cent: np.ndarray, G: int, out: str = "f32",
-                 rope: Optional[np.ndarray] = None, rope_heads: Optional[int] = None) -> np.ndarray:
+                 rope: Optional[np.ndarray] = None, rope_heads: Optional[int] = None,
+                 scale_exp: Optional[np.ndarray] = None) -> np.ndarray:
     """Rebuild [H][N][d] from one chunk's stored encoding.
 
     out="f32": fp32 sums in the order dequant + C(T) + ... + C(1);
@@ -365,13 +389,14 @@ def decode_chunk(codes: np.ndarray, scales: np.ndarray, asg: np.ndarray,
     out="f64": the exact float64 sum (for error bounds).
     rope: [N][d/2][2] (cos, sin) that rotates heads [0, rope_heads) (all heads
     when rope_heads is None) after the fp32 sums and before the rounding to the
-    output type (f32 and bf16 only)."""
+    output type (f32 and bf16 only).  scale_exp: [H] second-level exponents
+    of two-level scales (None: plain E4M3 scales)."""
     H, N, _ = codes.shape
     T = asg.shape[0]
     nrot = 0 if rope is None else (H if rope_heads is None else rope_heads)
     ys = []
     for h in range(H):
-        y = dequant(codes[h], scales[h], G)
+        y = dequant(codes[h], scales[h], G, 0 if scale_exp is None else int(scale_exp[h]))
         if out == "f64":
             assert rope is None
             y = y.astype(np.float64)
@@ -389,7 +414,7 @@ def decode_chunk(codes: np.ndarray, scales: np.ndarray, asg: np.ndarray,
 
 
 def decode(enc: Encoded, G: int, out: str = "f32") -> np.ndarray:
-    return decode_chunk(enc.codes, enc.scales, enc.assign, enc.centroids, G, out)
+    return decode_chunk(enc.codes, enc.scales, enc.assign, enc.centroids, G, out, scale_exp=enc.scale_exp)
 
 
 def attention(Q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):

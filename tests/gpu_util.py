@@ -35,7 +35,7 @@ def ocfg(p: synthkv.Preset, tensor: str, **kw) -> oracle.CodecConfig:
 def gcfg(oc: oracle.CodecConfig):
     q = lib()
     return q.config(oc.d, oc.n_centroids, oc.n_stages, oc.group_size, oc.iters_cold, oc.iters_warm,
-                    oc.seed, oc.dtype, oc.converge, oc.centroid_format)
+                    oc.seed, oc.dtype, oc.converge, oc.centroid_format, oc.scale_mode)
 
 
 def fp8_tables(raw: np.ndarray, K: int, d: int):
@@ -82,7 +82,8 @@ def fetch(dst, chunk: int, oc: oracle.CodecConfig):
     if oc.centroid_format == "e4m3":
         cent, _ = fp8_tables(cent, oc.n_centroids, oc.d)
     return dict(codes=to_np(dst.codes[:, b:e]), scales=to_np(dst.scales[:, b:e]),
-                assign=to_np(dst.assign[:T, :, b:e]), centroids=cent)
+                assign=to_np(dst.assign[:T, :, b:e]), centroids=cent,
+                scale_exp=None if dst.scale_exp is None else to_np(dst.scale_exp[chunk]).astype(np.int32))
 
 
 def distance_table(Xop: np.ndarray, C: np.ndarray) -> np.ndarray:

@@ -44,7 +44,7 @@ def test_struct_layouts_match_the_header(q):
     assert ctypes.sizeof(q.qvg_config) == 48
     assert q.qvg_config.seed.offset == 24 and q.qvg_config.dtype.offset == 32
     assert q.qvg_config.converge.offset == 36 and q.qvg_config.centroid_format.offset == 40
-    assert ctypes.sizeof(q.qvg_cache_view) == 48
+    assert ctypes.sizeof(q.qvg_cache_view) == 56
     assert q.qvg_cache_view.cap_tokens.offset == 32 and q.qvg_cache_view.heads.offset == 44
     assert ctypes.sizeof(q.qvg_kernel_stat) == 64
 
@@ -95,7 +95,7 @@ def test_workspace_sizes(q):
 @pytest.mark.parametrize("field,value,status", [
     ("n_centroids", 0, -1), ("n_centroids", 257, -1), ("n_stages", -1, -1), ("n_stages", 9, -1),
     ("group_size", 48, -1), ("group_size", 0, -1), ("iters_cold", -1, -1), ("dtype", 7, -1),
-    ("converge", -1, -1), ("centroid_format", 2, -1), ("reserved", 1, -1), ("d", 192, -2), ("d", 256, -2), ("group_size", 8, -2)])
+    ("converge", -1, -1), ("centroid_format", 2, -1), ("scale_mode", 2, -1), ("d", 192, -2), ("d", 256, -2), ("group_size", 8, -2)])
 def test_config_validation(q, field, value, status):
     g, _ = _cfg(q, synthkv.PRESETS[2])
     setattr(g, field, value)
@@ -106,7 +106,7 @@ def test_config_validation(q, field, value, status):
 
 
 def _view(q, heads=2, cap=100, chunk=50, ptr=4096):
-    return q.qvg_cache_view(ptr, ptr, ptr, ptr, cap, chunk, heads)
+    return q.qvg_cache_view(ptr, ptr, ptr, ptr, cap, chunk, heads, None)
 
 
 def test_encode_argument_errors_launch_nothing(q):

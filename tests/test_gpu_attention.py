@@ -32,20 +32,24 @@ def _decoded(oc, dst, b, e, chunk, heads, rope=None):
                 full[lo - cb:hi - cb] = rope[lo - b:hi - b]
                 r = full
             y = oracle.decode_chunk(g["codes"][h:h + 1], g["scales"][h:h + 1], g["assign"][:, h:h + 1],
-                                    g["centroids"][:, h:h + 1], oc.group_size, "bf16", rope=r)[0]
+                                    g["centroids"][:, h:h + 1], oc.group_size, "bf16", rope=r,
+                                    scale_exp=None if g["scale_exp"] is None else g["scale_exp"][h:h + 1])[0]
             rows.append(y[sl])
         out.append(np.stack(rows))
     return np.concatenate(out, axis=1)
 
 
-@pytest.mark.parametrize("fmt,use_rope,b,e,Nq", [("native", False, 0, 2000, 300), ("native", True, 137, 1931, 256),
-                                                 ("e4m3", True, 700, 2000, 77), ("native", False, 0, 64, 1)])
-def test_attention_over_compressed_cache(fmt, use_rope, b, e, Nq):
-    say(f"attention fmt={fmt} rope={use_rope} keys [{b}, {e}) Nq={Nq}")
+@pytest.mark.parametrize("fmt,use_rope,b,e,Nq,sm", [("native", False, 0, 2000, 300, "e4m3"),
+                                                    ("native", True, 137, 1931, 256, "e4m3"),
+                                                    ("e4m3", True, 700, 2000, 77, "e4m3"),
+                                                    ("native", False, 0, 64, 1, "e4m3"),
+                                                    ("native", True, 0, 2000, 100, "two_level")])
+def test_attention_over_compressed_cache(fmt, use_rope, b, e, Nq, sm):
+    say(f"attention fmt={fmt} rope={use_rope} keys [{b}, {e}) Nq={Nq} scales {sm}")
     q = lib()
     p = synthkv.PRESETS[2]
     H, chunk = 2, 1000
-    oc = ocfg(p, "K", n_centroids=64, iters_cold=3, iters_warm=2, centroid_format=fmt)
+    oc = ocfg(p, "K", n_centroids=64, iters_cold=3, iters_warm=2, centroid_format=fmt, scale_mode=sm)
     # K and V of H heads as one 2H-head tensor (keys first)
     X = np.concatenate([synthkv.gen_numpy(p, t, heads=H, n_tokens=2000) for t in ("K", "V")])
     dst, _ = gpu_encode_chunks(oc, X, chunk)
