@@ -355,8 +355,10 @@ hipError_t launch_init_centroids(int D, int dtype, int H, int K, const Src &src,
 // which keeps every value negative (the 2^-12 |x|^2 margin is far larger)
 // and misorders two centroids only if they lie within
 // 2^-17.4 (|x|^2 + max |c|^2) of each other; a key is within 2^-15 of its
-// value.  A candidate whose key is further below the best key k1 than
-//   2^-16 (|x|^2 + max |c|^2) + 2^-14 (|k1| + |k|)
+// value.  (The 24 ulp assume every rounding directed, 1 ulp, at each of six
+// levels of each instruction; round-to-nearest halves it.)  A candidate whose
+// key is further below the best key k1 than
+//   2^-17 (|x|^2 + max |c|^2) + 2^-14 (|k1| + |k|)
 // cannot be the nearest; a token with no such second or third candidate keeps
 // the fp32 winner.  The others are re-decided on fp64 distances of the two or
 // three candidates, 16 lanes per token: every bf16 x bf16 product is exact in
@@ -589,8 +591,8 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
         }
         const int c1 = (int)(__float_as_uint(k1) & 0xFFu), c2 = (int)(__float_as_uint(k2) & 0xFFu);
         const int c3 = (int)(__float_as_uint(k3) & 0xFFu);
-        const float tol2 = 0x1p-16f * (xx[b] - 2.0f * fminf(lhcn[c1], lhcn[c2])) + 0x1p-14f * (fabsf(k1) + fabsf(k2));
-        const float tol3 = 0x1p-16f * (xx[b] - 2.0f * fminf(lhcn[c1], lhcn[c3])) + 0x1p-14f * (fabsf(k1) + fabsf(k3));
+        const float tol2 = 0x1p-17f * (xx[b] - 2.0f * fminf(lhcn[c1], lhcn[c2])) + 0x1p-14f * (fabsf(k1) + fabsf(k2));
+        const float tol3 = 0x1p-17f * (xx[b] - 2.0f * fminf(lhcn[c1], lhcn[c3])) + 0x1p-14f * (fabsf(k1) + fabsf(k3));
         const bool third = (k1 - k3) <= tol3;   // c3 might be the nearest too
         const bool tie = third || (k1 - k2) <= tol2;
         const int n = tok0 + 16 * b + r16;
