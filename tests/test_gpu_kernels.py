@@ -157,10 +157,13 @@ def test_assign_three_centroids_inside_the_fp32_band():
     """Each token has three candidate centroids whose exact distances differ by
     2^-14 .. 9 * 2^-14 while |x|^2 is about 2e6 (value-like outlier channels),
     far inside the matrix cores' fp32 error band, and the exact nearest has the
-    highest index of the three.  The fp32 ranking of the three is then noise,
-    and the fp64 re-decision sees only the fp32 top two, so the exact nearest
-    can be missed.  Whatever the kernel returns must obey the near-tie rule
-    (relative gap < 1e-4) and be one of the three; the outcome is printed."""
+    highest index of the three.  The fp32 ranking of the three is then noise.
+    The fp64 re-decision sees the best two of each lane's quarter of the
+    centroids, merged into the token's best three, so the exact nearest can be
+    missed when all three candidates fall in one quarter (centroid numbers
+    with equal (k mod 16) / 4).  Whatever the kernel returns must obey the
+    near-tie rule (relative gap < 1e-4) and be one of the three; the outcome
+    is printed."""
     say("kmeans_assign, three centroids within the fp32 error band")
     q = lib()
     rng = np.random.default_rng(21)
