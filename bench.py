@@ -227,7 +227,7 @@ def main():
     else:
         prof_ms_step = None
 
-    # rooflines: assign against the bf16 matrix peak, update and decode against HBM
+    # rooflines: assign against the bf16 matrix peak, update, quantiser and decode against HBM
     roofs = {}
     dec_roof = dict(kernel="decode", bound="hbm", achieved=round(decode_gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(decode_gbs / HBM_PEAK_GBS, 4), traffic=hbm_traffic("decode"),
@@ -236,7 +236,7 @@ def main():
     roofs["decode"] = dec_roof
     if rope_rec is not None:
         roofs["decode_rope"] = rope_rec.pop("roofline")
-    for name in ("assign", "update"):
+    for name, key in (("assign", "assign"), ("update", "update"), ("residual_quant", "quant")):
         if name not in raw_stats:
             continue
         r = raw_stats[name]
@@ -244,15 +244,15 @@ def main():
         secs = r["total_ms"] * 1e-3 / r["launches"]
         if name == "assign":
             ach = per / secs / 1e12
-            roofs[name] = dict(kernel=name, bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFLOPS,
-                               unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4))
+            roofs[key] = dict(kernel=key, bound="mfma", achieved=round(ach, 2), peak=MFMA_BF16_PEAK_TFLOPS,
+                              unit="TFLOP/s", frac=round(ach / MFMA_BF16_PEAK_TFLOPS, 4))
         else:
             ach = per / secs / 1e9
-            roofs[name] = dict(kernel=name, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                               frac=round(ach / HBM_PEAK_GBS, 4))
-        roofs[name].update(traffic=hbm_traffic(name), avg_launch_us=round(secs * 1e6, 2),
-                           algorithmic_per_launch=per,
-                           timed="HIP events around every launch of the profiled steps, on the launch stream")
+            roofs[key] = dict(kernel=key, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                              frac=round(ach / HBM_PEAK_GBS, 4))
+        roofs[key].update(traffic=hbm_traffic(key), avg_launch_us=round(secs * 1e6, 2),
+                          algorithmic_per_launch=per,
+                          timed="HIP events around every launch of the profiled steps, on the launch stream")
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"]) if kernels else "decode"
     roof = roofs.get(dom, dec_roof)
 

@@ -1842,9 +1842,14 @@ __global__ __launch_bounds__(256) void k_quant(Src src, int N, const KVT *cent, 
                                                uint32_t *amax_out, const uint32_t *amax_in, int8_t *exp_out) {
     constexpr int SL = D / 16;
     constexpr int TPB = 256 / SL;
-    const int h = blockIdx.y;
+    // one-dimensional grid: the blocks of one head on one XCD, in token order,
+    // so that the head's centroid tables are fetched into that XCD's L2 once
+    // (a grid too large for one dimension has one row of blocks per head)
+    const uint32_t bph = (N + TPB - 1) / TPB;   // blocks per head
+    const uint32_t tile = gridDim.y > 1 ? blockIdx.y * bph + blockIdx.x : xcd_tile(blockIdx.x, gridDim.x);
+    const int h = (int)(tile / bph);
     const int j = threadIdx.x % SL;
-    const int n = blockIdx.x * TPB + threadIdx.x / SL;
+    const int n = (int)(tile % bph) * TPB + threadIdx.x / SL;
     if (n >= N) return;   // whole groups leave together (SL divides 64)
     float r[16];
     if constexpr (PM <= 1) {
@@ -1910,7 +1915,9 @@ hipError_t launch_quant(int D, int dtype, int H, int N, const Src &src, const vo
                         const uint8_t *pi, int64_t pi_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap, int G,
                         uint32_t *amax_out, const uint32_t *amax_in, int8_t *exp_out, hipStream_t s) {
     const int TPB = 256 / (D / 16);
-    dim3 g((N + TPB - 1) / TPB, H), b(256);
+    const int64_t bph = (N + TPB - 1) / TPB, nb = (int64_t)H * bph;
+    const bool one_dim = nb * 256 < ((int64_t)1 << 32);
+    dim3 g(one_dim ? (uint32_t)nb : (uint32_t)bph, one_dim ? 1u : (uint32_t)H), b(256);
 #define QVG_QUANT_LAUNCH(CE, PMV)                                                                            \
     QVG_KERNEL((k_quant<DD, KVT, CE, PMV>), g, b, 0, s, src, N, (const KVT *)cent, cent_rows, pi, pi_hs, codes, \
                scales, q_cap, G, amax_out, amax_in, exp_out)
