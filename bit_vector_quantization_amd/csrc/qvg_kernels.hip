@@ -2154,6 +2154,15 @@ constexpr int DEC_TRIP = 512;   // tokens per trip
 constexpr int DEC_PARTS = 2;    // workgroups per (chunk, head), each with its part of every row
 constexpr size_t DEC_LDS_MAX = 160 * 1024 - 1024;   // LDS bytes one workgroup may take
 
+// Rotated decodes give each XCD one contiguous run of (chunk, head) units in
+// chunk-major order, of about equal token work: the rotated heads of a chunk
+// then share one XCD, whose L2 fetches the chunk's rows of the rotation table
+// once for all of them (with the units spread over the XCDs by head, every XCD
+// fetched every chunk's rows).  start[x] .. start[x + 1] are XCD x's units.
+struct DecRuns {
+    int64_t start[9];
+};
+
 // LDS bytes of one trip's staged codes, scales and assignments.
 constexpr size_t dec_meta_bytes(int D, int G, int T) {
     return (size_t)DEC_TRIP * (D / 4 / DEC_PARTS) + (size_t)DEC_TRIP * (D / DEC_PARTS >= G ? D / DEC_PARTS / G : 1) +
@@ -2177,7 +2186,7 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, 8) void k_decode_lds(const uint8_t
                                                                    const void *__restrict__ cent_v, int64_t cap,
                                                                    int chunk_tokens, int H, int K,
                                                                    int64_t tok_begin, int64_t tok_end,
-                                                                   int64_t c_first, int64_t n_units,
+                                                                   int64_t c_first, int64_t n_units, DecRuns runs,
                                                                    const float *__restrict__ rope, int rope_heads,
                                                                    const int8_t *__restrict__ scale_exp,
                                                                    OutT *__restrict__ out, int64_t out_hs) {
@@ -2198,9 +2207,18 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, 8) void k_decode_lds(const uint8_t
     // the same XCD, running together, so a code line fetched by one is still in
     // that XCD's L2 for the other.  Workgroups past the last (chunk, head) of a
     // grid padded to a multiple of 8 x PARTS have nothing to do.
+    // Rotated decodes: XCD blockIdx % 8 takes its run of units in order, the
+    // PARTS workgroups of a unit one after the other.
     const int hf = (int)((blockIdx.x / 8) % PARTS);
-    const int64_t uu = (int64_t)(blockIdx.x / 8 / PARTS) * 8 + blockIdx.x % 8;
-    if (uu >= n_units) return;
+    int64_t uu;
+    if constexpr (ROPE) {
+        const int x = blockIdx.x % 8;
+        uu = runs.start[x] + blockIdx.x / 8 / PARTS;
+        if (uu >= runs.start[x + 1]) return;
+    } else {
+        uu = (int64_t)(blockIdx.x / 8 / PARTS) * 8 + blockIdx.x % 8;
+        if (uu >= n_units) return;
+    }
     const int h = (int)(uu % H);
     const int64_t c = c_first + uu / H;
     const int tid = threadIdx.x;
@@ -2324,7 +2342,46 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
     if (a.T >= 1 && a.T <= 4 && lds <= DEC_LDS_MAX && scales_aligned) {
         const int64_t c0 = a.tok_begin / a.chunk_tokens, c1 = (a.tok_begin + a.ntok - 1) / a.chunk_tokens;
         const int64_t units = (c1 - c0 + 1) * a.H;   // (chunk, head) pairs
-        const int64_t nb = (units + 7) / 8 * 8 * DEC_PARTS;
+        int64_t nb = (units + 7) / 8 * 8 * DEC_PARTS;
+        DecRuns runs{};
+        if (a.rope) {
+            // runs of equal token work: unit u = (chunk c0 + u / H, head u % H)
+            // holds the chunk's tokens inside [tok_begin, tok_begin + ntok)
+            const int64_t tb = a.tok_begin, te = a.tok_begin + a.ntok, ct = a.chunk_tokens;
+            auto tokens_before = [&](int64_t u) {   // token work of units [0, u)
+                const int64_t full = u / a.H, part = u % a.H;
+                auto chunk_tokens = [&](int64_t c) {
+                    return std::min(te, (c + 1) * ct) - std::max(tb, c * ct);
+                };
+                // every chunk between the first and the last is whole
+                int64_t w = 0;
+                if (full > 0) {
+                    w += chunk_tokens(c0) * a.H;
+                    if (full > 1) {
+                        const int64_t cl = c0 + full - 1;   // the last whole chunk counted
+                        w += (full - 2) * ct * a.H + chunk_tokens(cl) * a.H;
+                    }
+                }
+                if (part > 0) w += chunk_tokens(c0 + full) * part;
+                return w;
+            };
+            const int64_t total = tokens_before(units);
+            int64_t most = 0;
+            runs.start[0] = 0;
+            for (int x = 1; x <= 8; ++x) {
+                // the first unit whose work before it reaches x / 8 of the total
+                int64_t lo = runs.start[x - 1], hi = units;
+                const int64_t goal = total * x / 8;
+                while (lo < hi) {
+                    const int64_t mid = (lo + hi) / 2;
+                    if (tokens_before(mid) >= goal) hi = mid;
+                    else lo = mid + 1;
+                }
+                runs.start[x] = x == 8 ? units : lo;
+                most = std::max(most, runs.start[x] - runs.start[x - 1]);
+            }
+            nb = 8 * most * DEC_PARTS;
+        }
         if (nb < (int64_t)UINT32_MAX) {
             dim3 g((unsigned)nb), b(DEC_LDS_THREADS);
 #define QVG_DECL_R(DD, GG, CT, OT, TT, RO)                                                                        \
@@ -2334,13 +2391,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
             QVG_KERNEL((k_decode_lds<DD, GG, uint16_t, OT, TT, RO, true>), g, b, lds, s, a.codes, a.scales,       \
                        a.assign, a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.tok_begin, a.tok_begin + a.ntok, c0,  \
-                       units, a.rope, a.rope_heads, a.scale_exp, (OT *)a.out, a.out_hs);                          \
+                       units, runs, a.rope, a.rope_heads, a.scale_exp, (OT *)a.out, a.out_hs);                          \
         } else {                                                                                                  \
             (void)hipFuncSetAttribute((const void *)k_decode_lds<DD, GG, CT, OT, TT, RO, false>,                  \
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);                      \
             QVG_KERNEL((k_decode_lds<DD, GG, CT, OT, TT, RO, false>), g, b, lds, s, a.codes, a.scales, a.assign,  \
                        a.cent, a.cap, a.chunk_tokens, a.H, a.K, a.tok_begin, a.tok_begin + a.ntok, c0, units,     \
-                       a.rope, a.rope_heads, a.scale_exp, (OT *)a.out, a.out_hs);                                 \
+                       runs, a.rope, a.rope_heads, a.scale_exp, (OT *)a.out, a.out_hs);                                 \
         }                                                                                                         \
     } while (0)
 #define QVG_DECL(DD, GG, CT, OT, TT)                               \
