@@ -2516,38 +2516,75 @@ constexpr int ATT_KROW = ATT_D + 8;      // bf16 per K row in LDS (padded agains
 constexpr int ATT_VROW = ATT_BK + 8;     // bf16 per transposed V row
 constexpr size_t ATT_LDS = (size_t)2 * (ATT_BK * ATT_KROW + ATT_D * ATT_VROW);
 
-// 8 channels [8 j, 8 j + 8) of key n of one head of a compressed tensor, in fp32:
-// dequantised, then the stages' centroid rows added from T - 1 down to 0.
+// 8 channels [8 j, 8 j + 8) of key n of one head of a compressed tensor, in
+// three steps so that the loads of K and V go out together: fetch1 issues the
+// loads that need nothing (codes, scale, second-level exponent, labels, FP8
+// table exponents), fetch2 the centroid rows the labels select, and build
+// dequantises and adds the rows from stage T - 1 down to 0 in fp32.
 template <int TT, bool FP8>
-__device__ __forceinline__ void attn_row8(const AttnSrc &a, int head, int64_t n, int j, float *y) {
+struct AttnRow {
+    uint32_t w, sc;
+    int sexp;
+    int64_t c;
+    int lab[TT];
+    int texp[TT];
+    uint4 cv[TT];   // bf16 row chunk, or (FP8) the 8 code bytes in .x, .y
+};
+
+template <int TT, bool FP8>
+__device__ __forceinline__ void attn_fetch1(const AttnSrc &a, int head, int64_t n, int j, AttnRow<TT, FP8> &r) {
     constexpr int D = ATT_D;
     const size_t row = (size_t)head * a.cap + n;
-    const uint32_t w = reinterpret_cast<const uint16_t *>(a.codes)[row * (D / 8) + j];
-    const uint32_t sc = a.scales[row * (D / a.G) + (8 * j) / a.G];
-    const int64_t c = n / a.chunk_tokens;
-    const float sx = a.scale_exp ? ldexpf(1.f, a.scale_exp[c * a.heads + head]) : 1.f;
-    dequant8(w, e4m3_decode(sc) * sx, y);
+    r.w = reinterpret_cast<const uint16_t *>(a.codes)[row * (D / 8) + j];
+    r.sc = a.scales[row * (D / a.G) + (8 * j) / a.G];
+    r.c = n / a.chunk_tokens;
+    r.sexp = a.scale_exp ? a.scale_exp[r.c * a.heads + head] : 0;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        r.lab[t] = a.assign[((size_t)t * a.heads + head) * a.cap + n];
+        if constexpr (FP8)
+            r.texp[t] = *reinterpret_cast<const int32_t *>(static_cast<const uint8_t *>(a.cent) +
+                                                           (((size_t)r.c * TT + t) * a.heads + head) * (a.K * D + 16));
+    }
+}
+
+template <int TT, bool FP8>
+__device__ __forceinline__ void attn_fetch2(const AttnSrc &a, int head, int j, AttnRow<TT, FP8> &r) {
+    constexpr int D = ATT_D;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const int k = r.lab[t] < a.K ? r.lab[t] : a.K - 1;
+        if constexpr (FP8) {
+            const uint8_t *tbl = static_cast<const uint8_t *>(a.cent) + (((size_t)r.c * TT + t) * a.heads + head) *
+                                                                            (a.K * D + 16);
+            const uint2 v = *reinterpret_cast<const uint2 *>(tbl + 16 + (size_t)k * D + 8 * j);
+            r.cv[t] = make_uint4(v.x, v.y, 0u, 0u);
+        } else {
+            r.cv[t] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.cent) +
+                                                       ((((size_t)r.c * TT + t) * a.heads + head) * a.K + k) * D + 8 * j);
+        }
+    }
+}
+
+template <int TT, bool FP8>
+__device__ __forceinline__ void attn_build(const AttnSrc &a, const AttnRow<TT, FP8> &r, float *y) {
+    const float sx = a.scale_exp ? ldexpf(1.f, r.sexp) : 1.f;
+    dequant8(r.w, e4m3_decode(r.sc) * sx, y);
 #pragma unroll
     for (int t = TT - 1; t >= 0; --t) {
-        int k = a.assign[((size_t)t * a.heads + head) * a.cap + n];
-        k = k < a.K ? k : a.K - 1;
         uint4 cv;
         if constexpr (FP8) {
-            const uint8_t *tbl = static_cast<const uint8_t *>(a.cent) + (((size_t)c * TT + t) * a.heads + head) *
-                                                                            (a.K * D + 16);
-            const float sf = ldexpf(1.f, *reinterpret_cast<const int32_t *>(tbl));
-            const uint2 v = *reinterpret_cast<const uint2 *>(tbl + 16 + (size_t)k * D + 8 * j);
+            const float sf = ldexpf(1.f, r.texp[t]);
             uint32_t o[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t ww = q < 2 ? v.x : v.y, sh = 16 * (q & 1);
+                const uint32_t ww = q < 2 ? r.cv[t].x : r.cv[t].y, sh = 16 * (q & 1);
                 o[q] = (__float_as_uint(e4m3_decode((ww >> sh) & 0xFFu) * sf) >> 16) |
                        (__float_as_uint(e4m3_decode((ww >> (sh + 8)) & 0xFFu) * sf) & 0xFFFF0000u);
             }
             cv = make_uint4(o[0], o[1], o[2], o[3]);
         } else {
-            cv = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.cent) +
-                                                  ((((size_t)c * TT + t) * a.heads + head) * a.K + k) * D + 8 * j);
+            cv = r.cv[t];
         }
         add8<uint16_t>(&cv, y);
     }
@@ -2585,13 +2622,16 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
             const int64_t n = t0 + kk;
             float yk[8], yv[8];
             if (n < kb1) {
-                attn_row8<TT, FP8>(a.k, a.khead0 + h, n, j, yk);
-                if (a.rope) {
-                    float cs[8];
-                    load8_f32(a.rope + (size_t)(n - a.tok_begin) * D + 8 * j, cs);
-                    rope8(cs, yk);
-                }
-                attn_row8<TT, FP8>(a.v, a.vhead0 + h, n, j, yv);
+                AttnRow<TT, FP8> rk, rv;
+                attn_fetch1<TT, FP8>(a.k, a.khead0 + h, n, j, rk);
+                attn_fetch1<TT, FP8>(a.v, a.vhead0 + h, n, j, rv);
+                float cs[8];
+                if (a.rope) load8_f32(a.rope + (size_t)(n - a.tok_begin) * D + 8 * j, cs);
+                attn_fetch2<TT, FP8>(a.k, a.khead0 + h, j, rk);
+                attn_fetch2<TT, FP8>(a.v, a.vhead0 + h, j, rv);
+                attn_build<TT, FP8>(a.k, rk, yk);
+                if (a.rope) rope8(cs, yk);
+                attn_build<TT, FP8>(a.v, rv, yv);
             } else {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) yk[i] = yv[i] = 0.f;
