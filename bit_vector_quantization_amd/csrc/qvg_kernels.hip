@@ -2514,7 +2514,9 @@ constexpr int ATT_BK = 64;               // keys per tile
 constexpr int ATT_D = 128;
 constexpr int ATT_KROW = ATT_D + 8;      // bf16 per K row in LDS (padded against bank conflicts)
 constexpr int ATT_VROW = ATT_BK + 8;     // bf16 per transposed V row
-constexpr size_t ATT_LDS = (size_t)2 * (ATT_BK * ATT_KROW + ATT_D * ATT_VROW);
+// K tile, V^T tile, and each wave's query operands (kept in LDS rather than in
+// registers while the tiles are rebuilt)
+constexpr size_t ATT_LDS = (size_t)2 * (ATT_BK * ATT_KROW + ATT_D * ATT_VROW) + (size_t)ATT_WAVES * (ATT_D / 32) * 64 * 16;
 
 // 8 channels [8 j, 8 j + 8) of key n of one head of a compressed tensor, in
 // three steps so that the loads of K and V go out together: fetch1 issues the
@@ -2603,12 +2605,15 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
     const int g = lane >> 4, c16 = lane & 15;
     const int q0 = blockIdx.x * ATT_BQ + wave * 16;
     // this wave's queries as B operands of S^T = K Q^T: column c16, channels 32 s + 8 g .. + 7
-    bf16x8_t qb[D / 32];
+    // lq[wave][s][lane]: the lane's 16 bytes of k-step s, read back per tile so
+    // that they hold no registers while the tiles are rebuilt (a wave reads
+    // only what it wrote)
+    uint4 *lq = reinterpret_cast<uint4 *>(lvt + ATT_D * ATT_VROW) + (size_t)wave * (D / 32) * 64 + lane;
     {
         const int qr = min(q0 + c16, a.Nq - 1);
         const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (size_t)h * a.q_hs + (size_t)qr * D + 8 * g);
 #pragma unroll
-        for (int s = 0; s < D / 32; ++s) qb[s] = __builtin_bit_cast(bf16x8_t, qp[4 * s]);
+        for (int s = 0; s < D / 32; ++s) lq[s * 64] = qp[4 * s];
     }
     // O^T = V^T P^T: lane holds channels 16 b + 4 g + r of query c16
     f32x4_t o[D / 16];
@@ -2650,6 +2655,9 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
         // S^T = K Q^T for 4 blocks of 16 keys: sacc[kb][r] = score of key
         // 16 kb + 4 g + r for the lane's query c16
         f32x4_t sacc[ATT_BK / 16];
+        bf16x8_t qb[D / 32];
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s) qb[s] = __builtin_bit_cast(bf16x8_t, lq[s * 64]);
 #pragma unroll
         for (int kb = 0; kb < ATT_BK / 16; ++kb) {
             sacc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
