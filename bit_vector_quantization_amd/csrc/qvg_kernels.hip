@@ -2514,9 +2514,14 @@ constexpr int ATT_BK = 64;               // keys per tile
 constexpr int ATT_D = 128;
 constexpr int ATT_KROW = ATT_D + 8;      // bf16 per K row in LDS (padded against bank conflicts)
 constexpr int ATT_VROW = ATT_BK + 8;     // bf16 per transposed V row
+// bf16 per group of 8 transposed V rows (the 8 channels one thread rebuilds):
+// 4 more than 8 rows, so that the 16 groups begin on 16 different banks and the
+// rebuild's 2-byte stores, which write one row of each group at once, do not
+// all fall on one bank
+constexpr int ATT_VGRP = 8 * ATT_VROW + 4;
 // K tile, V^T tile, and each wave's query operands (kept in LDS rather than in
 // registers while the tiles are rebuilt)
-constexpr size_t ATT_LDS = (size_t)2 * (ATT_BK * ATT_KROW + ATT_D * ATT_VROW) + (size_t)ATT_WAVES * (ATT_D / 32) * 64 * 16;
+constexpr size_t ATT_LDS = (size_t)2 * (ATT_BK * ATT_KROW + (ATT_D / 8) * ATT_VGRP) + (size_t)ATT_WAVES * (ATT_D / 32) * 64 * 16;
 
 // 8 channels [8 j, 8 j + 8) of key n of one head of a compressed tensor, in
 // three steps so that the loads of K and V go out together: fetch1 issues the
@@ -2597,7 +2602,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
     constexpr int D = ATT_D;
     extern __shared__ uint16_t att_lds[];
     uint16_t *lk = att_lds;                              // [ATT_BK][ATT_KROW]
-    uint16_t *lvt = lk + ATT_BK * ATT_KROW;              // [D][ATT_VROW]
+    uint16_t *lvt = lk + ATT_BK * ATT_KROW;              // [D / 8][ATT_VGRP]: row c at (c / 8) ATT_VGRP + (c % 8) ATT_VROW
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.y, split = blockIdx.z;
     const int64_t kb0 = a.tok_begin + (int64_t)split * a.keys_per_split;
@@ -2608,7 +2613,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
     // lq[wave][s][lane]: the lane's 16 bytes of k-step s, read back per tile so
     // that they hold no registers while the tiles are rebuilt (a wave reads
     // only what it wrote)
-    uint4 *lq = reinterpret_cast<uint4 *>(lvt + ATT_D * ATT_VROW) + (size_t)wave * (D / 32) * 64 + lane;
+    uint4 *lq = reinterpret_cast<uint4 *>(lvt + (D / 8) * ATT_VGRP) + (size_t)wave * (D / 32) * 64 + lane;
     {
         const int qr = min(q0 + c16, a.Nq - 1);
         const uint4 *qp = reinterpret_cast<const uint4 *>(a.q + (size_t)h * a.q_hs + (size_t)qr * D + 8 * g);
@@ -2647,8 +2652,8 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
 #pragma unroll
             for (int i = 0; i < 8; i += 2) {
                 const uint32_t pv = pack_bf16x2(yv[i], yv[i + 1]);
-                lvt[(8 * j + i) * ATT_VROW + kk] = (uint16_t)pv;
-                lvt[(8 * j + i + 1) * ATT_VROW + kk] = (uint16_t)(pv >> 16);
+                lvt[j * ATT_VGRP + i * ATT_VROW + kk] = (uint16_t)pv;
+                lvt[j * ATT_VGRP + (i + 1) * ATT_VROW + kk] = (uint16_t)(pv >> 16);
             }
         }
         __syncthreads();
@@ -2714,7 +2719,8 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
             const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
 #pragma unroll
             for (int b = 0; b < D / 16; ++b) {
-                const uint16_t *vr = lvt + (16 * b + c16) * ATT_VROW + 32 * s + 4 * g;
+                const int vrow = 16 * b + c16;
+                const uint16_t *vr = lvt + (vrow >> 3) * ATT_VGRP + (vrow & 7) * ATT_VROW + 32 * s + 4 * g;
                 const uint2 lo = *reinterpret_cast<const uint2 *>(vr), hi = *reinterpret_cast<const uint2 *>(vr + 16);
                 const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
                 o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[b], 0, 0, 0);
