@@ -2510,10 +2510,11 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t s) {
 // the splits by their log-sum-exp.
 constexpr int ATT_WAVES = 16;
 constexpr int ATT_BQ = 16 * ATT_WAVES;   // queries per workgroup
-constexpr int ATT_BK = 64;               // keys per tile
+constexpr int ATT_BK = 64;               // keys per step of the scores and the softmax
+constexpr int ATT_TILE = 128;            // keys rebuilt into LDS between two barriers
 constexpr int ATT_D = 128;
 constexpr int ATT_KROW = ATT_D + 8;      // bf16 per K row in LDS (padded against bank conflicts)
-constexpr int ATT_VROW = ATT_BK + 8;     // bf16 per transposed V row
+constexpr int ATT_VROW = ATT_TILE + 8;   // bf16 per transposed V row
 // bf16 per group of 8 transposed V rows (the 8 channels one thread rebuilds):
 // 4 more than 8 rows, so that the 16 groups begin on 16 different banks and the
 // rebuild's 2-byte stores, which write one row of each group at once, do not
@@ -2521,7 +2522,7 @@ constexpr int ATT_VROW = ATT_BK + 8;     // bf16 per transposed V row
 constexpr int ATT_VGRP = 8 * ATT_VROW + 4;
 // K tile, V^T tile, and each wave's query operands (kept in LDS rather than in
 // registers while the tiles are rebuilt)
-constexpr size_t ATT_LDS = (size_t)2 * (ATT_BK * ATT_KROW + (ATT_D / 8) * ATT_VGRP) + (size_t)ATT_WAVES * (ATT_D / 32) * 64 * 16;
+constexpr size_t ATT_LDS = (size_t)2 * (ATT_TILE * ATT_KROW + (ATT_D / 8) * ATT_VGRP) + (size_t)ATT_WAVES * (ATT_D / 32) * 64 * 16;
 
 // 8 channels [8 j, 8 j + 8) of key n of one head of a compressed tensor, in
 // three steps so that the loads of K and V go out together: fetch1 issues the
@@ -2601,8 +2602,8 @@ template <int TT, bool FP8>
 __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
     constexpr int D = ATT_D;
     extern __shared__ uint16_t att_lds[];
-    uint16_t *lk = att_lds;                              // [ATT_BK][ATT_KROW]
-    uint16_t *lvt = lk + ATT_BK * ATT_KROW;              // [D / 8][ATT_VGRP]: row c at (c / 8) ATT_VGRP + (c % 8) ATT_VROW
+    uint16_t *lk = att_lds;                              // [ATT_TILE][ATT_KROW]
+    uint16_t *lvt = lk + ATT_TILE * ATT_KROW;              // [D / 8][ATT_VGRP]: row c at (c / 8) ATT_VGRP + (c % 8) ATT_VROW
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.y, split = blockIdx.z;
     const int64_t kb0 = a.tok_begin + (int64_t)split * a.keys_per_split;
@@ -2625,10 +2626,12 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
 #pragma unroll
     for (int b = 0; b < D / 16; ++b) o[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m = -__builtin_inff(), l = 0.f;   // the lane's query: running maximum (base 2) and sum
-    const int kk = tid >> 4, j = tid & 15;  // the key and 8-channel slice this thread rebuilds
-    for (int64_t t0 = kb0; t0 < kb1; t0 += ATT_BK) {
+    const int j = tid & 15;  // the 8-channel slice this thread rebuilds
+    for (int64_t t0 = kb0; t0 < kb1; t0 += ATT_TILE) {
         __syncthreads();   // the previous tile's readers are done
-        {
+#pragma unroll 1
+        for (int kp = 0; kp < ATT_TILE; kp += 64) {
+            const int kk = (tid >> 4) + kp;   // the key this thread rebuilds
             const int64_t n = t0 + kk;
             float yk[8], yv[8];
             if (n < kb1) {
@@ -2657,16 +2660,18 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
             }
         }
         __syncthreads();
-        // S^T = K Q^T for 4 blocks of 16 keys: sacc[kb][r] = score of key
-        // 16 kb + 4 g + r for the lane's query c16
-        f32x4_t sacc[ATT_BK / 16];
         bf16x8_t qb[D / 32];
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) qb[s] = __builtin_bit_cast(bf16x8_t, lq[s * 64]);
+#pragma unroll 1
+        for (int k0 = 0; k0 < ATT_TILE; k0 += ATT_BK) {   // steps of ATT_BK keys of the tile
+        // S^T = K Q^T for 4 blocks of 16 keys: sacc[kb][r] = score of key
+        // k0 + 16 kb + 4 g + r for the lane's query c16
+        f32x4_t sacc[ATT_BK / 16];
 #pragma unroll
         for (int kb = 0; kb < ATT_BK / 16; ++kb) {
             sacc[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            const uint16_t *kr = lk + (16 * kb + c16) * ATT_KROW + 8 * g;
+            const uint16_t *kr = lk + (k0 + 16 * kb + c16) * ATT_KROW + 8 * g;
 #pragma unroll
             for (int s = 0; s < D / 32; ++s)
                 sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -2680,7 +2685,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
         for (int kb = 0; kb < ATT_BK / 16; ++kb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const bool valid = t0 + 16 * kb + 4 * g + r < kb1;
+                const bool valid = t0 + k0 + 16 * kb + 4 * g + r < kb1;
                 const float v = valid ? sacc[kb][r] * a.scale_log2 : -__builtin_inff();
                 sacc[kb][r] = v;
                 mx = fmaxf(mx, v);
@@ -2720,11 +2725,12 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
 #pragma unroll
             for (int b = 0; b < D / 16; ++b) {
                 const int vrow = 16 * b + c16;
-                const uint16_t *vr = lvt + (vrow >> 3) * ATT_VGRP + (vrow & 7) * ATT_VROW + 32 * s + 4 * g;
+                const uint16_t *vr = lvt + (vrow >> 3) * ATT_VGRP + (vrow & 7) * ATT_VROW + k0 + 32 * s + 4 * g;
                 const uint2 lo = *reinterpret_cast<const uint2 *>(vr), hi = *reinterpret_cast<const uint2 *>(vr + 16);
                 const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
                 o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[b], 0, 0, 0);
             }
+        }
         }
     }
     // this split's unnormalised output and row statistics
