@@ -45,11 +45,24 @@ def _decoded(oc, dst, b, e, chunk, heads, rope=None):
                                                     ("native", False, 0, 64, 1, "e4m3"),
                                                     ("native", True, 0, 2000, 100, "two_level")])
 def test_attention_over_compressed_cache(fmt, use_rope, b, e, Nq, sm):
-    say(f"attention fmt={fmt} rope={use_rope} keys [{b}, {e}) Nq={Nq} scales {sm}")
+    _attention_case(fmt, use_rope, b, e, Nq, sm)
+
+
+@pytest.mark.parametrize("T,fmt,use_rope,b,e,Nq", [(1, "native", True, 5, 2000, 129),
+                                                   (3, "e4m3", False, 0, 1999, 260),
+                                                   (4, "native", True, 300, 1700, 40)])
+def test_attention_stage_counts(T, fmt, use_rope, b, e, Nq):
+    """The kernel's instances for 1, 3 and 4 stages (the other cases run 2)."""
+    _attention_case(fmt, use_rope, b, e, Nq, "e4m3", T=T)
+
+
+def _attention_case(fmt, use_rope, b, e, Nq, sm, T=None):
+    say(f"attention fmt={fmt} rope={use_rope} keys [{b}, {e}) Nq={Nq} scales {sm} T={T}")
     q = lib()
     p = synthkv.PRESETS[2]
     H, chunk = 2, 1000
-    oc = ocfg(p, "K", n_centroids=64, iters_cold=3, iters_warm=2, centroid_format=fmt, scale_mode=sm)
+    extra = {} if T is None else {"n_stages": T}
+    oc = ocfg(p, "K", n_centroids=64, iters_cold=3, iters_warm=2, centroid_format=fmt, scale_mode=sm, **extra)
     # K and V of H heads as one 2H-head tensor (keys first)
     X = np.concatenate([synthkv.gen_numpy(p, t, heads=H, n_tokens=2000) for t in ("K", "V")])
     dst, _ = gpu_encode_chunks(oc, X, chunk)
