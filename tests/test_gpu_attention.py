@@ -56,6 +56,13 @@ def test_attention_stage_counts(T, fmt, use_rope, b, e, Nq):
     _attention_case(fmt, use_rope, b, e, Nq, "e4m3", T=T)
 
 
+@pytest.mark.parametrize("b,e,Nq", [(999, 1000, 17), (999, 1001, 33), (1, 2000, 257)])
+def test_attention_edge_ranges(b, e, Nq):
+    """One key; two keys on either side of a chunk boundary; query counts that
+    leave partial 16-query groups and a partial 256-query block."""
+    _attention_case("native", True, b, e, Nq, "e4m3")
+
+
 def _attention_case(fmt, use_rope, b, e, Nq, sm, T=None):
     say(f"attention fmt={fmt} rope={use_rope} keys [{b}, {e}) Nq={Nq} scales {sm} T={T}")
     q = lib()
