@@ -164,7 +164,7 @@ struct EncodeWorkspace {
         idx = take((size_t)T * H * K * 4);
         vstats = take(value_stats_words(H) * 4);
         tstats = take((size_t)T * H * TSTAT_BLOCKS * 2 * 4);
-        if (c.dtype == QVG_BF16 && T >= 2) r1 = take((size_t)H * N * D * 2);   // R(1) as the stage-2 operand
+        if (c.dtype == QVG_BF16 && T >= 2) r1 = take((size_t)H * N * D * 2);   // bf16(R(t)), the next stage's operand
         conv = take(conv_words(H, T) * 4);
         // FP8 tables: their values in the tensor dtype, which later residuals read
         if (c.centroid_format == QVG_CENT_E4M3) mirror = take((size_t)T * H * K * D * dtype_size(c.dtype));
@@ -390,8 +390,9 @@ static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_he
     int32_t *idx = at<int32_t>(workspace, ws.idx);
     uint32_t *vstats = at<uint32_t>(workspace, ws.vstats);
     uint32_t *tstats = at<uint32_t>(workspace, ws.tstats);   // [T][H][TSTAT_BLOCKS] stored-table magnitudes
-    // bf16 tensors: the final assign of stage 1 leaves bf16(R(1)) [H][N][D], which
-    // the assigns of stage 2 read in place of x less the stage-1 rows
+    // bf16 tensors: the final assign of stage t < T leaves bf16(R(t)) [H][N][D],
+    // which the assigns of stage t + 1 read in place of x less the earlier
+    // stages' rows (one buffer, rewritten in place by each stage's final assign)
     uint16_t *r1 = cfg->dtype == QVG_BF16 && T >= 2 ? at<uint16_t>(workspace, ws.r1) : nullptr;
     Src r1src = plain_src(r1, (int64_t)N * D);
     const bool warm_cache = cache && cache->valid;
@@ -426,7 +427,7 @@ static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_he
         // algorithmic traffic: the input row plus one assignment byte per earlier stage
         const double row_bytes = HND * esz + (double)H * N * (t - 1);
         const double assign_flops = 2.0 * H * N * K * D;
-        const bool use_r1 = r1 && t == 2;
+        const bool use_r1 = r1 && t >= 2;
         const Src &asrc = use_r1 ? r1src : src;   // what the assigns read
         const double assign_bytes = (use_r1 ? HND * 2 : row_bytes) + H * N + table;
         QVG_LAUNCH("init_centroids", 0, (double)H * K * D * (esz + 4) + table,
@@ -450,7 +451,7 @@ static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_he
             }
             QVG_LAUNCH("assign", assign_flops, assign_bytes,
                        launch_assign(D, cfg->dtype, H, N, K, asrc, Cb, pi, cap, cnt[c],
-                                     t == 1 && it == 0 && stats_in_assign ? vstats : nullptr, nullptr,
+                                     t == 1 && it == 0 && stats_in_assign ? vstats : nullptr, nullptr, nullptr,
                                      cvg ? done : nullptr, cvg ? ndone : nullptr,
                                      cvg && it > 0 ? chg[c] : nullptr, s));
             if (seg) {
@@ -483,10 +484,12 @@ static qvg_status encode_impl(const qvg_config *cfg, const void *x, int64_t x_he
                        launch_store_centroids(D, H, K, C, cfg->dtype, cslot, cache ? cache->data + slice : nullptr,
                                               tstats + (size_t)(t - 1) * H * TSTAT_BLOCKS * 2, s));
         }
-        uint16_t *rout = r1 && t == 1 ? r1 : nullptr;
-        QVG_LAUNCH("assign", assign_flops, assign_bytes + (rout ? HND * 2 : 0.0),
-                   launch_assign(D, cfg->dtype, H, N, K, asrc, Cb, pi, cap, nullptr, nullptr, rout, nullptr, nullptr,
-                                 nullptr, s));
+        // the next stage's operand: from the input itself at t = 1, else from
+        // R(t-1) rebuilt in fp32 out of x and the earlier stages' stored rows
+        uint16_t *rout = r1 && t < T ? r1 : nullptr;
+        QVG_LAUNCH("assign", assign_flops, assign_bytes + (rout ? HND * 2 : 0.0) + (rout && t > 1 ? row_bytes : 0.0),
+                   launch_assign(D, cfg->dtype, H, N, K, asrc, Cb, pi, cap, nullptr, nullptr, rout,
+                                 rout && t > 1 ? &src : nullptr, nullptr, nullptr, nullptr, s));
         if (t < T) {
             src.cent[t - 1] = fp8 ? mslot : cslot;
             src.pi[t - 1] = pi;
@@ -723,7 +726,7 @@ qvg_status qvg_kmeans_assign(const void *x, int32_t x_dtype, int64_t x_head_stri
     QVG_LAUNCH("assign", 2.0 * heads * n_tokens * n_centroids * d,
                (double)heads * n_tokens * (d * dtype_size(x_dtype) + 1) + table,
                launch_assign(d, x_dtype, heads, n_tokens, n_centroids, src, Cb, assign_out, assign_head_stride, nullptr,
-                             nullptr, nullptr, nullptr, nullptr, nullptr, s));
+                             nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, s));
     return QVG_OK;
 }
 

@@ -475,11 +475,12 @@ __device__ __forceinline__ void assign_load(const Src &src, int h, int N, int to
 }
 
 // One wave: the nearest centroid of the TILE tokens from tok0, whose operands are in bt.
-template <int D, typename KVT>
+// ROUT: the next stage's operand may be written (launches with the specialised operand load).
+template <int D, typename KVT, bool ROUT>
 __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int tok0, const bf16x8_t (&bt)[ASSIGN_TB][D / 32],
                                             const uint4 *lds, const double *lcn64, const float *lhcn, int32_t *list,
                                             uint8_t *labs, int Kp, uint8_t *pi, int64_t pi_hs, int32_t *counts,
-                                            uint16_t *rout, int32_t *changed) {
+                                            uint16_t *rout, const Src &rsrc, int32_t *changed) {
     constexpr int KS = D / 32;
     constexpr int CH = D / 8;
     const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
@@ -667,8 +668,10 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
         for (int o = 32; o >= 1; o >>= 1) nchg += __shfl_xor(nchg, o);
         if (lane == 0 && nchg) atomicAdd(&changed[h], nchg);
     }
-    if (!rout) return;
-    // the next stage's operand: bf16(fp32(x - c)) with c the token's stored row
+    if (!ROUT || !rout) return;
+    // the next stage's operand bf16(R(t)) = bf16(fp32(R(t-1) - c)), c the token's
+    // stored row: from the operands when they are R(t-1) itself (the input of
+    // stage 1), else from R(t-1) rebuilt in fp32 by rsrc
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) {
@@ -676,7 +679,22 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
         const int L = n < N ? (int)labs[16 * b + r16] : 0;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            const uint4 r = sub_bf16x8(__builtin_bit_cast(uint4, bt[b][s]), lds[L * (CH + 1) + 4 * s + g]);
+            const uint4 c = lds[L * (CH + 1) + 4 * s + g];
+            uint4 r;
+            if (rsrc.P == 0) {
+                r = sub_bf16x8(__builtin_bit_cast(uint4, bt[b][s]), c);
+            } else {
+                float v[8];
+                src_row8<D, KVT>(rsrc, h, min(n, N - 1), 32 * s + 8 * g, v);
+                const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[2 * i] = v[2 * i] - __uint_as_float(cw[i] << 16);
+                    v[2 * i + 1] = v[2 * i + 1] - __uint_as_float(cw[i] & 0xFFFF0000u);
+                }
+                r = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                               pack_bf16x2(v[6], v[7]));
+            }
             if (n < N) *reinterpret_cast<uint4 *>(rout + ((size_t)h * N + n) * D + 32 * s + 8 * g) = r;
         }
     }
@@ -692,7 +710,7 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
                                                                  int K, int Kp, uint8_t *__restrict__ pi,
                                                                  int64_t pi_hs, int32_t *__restrict__ counts,
                                                                  uint32_t *__restrict__ vstats,
-                                                                 uint16_t *__restrict__ rout,
+                                                                 uint16_t *__restrict__ rout, Src rsrc,
                                                                  const int32_t *__restrict__ skip,
                                                                  const int32_t *__restrict__ nskip,
                                                                  int32_t *__restrict__ changed) {
@@ -789,8 +807,8 @@ __global__ __launch_bounds__(64 * ASSIGN_WAVES, 4) void k_assign(Src src, int H,
                     }
                 }
             }
-            assign_wave<D, KVT>(src, h, N, tok0, bt, lds + sl * Kp * (CH + 1), lcn64 + sl * Kp, lhcn + sl * Kp,
-                                lists + wave * TILE, labs + wave * TILE, Kp, pi, pi_hs, counts, rout, changed);
+            assign_wave<D, KVT, !ANYP>(src, h, N, tok0, bt, lds + sl * Kp * (CH + 1), lcn64 + sl * Kp, lhcn + sl * Kp,
+                                lists + wave * TILE, labs + wave * TILE, Kp, pi, pi_hs, counts, rout, rsrc, changed);
         }
         __syncthreads();   // the tables are replaced only once every wave is done with them
         u = e;
@@ -810,8 +828,8 @@ static int device_cus() {
 }
 
 hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, const uint16_t *Cb, uint8_t *pi,
-                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, uint16_t *rout, const int32_t *skip,
-                         const int32_t *nskip, int32_t *changed, hipStream_t s) {
+                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, uint16_t *rout, const Src *rsrc,
+                         const int32_t *skip, const int32_t *nskip, int32_t *changed, hipStream_t s) {
     const int Kp = padded_k(K);
     const size_t lds = 2 * ((size_t)Kp * (D / 8 + 1) * 16 + (size_t)Kp * 12) + (ASSIGN_WAVES * TILE + 4) * sizeof(int32_t) +
                        ASSIGN_WAVES * TILE;
@@ -823,19 +841,20 @@ hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, 
     // bf16 tensors with at most one earlier stage (every stage at T <= 2) take the
     // specialised operand load
     const bool anyp = !(dtype == DT_BF16 && src.P <= 1);
-    if (rout && (anyp || src.P != 0)) return hipErrorInvalidValue;
+    if (rout && (anyp || (!rsrc && src.P != 0))) return hipErrorInvalidValue;
+    const Src &rs = rsrc ? *rsrc : src;   // where rout's fp32 R(t-1) comes from
     QVG_DISPATCH_DT(D, dtype, {
         if (anyp || sizeof(KVT) != 2) {
             (void)hipFuncSetAttribute((const void *)k_assign<DD, KVT, true>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             QVG_KERNEL((k_assign<DD, KVT, true>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts,
-                       (uint32_t *)nullptr, (uint16_t *)nullptr, skip, nskip, changed);
+                       (uint32_t *)nullptr, (uint16_t *)nullptr, src, skip, nskip, changed);
         } else {
             using KB = uint16_t;   // (this branch is only taken for bf16)
             (void)hipFuncSetAttribute((const void *)k_assign<DD, KB, false>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             QVG_KERNEL((k_assign<DD, KB, false>), g, b, lds, s, src, H, N, Cb, K, Kp, pi, pi_hs, counts, vstats, rout,
-                       skip, nskip, changed);
+                       rs, skip, nskip, changed);
         }
     });
     return hipGetLastError();

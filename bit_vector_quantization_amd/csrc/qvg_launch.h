@@ -65,15 +65,19 @@ struct ConvState {
 // exactly in fp64.  counts (non-null) [H][Kp] += tokens per centroid.  vstats
 // (non-null; a bf16 tensor without earlier stages only): the input's value
 // statistics are folded into partial 0 of each head (cleared beforehand).
-// rout (non-null; a bf16 tensor without earlier stages only) [H][N][D] bf16
-// receives bf16(fp32(x - Cb[pi])), the operand that the next stage's assign
-// would otherwise rebuild from x, its table and its assignment.  skip
+// rout (non-null; a bf16 tensor whose operands take the specialised load)
+// [H][N][D] bf16 receives bf16(fp32(R(t-1) - Cb[pi])), the operand that the
+// next stage's assign would otherwise rebuild from x and the stored tables and
+// assignments: R(t-1) is the operand itself when rsrc is null (src without
+// earlier stages), else rebuilt in fp32 by rsrc (any number of stages; rout may
+// be the buffer the operands come from, as each tile reads its own rows before
+// it writes them).  skip
 // (non-null) [H]: heads with skip[h] != 0 are left alone (and with *nskip ==
 // H nothing is done).  changed (non-null) [H] += labels that differ from
 // what pi held before.
 hipError_t launch_assign(int D, int dtype, int H, int N, int K, const Src &src, const uint16_t *Cb, uint8_t *pi,
-                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, uint16_t *rout, const int32_t *skip,
-                         const int32_t *nskip, int32_t *changed, hipStream_t s);
+                         int64_t pi_hs, int32_t *counts, uint32_t *vstats, uint16_t *rout, const Src *rsrc,
+                         const int32_t *skip, const int32_t *nskip, int32_t *changed, hipStream_t s);
 
 // Histogram of an assignment (counts must be zero on entry).
 hipError_t launch_count(int H, int N, int Kp, const uint8_t *pi, int64_t pi_hs, int32_t *counts,
