@@ -2327,6 +2327,14 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, 8) void k_decode_lds(const uint8_t
         for (int u = 0; u < DEC_TRIP / STEP; ++u) {
             const int i = u * STEP + slot;
             if (i >= nt) break;
+            const size_t orow = (size_t)(i0 + i - tok_begin) * D;
+            // the rotation table has the output's token rows; pair p of a row is
+            // the float pair (cos, sin) at channels 2p, 2p + 1.  Requested before
+            // the rebuild, which hides its latency (with bf16 tables; fp32 tables
+            // leave no registers for it)
+            constexpr bool EARLY = sizeof(CentT) == 2;
+            float cs[8];
+            if (EARLY && rot) load8_f32(rope + orow + c0, cs);
             const uint32_t w = reinterpret_cast<const uint16_t *>(mcodes)[i * (CB / 2) + jj];
             float y[8];
             dequant8(w, e4m3_decode(msc[i * SPT + sofs]) * sx, y);
@@ -2339,12 +2347,8 @@ __global__ __launch_bounds__(DEC_LDS_THREADS, 8) void k_decode_lds(const uint8_t
                 for (int q = 0; q < CP8; ++q) cv8[q] = tab[r * CHH + ((CP8 * jj + q) ^ (r & (CHH - 1)))];
                 add8<CentT>(cv8, y);
             }
-            const size_t orow = (size_t)(i0 + i - tok_begin) * D;
             if (rot) {
-                // the rotation table has the output's token rows; pair p of a row
-                // is the float pair (cos, sin) at channels 2p, 2p + 1
-                float cs[8];
-                load8_f32(rope + orow + c0, cs);
+                if (!EARLY) load8_f32(rope + orow + c0, cs);
                 rope8(cs, y);
             }
             store8_out<OutT>(oh + orow, y);
