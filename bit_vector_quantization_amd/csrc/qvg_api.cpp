@@ -610,13 +610,29 @@ qvg_status qvg_decode_rope(const qvg_config *cfg, const qvg_cache_view *src, int
     return decode_impl(cfg, src, tok_begin, tok_end, rope, rope_heads, out, out_head_stride, out_dtype, stream);
 }
 
-// Splits of the key range of an attention call: enough workgroups to fill the
-// chip twice over, at least 4 tiles of 64 keys per split, at most 64 splits.
+// Splits of the key range of an attention call.  One attention workgroup runs
+// per CU (256 on the chip) and the splits of a call are of equal length, so the
+// workgroups run in rounds of 256 and a last round that is only partly full
+// leaves CUs idle for a whole round.  Starting from enough workgroups to fill
+// the chip twice over, up to four times that many splits are considered and
+// the count whose workgroups fill their rounds best is taken (the fewest on a
+// tie); at least 4 tiles of 64 keys per split, at most 64 splits.
 static int attention_splits(int H, int Nq, int64_t Nk) {
-    const int64_t qblocks = (Nq + 255) / 256;
-    int64_t sp = (512 + qblocks * H - 1) / (qblocks * H);
-    sp = std::min<int64_t>(sp, std::max<int64_t>(1, Nk / 256));
-    return (int)std::max<int64_t>(1, std::min<int64_t>(sp, 64));
+    constexpr int64_t CUS = 256;
+    const int64_t qblocks = (Nq + 255) / 256, w = qblocks * H;
+    const int64_t most = std::max<int64_t>(1, std::min<int64_t>(64, Nk / 256));
+    const int64_t sp0 = std::min<int64_t>(most, (2 * CUS + w - 1) / w);
+    int64_t best = sp0;
+    double best_fill = 0.0;
+    for (int64_t sp = sp0; sp <= std::min<int64_t>(most, 4 * sp0); ++sp) {
+        const int64_t wg = w * sp, rounds = (wg + CUS - 1) / CUS;
+        const double fill = (double)wg / (double)(rounds * CUS);
+        if (fill > best_fill + 1e-9) {
+            best_fill = fill;
+            best = sp;
+        }
+    }
+    return (int)best;
 }
 
 qvg_status qvg_attention_workspace_bytes(const qvg_config *cfg, int32_t heads, int32_t n_queries, int64_t n_keys,

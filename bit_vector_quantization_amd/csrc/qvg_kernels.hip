@@ -2704,15 +2704,25 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
         // online softmax in base 2 for the lane's query; its 64 scores sit in
         // the 4 lanes c16, c16 + 16, c16 + 32, c16 + 48
         float mx = -__builtin_inff();
+        if (t0 + k0 + ATT_BK <= kb1) {   // every key of the step is in range
 #pragma unroll
-        for (int kb = 0; kb < ATT_BK / 16; ++kb)
+            for (int kb = 0; kb < ATT_BK / 16; ++kb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const bool valid = t0 + k0 + 16 * kb + 4 * g + r < kb1;
-                const float v = valid ? sacc[kb][r] * a.scale_log2 : -__builtin_inff();
-                sacc[kb][r] = v;
-                mx = fmaxf(mx, v);
-            }
+                for (int r = 0; r < 4; ++r) {
+                    sacc[kb][r] = sacc[kb][r] * a.scale_log2;
+                    mx = fmaxf(mx, sacc[kb][r]);
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < ATT_BK / 16; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool valid = t0 + k0 + 16 * kb + 4 * g + r < kb1;
+                    const float v = valid ? sacc[kb][r] * a.scale_log2 : -__builtin_inff();
+                    sacc[kb][r] = v;
+                    mx = fmaxf(mx, v);
+                }
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mn = fmaxf(m, mx);
@@ -2730,10 +2740,14 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
         rs += __shfl_xor(rs, 16);
         rs += __shfl_xor(rs, 32);
         l = l * corr + rs;
+        // once the running maxima settle, corr is exactly 1 for every query of
+        // the wave and the rescale would change nothing
+        if (__builtin_amdgcn_ballot_w64(corr != 1.f)) {
 #pragma unroll
-        for (int b = 0; b < D / 16; ++b)
+            for (int b = 0; b < D / 16; ++b)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[b][r] *= corr;
+                for (int r = 0; r < 4; ++r) o[b][r] *= corr;
+        }
         // O^T += V^T P^T over 32-key steps.  The step's k index 8 g + i stands
         // for key 4 g + i (i < 4) or 16 + 4 g + i - 4 (i >= 4) of the step, the
         // keys this lane holds P of, so P^T comes straight from registers; V^T
