@@ -92,6 +92,43 @@ def test_workspace_sizes(q):
     assert q.qvg_stage_workspace_bytes(H, N, d, 256) >= H * N * 4
 
 
+def _attention_splits(q, g, H, Nq, Nk):
+    """The split count behind qvg_attention_workspace_bytes: its partial outputs
+    take round_up(splits x H x Nq x d x 4, 256) bytes and its (max, sum) pairs
+    splits x H x Nq x 8."""
+    ws = q.qvg_attention_workspace_bytes(g, H, Nq, Nk)
+    per = H * Nq * 128 * 4
+    for sp in range(1, 65):
+        if ws == (sp * per + 255) // 256 * 256 + sp * H * Nq * 8:
+            return sp
+    raise AssertionError(f"workspace {ws} matches no split count")
+
+
+@pytest.mark.parametrize("H,Nq,Nk", [(12, 4680, 1_092_000), (12, 4680, 9360), (40, 4680, 38_000), (2, 300, 19_017),
+                                     (12, 1, 1_092_000), (1, 1, 10), (7, 1000, 500_000), (3, 257, 70_000)])
+def test_attention_splits_fill_their_rounds(q, H, Nq, Nk):
+    """One attention workgroup runs per CU (256) and the splits are equal, so the
+    workgroups run in rounds of 256: the split count never fills its rounds worse
+    than the plain rule (enough workgroups to fill the chip twice), stays within
+    1..64 and keeps at least 256 keys per split."""
+    p = synthkv.PRESETS[3]
+    g, _ = _cfg(q, p)
+    sp = _attention_splits(q, g, H, Nq, Nk)
+    w = (Nq + 255) // 256 * H
+    most = max(1, min(64, Nk // 256))
+    plain = min(most, (512 + w - 1) // w)
+
+    def fill(s):
+        return w * s / (-(-w * s // 256) * 256)
+
+    assert 1 <= sp <= most
+    assert fill(sp) >= fill(plain) - 1e-12
+    if (H, Nq, Nk) == (12, 4680, 1_092_000):   # the long-horizon attention: 2,280 workgroups in 9 rounds
+        assert sp == 10
+    if (H, Nq, Nk) == (40, 4680, 38_000):      # already 760 of 768 slots with one split
+        assert sp == 1
+
+
 @pytest.mark.parametrize("field,value,status", [
     ("n_centroids", 0, -1), ("n_centroids", 257, -1), ("n_stages", -1, -1), ("n_stages", 9, -1),
     ("group_size", 48, -1), ("group_size", 0, -1), ("iters_cold", -1, -1), ("dtype", 7, -1),
