@@ -2562,13 +2562,36 @@ struct AttnRow {
     uint4 cv[TT];   // bf16 row chunk, or (FP8) the 8 code bytes in .x, .y
 };
 
+// The chunk of key n of a tile whose first key lies in chunk c0 (chunk c0 + 1
+// starts at c1): one division per tile instead of one per key, and none when
+// the chunks are at least a tile long.
+struct AttnChunks {
+    int64_t c0, c1;
+    bool short_chunks;
+};
+
+__device__ __forceinline__ AttnChunks attn_chunks(int64_t t0, int chunk_tokens) {
+    AttnChunks k;
+    k.c0 = t0 / chunk_tokens;
+    k.c1 = (k.c0 + 1) * chunk_tokens;
+    k.short_chunks = chunk_tokens < ATT_TILE;
+    return k;
+}
+
+__device__ __forceinline__ int64_t attn_chunk_of(const AttnChunks &k, int64_t n, int chunk_tokens) {
+    if (k.short_chunks) return n / chunk_tokens;
+    return k.c0 + (n >= k.c1 ? 1 : 0);
+}
+
 template <int TT, bool FP8>
-__device__ __forceinline__ void attn_fetch1(const AttnSrc &a, int head, int64_t n, int j, AttnRow<TT, FP8> &r) {
+__device__ __forceinline__ void attn_fetch1(const AttnSrc &a, const AttnChunks &ck, int head, int64_t n, int j,
+                                            AttnRow<TT, FP8> &r) {
     constexpr int D = ATT_D;
     const size_t row = (size_t)head * a.cap + n;
+    const int gs = __builtin_ctz(a.G);   // the group size is a power of two
     r.w = reinterpret_cast<const uint16_t *>(a.codes)[row * (D / 8) + j];
-    r.sc = a.scales[row * (D / a.G) + (8 * j) / a.G];
-    r.c = n / a.chunk_tokens;
+    r.sc = a.scales[(row << (7 - gs)) + ((8 * j) >> gs)];   // row x D / G + 8 j / G, D = 128
+    r.c = attn_chunk_of(ck, n, a.chunk_tokens);
     r.sexp = a.scale_exp ? a.scale_exp[r.c * a.heads + head] : 0;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
@@ -2652,6 +2675,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
     const int j = tid & 15;  // the 8-channel slice this thread rebuilds
     for (int64_t t0 = kb0; t0 < kb1; t0 += ATT_TILE) {
         __syncthreads();   // the previous tile's readers are done
+        const AttnChunks ckk = attn_chunks(t0, a.k.chunk_tokens), ckv = attn_chunks(t0, a.v.chunk_tokens);
 #pragma unroll 1
         for (int kp = 0; kp < ATT_TILE; kp += 64) {
             const int kk = (tid >> 4) + kp;   // the key this thread rebuilds
@@ -2659,8 +2683,8 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
             float yk[8], yv[8];
             if (n < kb1) {
                 AttnRow<TT, FP8> rk, rv;
-                attn_fetch1<TT, FP8>(a.k, a.khead0 + h, n, j, rk);
-                attn_fetch1<TT, FP8>(a.v, a.vhead0 + h, n, j, rv);
+                attn_fetch1<TT, FP8>(a.k, ckk, a.khead0 + h, n, j, rk);
+                attn_fetch1<TT, FP8>(a.v, ckv, a.vhead0 + h, n, j, rv);
                 float cs[8];
                 if (a.rope) load8_f32(a.rope + (size_t)(n - a.tok_begin) * D + 8 * j, cs);
                 attn_fetch2<TT, FP8>(a.k, a.khead0 + h, j, rk);
