@@ -1855,91 +1855,121 @@ hipError_t launch_store_centroids(int D, int H, int K, const float *C, int dtype
 // with the second-level exponent f, the smallest f >= 0 with
 // fp32(max|r| / 1.5) <= 448 * 2^f (scale code = E4M3 of fp32(a / 1.5) / 2^f,
 // worth its value times 2^f), and writes f to exp_out[h].
+// Tokens per thread of the quantiser: two for bf16 tensors whose residual
+// comes from the input less at most one earlier stage (more bytes in flight
+// per wave), one where fp32 rows or a rebuild over several stages would take
+// the registers that the waves in flight need.
+template <typename KVT, int PM>
+constexpr int quant_tokens() { return sizeof(KVT) == 2 && PM <= 1 ? 2 : 1; }
+
 template <int D, typename KVT, bool CENT, int PM>
 __global__ __launch_bounds__(256) void k_quant(Src src, int N, const KVT *cent, int cent_rows, const uint8_t *pi,
                                                int64_t pi_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap, int G,
                                                uint32_t *amax_out, const uint32_t *amax_in, int8_t *exp_out) {
     constexpr int SL = D / 16;
     constexpr int TPB = 256 / SL;
+    constexpr int QU = quant_tokens<KVT, PM>();
     // one-dimensional grid: the blocks of one head on one XCD, in token order,
     // so that the head's centroid tables are fetched into that XCD's L2 once
     // (a grid too large for one dimension has one row of blocks per head)
-    const uint32_t bph = (N + TPB - 1) / TPB;   // blocks per head
+    const uint32_t bph = (N + TPB * QU - 1) / (TPB * QU);   // blocks per head
     const uint32_t tile = gridDim.y > 1 ? blockIdx.y * bph + blockIdx.x : xcd_tile(blockIdx.x, gridDim.x);
     const int h = (int)(tile / bph);
     const int j = threadIdx.x % SL;
-    const int n = (int)(tile % bph) * TPB + threadIdx.x / SL;
-    if (n >= N) return;   // whole groups leave together (SL divides 64)
-    float r[16];
+    const int n0 = (int)(tile % bph) * TPB * QU + threadIdx.x / SL;
+    if (n0 >= N) return;   // whole groups leave together (SL divides 64)
+    int n[QU];   // the thread's tokens; one past N reads token n0 again and stores nothing
+#pragma unroll
+    for (int u = 0; u < QU; ++u) n[u] = n0 + u * TPB < N ? n0 + u * TPB : n0;
+    float r[QU][16];
     if constexpr (PM <= 1) {
         // every label first, then every row: two dependent reads in all
-        const KVT *xr = static_cast<const KVT *>(src.x) + (size_t)h * src.x_hs + (size_t)n * D + 16 * j;
-        const int k1 = PM == 1 ? (int)src.pi[0][(size_t)h * src.pi_hs + n] : 0;
-        const int kt = CENT ? (int)pi[(size_t)h * pi_hs + n] : 0;
-        load16<KVT>(xr, r);
-        float c1[16], ct[16];
-        if constexpr (PM == 1) load16<KVT>(static_cast<const KVT *>(src.cent[0]) + ((size_t)h * src.K + k1) * D + 16 * j, c1);
-        if constexpr (CENT) load16<KVT>(cent + ((size_t)h * cent_rows + kt) * D + 16 * j, ct);
-        if constexpr (PM == 1) {
+        int k1[QU], kt[QU];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) r[i] = r[i] - c1[i];
+        for (int u = 0; u < QU; ++u) {
+            k1[u] = PM == 1 ? (int)src.pi[0][(size_t)h * src.pi_hs + n[u]] : 0;
+            kt[u] = CENT ? (int)pi[(size_t)h * pi_hs + n[u]] : 0;
         }
-        if constexpr (CENT) {
+        float c1[QU][16], ct[QU][16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) r[i] = r[i] - ct[i];
+        for (int u = 0; u < QU; ++u) {
+            load16<KVT>(static_cast<const KVT *>(src.x) + (size_t)h * src.x_hs + (size_t)n[u] * D + 16 * j, r[u]);
+            if constexpr (PM == 1)
+                load16<KVT>(static_cast<const KVT *>(src.cent[0]) + ((size_t)h * src.K + k1[u]) * D + 16 * j, c1[u]);
+            if constexpr (CENT) load16<KVT>(cent + ((size_t)h * cent_rows + kt[u]) * D + 16 * j, ct[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < QU; ++u) {
+            if constexpr (PM == 1) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) r[u][i] = r[u][i] - c1[u][i];
+            }
+            if constexpr (CENT) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) r[u][i] = r[u][i] - ct[u][i];
+            }
         }
     } else {
         float a[8], b[8];
-        src_row8<D, KVT>(src, h, n, 16 * j, a);
-        src_row8<D, KVT>(src, h, n, 16 * j + 8, b);
+        src_row8<D, KVT>(src, h, n[0], 16 * j, a);
+        src_row8<D, KVT>(src, h, n[0], 16 * j + 8, b);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { r[i] = a[i]; r[8 + i] = b[i]; }
+        for (int i = 0; i < 8; ++i) { r[0][i] = a[i]; r[0][8 + i] = b[i]; }
         if constexpr (CENT) {
-            const int k = pi[(size_t)h * pi_hs + n];
+            const int k = pi[(size_t)h * pi_hs + n[0]];
             float c[16];
             load16<KVT>(cent + ((size_t)h * cent_rows + k) * D + 16 * j, c);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) r[i] = r[i] - c[i];
+            for (int i = 0; i < 16; ++i) r[0][i] = r[0][i] - c[i];
         }
     }
-    float a = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(r[i]));
-    if (amax_out) {   // first launch of a two-level quantisation
-        atomicMax(&amax_out[h], __float_as_uint(a));
-        return;
-    }
     const int lanes = G >> 4;
-    for (int o = 1; o < lanes; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
-    int f = 0;
-    if (amax_in) {
-        const float a15 = __uint_as_float(amax_in[h]) / 1.5f;
-        while (a15 > ldexpf(448.f, f)) ++f;
-        if (n == 0 && j == 0) exp_out[h] = (int8_t)f;
-    }
-    const uint32_t sc = e4m3_encode_nonneg(ldexpf(a / 1.5f, -f));
-    const float s = ldexpf(e4m3_decode(sc), f);
-    uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const uint32_t q = (uint32_t)(r[i] >= -s) + (uint32_t)(r[i] >= 0.f) + (uint32_t)(r[i] >= s);
-        w |= q << (2 * i);
+    for (int u = 0; u < QU; ++u) {
+        const bool mine = u == 0 || n0 + u * TPB < N;
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(r[u][i]));
+        if (amax_out) {   // first launch of a two-level quantisation
+            if (mine) atomicMax(&amax_out[h], __float_as_uint(a));
+            continue;
+        }
+        for (int o = 1; o < lanes; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+        int f = 0;
+        if (amax_in) {
+            const float a15 = __uint_as_float(amax_in[h]) / 1.5f;
+            while (a15 > ldexpf(448.f, f)) ++f;
+            if (u == 0 && n0 == 0 && j == 0) exp_out[h] = (int8_t)f;
+        }
+        const uint32_t sc = e4m3_encode_nonneg(ldexpf(a / 1.5f, -f));
+        const float s = ldexpf(e4m3_decode(sc), f);
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t q = (uint32_t)(r[u][i] >= -s) + (uint32_t)(r[u][i] >= 0.f) + (uint32_t)(r[u][i] >= s);
+            w |= q << (2 * i);
+        }
+        if (!mine) continue;
+        const size_t row = (size_t)h * q_cap + n[u];
+        reinterpret_cast<uint32_t *>(codes + row * (D / 4))[j] = w;
+        if ((j & (lanes - 1)) == 0) scales[row * (D / G) + (16 * j) / G] = (uint8_t)sc;
     }
-    const size_t row = (size_t)h * q_cap + n;
-    reinterpret_cast<uint32_t *>(codes + row * (D / 4))[j] = w;
-    if ((j & (lanes - 1)) == 0) scales[row * (D / G) + (16 * j) / G] = (uint8_t)sc;
 }
 
 hipError_t launch_quant(int D, int dtype, int H, int N, const Src &src, const void *cent, int cent_rows,
                         const uint8_t *pi, int64_t pi_hs, uint8_t *codes, uint8_t *scales, int64_t q_cap, int G,
                         uint32_t *amax_out, const uint32_t *amax_in, int8_t *exp_out, hipStream_t s) {
     const int TPB = 256 / (D / 16);
-    const int64_t bph = (N + TPB - 1) / TPB, nb = (int64_t)H * bph;
-    const bool one_dim = nb * 256 < ((int64_t)1 << 32);
-    dim3 g(one_dim ? (uint32_t)nb : (uint32_t)bph, one_dim ? 1u : (uint32_t)H), b(256);
-#define QVG_QUANT_LAUNCH(CE, PMV)                                                                            \
-    QVG_KERNEL((k_quant<DD, KVT, CE, PMV>), g, b, 0, s, src, N, (const KVT *)cent, cent_rows, pi, pi_hs, codes, \
-               scales, q_cap, G, amax_out, amax_in, exp_out)
+    // blocks of TPB x (tokens per thread) tokens, per head
+    auto grid = [&](int qu) {
+        const int64_t bph = (N + (int64_t)TPB * qu - 1) / ((int64_t)TPB * qu), nb = (int64_t)H * bph;
+        const bool one_dim = nb * 256 < ((int64_t)1 << 32);
+        return dim3(one_dim ? (uint32_t)nb : (uint32_t)bph, one_dim ? 1u : (uint32_t)H);
+    };
+    const dim3 b(256);
+#define QVG_QUANT_LAUNCH(CE, PMV)                                                                                  \
+    QVG_KERNEL((k_quant<DD, KVT, CE, PMV>), grid(quant_tokens<KVT, PMV>()), b, 0, s, src, N, (const KVT *)cent, cent_rows, \
+               pi, pi_hs, codes, scales, q_cap, G, amax_out, amax_in, exp_out)
     QVG_DISPATCH_DT(D, dtype, {
         if (cent) {
             if (src.P == 0) QVG_QUANT_LAUNCH(true, 0);
