@@ -63,11 +63,19 @@ def test_attention_edge_ranges(b, e, Nq):
     _attention_case("native", True, b, e, Nq, "e4m3")
 
 
-def _attention_case(fmt, use_rope, b, e, Nq, sm, T=None):
-    say(f"attention fmt={fmt} rope={use_rope} keys [{b}, {e}) Nq={Nq} scales {sm} T={T}")
+@pytest.mark.parametrize("chunk,b,e,Nq", [(48, 0, 2000, 100), (48, 37, 1500, 20), (128, 5, 2000, 64)])
+def test_attention_chunk_lengths(chunk, b, e, Nq):
+    """Chunks shorter than a 128-key tile (a tile spans several chunks, each with
+    its own tables) and chunks of exactly one tile (tiles that start inside a
+    chunk span two)."""
+    _attention_case("native", True, b, e, Nq, "e4m3", chunk=chunk)
+
+
+def _attention_case(fmt, use_rope, b, e, Nq, sm, T=None, chunk=1000):
+    say(f"attention fmt={fmt} rope={use_rope} keys [{b}, {e}) Nq={Nq} scales {sm} T={T} chunk={chunk}")
     q = lib()
     p = synthkv.PRESETS[2]
-    H, chunk = 2, 1000
+    H = 2
     extra = {} if T is None else {"n_stages": T}
     oc = ocfg(p, "K", n_centroids=64, iters_cold=3, iters_warm=2, centroid_format=fmt, scale_mode=sm, **extra)
     # K and V of H heads as one 2H-head tensor (keys first)
