@@ -550,6 +550,9 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
     // Two-stage pipeline: the matrix cores work on block cb + 1 while the
     // vector ALUs fold block cb.
     f32x4_t accA[ASSIGN_TB], accB[ASSIGN_TB];
+    // a wave in its block loop issues ahead of the SIMD's other waves (in the
+    // merge, the near-tie pass or a tile's setup), so the matrix core stays fed
+    __builtin_amdgcn_s_setprio(2);
     dots(0, accA);
     int cb = 0;
     for (; cb + 2 < ncb; cb += 2) {
@@ -567,6 +570,7 @@ __device__ __forceinline__ void assign_wave(const Src &src, int h, int N, int to
     } else {
         keys(cb, accA);
     }
+    __builtin_amdgcn_s_setprio(0);
     float xx[ASSIGN_TB];
 #pragma unroll
     for (int b = 0; b < ASSIGN_TB; ++b) xx[b] = __int_as_float(list[16 * b + r16]);
