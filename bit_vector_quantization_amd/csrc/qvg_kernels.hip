@@ -1551,8 +1551,12 @@ __global__ __launch_bounds__(64 * SEG_WAVES) void k_update_seg(Src src, int H, i
             const int per = (W1 - W0 + SEG_WAVES - 1) / SEG_WAVES;
             const int beg = min(W1, W0 + wave * per), end = min(W1, beg + per);
             if (beg < end) {
+                // the streaming sums issue ahead of the other workgroups of the CU
+                // in their prologue, list build or means
+                __builtin_amdgcn_s_setprio(1);
                 if (run_exact) seg_sums<D, KVT, false>(src, h, N, list, off, acc, s_emin, s_amax, beg, end);
                 else seg_sums<D, KVT, true>(src, h, N, list, off, acc, s_emin, s_amax, beg, end);
+                __builtin_amdgcn_s_setprio(0);
             }
         }
         __syncthreads();
