@@ -2745,6 +2745,9 @@ __global__ __launch_bounds__(64 * ATT_WAVES, 1) void k_attention(AttnArgs a) {
             }
         }
         __syncthreads();
+        // a wave whose 16 queries all lie past Nq (the last query block of a
+        // head) helps rebuild the tiles but has nothing to multiply
+        if (q0 >= a.Nq) continue;
         bf16x8_t qb[D / 32];
 #pragma unroll
         for (int s = 0; s < D / 32; ++s) qb[s] = __builtin_bit_cast(bf16x8_t, lq[s * 64]);
