@@ -43,7 +43,8 @@ def _decoded(oc, dst, b, e, chunk, heads, rope=None):
                                                     ("native", True, 137, 1931, 256, "e4m3"),
                                                     ("e4m3", True, 700, 2000, 77, "e4m3"),
                                                     ("native", False, 0, 64, 1, "e4m3"),
-                                                    ("native", True, 0, 2000, 100, "two_level")])
+                                                    ("native", True, 0, 2000, 100, "two_level"),
+                                                    ("e4m3", True, 300, 1800, 90, "two_level")])
 def test_attention_over_compressed_cache(fmt, use_rope, b, e, Nq, sm):
     _attention_case(fmt, use_rope, b, e, Nq, sm)
 

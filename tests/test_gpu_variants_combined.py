@@ -16,14 +16,16 @@ from gpu_util import DEV, check_chunk, fetch, gcfg, lib, ocfg, say, to_dev, to_n
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("fmt,sm,conv,tensor", [("e4m3", "two_level", 0, "V"), ("e4m3", "e4m3", 2, "K"),
-                                                ("native", "two_level", 1, "V"), ("e4m3", "two_level", 3, "V")])
-def test_variants_together_match_oracle(fmt, sm, conv, tensor):
-    say(f"variants together: tables {fmt}, scales {sm}, converge {conv}, {tensor}")
+@pytest.mark.parametrize("fmt,sm,conv,tensor,T,G", [("e4m3", "two_level", 0, "V", 2, 64), ("e4m3", "e4m3", 2, "K", 2, 64),
+                                                    ("native", "two_level", 1, "V", 2, 64),
+                                                    ("e4m3", "two_level", 3, "V", 2, 64),
+                                                    ("e4m3", "two_level", 2, "K", 4, 16)])
+def test_variants_together_match_oracle(fmt, sm, conv, tensor, T, G):
+    say(f"variants together: tables {fmt}, scales {sm}, converge {conv}, {tensor}, T={T}, G={G}")
     p = synthkv.PRESETS[2]
     rounds_cap = 12 if conv else 3
     oc = ocfg(p, tensor, n_centroids=48, iters_cold=rounds_cap, iters_warm=rounds_cap if conv else 2,
-              centroid_format=fmt, scale_mode=sm, converge=conv)
+              centroid_format=fmt, scale_mode=sm, converge=conv, n_stages=T, group_size=G)
     H, N, chunk = 2, 2000, 1000
     X = synthkv.gen_numpy(p, tensor, heads=H, n_tokens=N)
     if sm == "two_level":   # residual groups past E4M3's range (a power of two: exact in bf16)
