@@ -8,7 +8,8 @@ code, E4M3 scale byte and label value occurs) and laid out as a cache of
 several chunks with a ragged last one; decoded ranges start and end inside
 chunks.  Both kernels are covered: the one that stages the tables in LDS
 (1 to 4 stages with small enough tables) and the one that reads them through
-L2 (no stages, more than 4, or tables too large for LDS)."""
+L2 (no stages, more than 4, or tables too large for LDS), with native and FP8
+(E4M3) centroid tables and with plain and two-level scales."""
 import numpy as np
 import pytest
 import torch
@@ -134,3 +135,59 @@ def test_decode_rope_head_stride_with_gaps():
     for out in ("bf16", "f32"):
         got = _run(q, arrs, H, cap, chunk, d, K, T, G, "bf16", tb, te, rope, 2, out, pad=24)
         _same(got, _reference(arrs, chunk, T, G, tb, te, out, rope, 2))
+
+
+FMT_CASES = [
+    # H, cap, chunk, K, T, G, tb, te, rope_heads, centroid format, two-level scales
+    (3, 777, 300, 32, 2, 64, 123, 700, 2, "e4m3", False),   # LDS kernel, FP8 tables
+    (2, 600, 300, 64, 2, 64, 0, 600, 1, "native", True),     # LDS kernel, two-level scales
+    (2, 700, 350, 256, 4, 16, 349, 351, 2, "e4m3", True),    # both, four stages, across a boundary
+    (1, 260, 130, 16, 5, 32, 1, 259, 1, "e4m3", True),       # both, five stages: L2 kernel
+]
+
+
+@pytest.mark.parametrize("case", FMT_CASES, ids=[f"H{c[0]}_T{c[4]}_{c[9]}_{'2l' if c[10] else '1l'}" for c in FMT_CASES])
+def test_decode_rope_fp8_tables_and_two_level_scales(case):
+    """The rotated decode over FP8 (E4M3) centroid tables (a power-of-two
+    exponent per table in a 16-byte header, then K x d codes) and over two-level
+    scales (a second-level exponent per (chunk, head)), against the oracle's
+    decode of the same stored values."""
+    H, cap, chunk, K, T, G, tb, te, rh, fmt, two = case
+    d = 128
+    say(f"decode_rope formats {case}")
+    q = lib()
+    rng = np.random.default_rng(cap + 17 * T)
+    codes, scales, asg, cent = _cache(rng, H, cap, chunk, d, K, T, G, "bf16")
+    C = -(-cap // chunk)
+    if fmt == "e4m3":
+        ok = np.array([v for v in range(256) if v & 0x7F != 0x7F], np.uint8)   # every E4M3 byte but NaN
+        raw = np.zeros((C, T, H, 16 + K * d), np.uint8)
+        raw[..., 16:] = rng.choice(ok, (C, T, H, K * d))
+        raw[..., :4] = rng.integers(-6, 7, (C, T, H), dtype=np.int32)[..., None].view(np.uint8).reshape(C, T, H, 4)
+        cent = oracle.e4m3_decode(raw[..., 16:]).reshape(C, T, H, K, d)
+        cent = np.ldexp(cent, raw[..., :4].copy().view(np.int32)[..., 0][..., None, None]).astype(np.float32)
+        dev_cent = torch.from_numpy(raw).to(DEV)
+    else:
+        dev_cent = to_dev(cent, "bf16")
+    sexp = rng.integers(0, 4, (C, H)).astype(np.int8) if two else None
+    rope = _table(rng, te - tb, d)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    keep = [dev(codes), dev(scales), dev(asg), dev_cent, dev(rope)]
+    if two:
+        keep.append(dev(sexp))
+    view = q.qvg_cache_view(keep[0].data_ptr(), keep[1].data_ptr(), keep[2].data_ptr(), keep[3].data_ptr(), cap,
+                            chunk, H, keep[5].data_ptr() if two else None)
+    cfg = q.config(d, K, T, G, 2, 2, 7, "bf16", 0, fmt, "two_level" if two else "e4m3")
+    for out_dtype in ("f32", "bf16"):
+        dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+        out = torch.empty((H, te - tb, d), dtype=dt, device=DEV)
+        q.qvg_decode_rope(cfg, view, tb, te, keep[4], rh, out, out.stride(0),
+                          q.QVG_F32 if out_dtype == "f32" else q.QVG_BF16)
+        torch.cuda.synchronize()
+        parts = []
+        for c in range(tb // chunk, (te - 1) // chunk + 1):
+            b, e = max(tb, c * chunk), min(te, (c + 1) * chunk)
+            parts.append(oracle.decode_chunk(codes[:, b:e], scales[:, b:e], asg[:T, :, b:e], cent[c, :T], G, out_dtype,
+                                             rope=rope[b - tb:e - tb], rope_heads=rh,
+                                             scale_exp=None if sexp is None else sexp[c]))
+        _same(to_np(out), np.concatenate(parts, axis=1))
