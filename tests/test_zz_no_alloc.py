@@ -2,7 +2,9 @@
 workspace is the library's fixed device array), against qvg_encode_chunk with
 a caller-given workspace, through the C ABI: two calls in a row on the same
 array, the second with a smaller chunk, every output byte equal; a call over
-the array's limit is rejected before anything is launched."""
+the array's limit is rejected before anything is launched.  The variants'
+workspace regions (the FP8 operand table, the per-head stop state) come from the
+array too."""
 import numpy as np
 import pytest
 import torch
@@ -25,9 +27,11 @@ def _encode_pair(q, oc, X, cache_a, cache_b, chunk, dst_a, dst_b, enc):
 def test_static_scratch_encode_equals_workspace_encode():
     q = lib()
     p = synthkv.PRESETS[3]
-    say("no-allocation encode: 12 heads x 4,680 tokens, then 5 heads x 1,000 tokens")
-    for H, N, tensor in ((12, p.chunk_tokens, "V"), (5, 1000, "K")):
-        oc = ocfg(p, tensor)
+    say("no-allocation encode: 12 heads x 4,680 tokens, then 5 heads x 1,000 tokens, then 4 heads x 1,500 "
+        "tokens with FP8 tables, two-level scales and the convergence stop")
+    variants = dict(centroid_format="e4m3", scale_mode="two_level", converge=2, iters_cold=8, iters_warm=8)
+    for H, N, tensor, extra in ((12, p.chunk_tokens, "V", {}), (5, 1000, "K", {}), (4, 1500, "V", variants)):
+        oc = ocfg(p, tensor, **extra)
         cfg = gcfg(oc)
         assert q.qvg_encode_workspace_bytes(cfg, H, N) <= q.QVG_STATIC_SCRATCH_BYTES
         X = torch.from_numpy(synthkv.gen_numpy(p, tensor, heads=H, n_tokens=2 * N)).to(torch.bfloat16).to(DEV)
